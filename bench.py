@@ -1,0 +1,403 @@
+#!/usr/bin/env python3
+"""Fused vs N-launch unfused chains on one MI355X: achieved HBM GB/s and per-call us.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  C1  fp32 relu(a+b)*0.5, 1,048,576 elements                     (fuse_chain)
+  C2  YOLO decode, fp16 [1,255,80|40|20,..] -> fp32 [1,25200,85]  (fuse_det_decode)
+  C3  bf16 residual add + RMSNorm [16384, 4096]                   (fuse_add_rmsnorm)
+  C4  bf16 QKV split + RoPE + scale, 16384 tokens x 3x24x128     (fuse_qkv_rope)
+  C5  seeded 29-op fp16 chain at 65,536 and 268,435,456 elements  (fuse_chain)
+value = algorithmic bytes of the step (each input read once, each output written
+once) / step time. Every fused call is also timed alone, next to its unfused
+counterpart (one kernel per operator) and, for the small chain, next to the
+NaiveRT write-up's launch-cost model L = (t_unfused - t_fused)/(K - 1).
+
+Usage: python bench.py [--steps K] [--warmup W] [--no-cpu] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+# The NaiveRT write-up's two public timings (ms per decode round, 29 calls per
+# layer fused into 1 kernel) and the figures it derives from them.
+PAGES_COST_MODEL = {"t_unfused_ms": 12.3, "t_fused_ms": 3.4, "k": 29}
+
+
+def cost_model(t_unfused: float, t_fused: float, k: int) -> dict:
+    """K*L + T = t_unfused, L + T = t_fused  ->  L, T, launch share, reported cut."""
+    L = (t_unfused - t_fused) / (k - 1)
+    T = t_fused - L
+    return {"L": L, "T": T, "launch_share": k * L / t_unfused, "cut": 1.0 - t_fused / t_unfused}
+
+
+# ------------------------------------------------------------ byte models
+
+def det_bytes(levels_hw, n_anchors=3, n_ch=85, in_size=2):
+    e = sum(n_anchors * n_ch * h * w for h, w in levels_hw)  # input elements
+    rows = sum(n_anchors * h * w for h, w in levels_hw)
+    fused = e * in_size + rows * n_ch * 4
+    per_ch = e / n_ch
+    # permute, sigma(xy), sigma(obj+cls), exp(wh), x anchor, + grid, x stride: read + write
+    unf = 2 * e * in_size + 2 * in_size * per_ch * (2 + (n_ch - 4) + 2 + 2 + 2 + 2)
+    unf += 2 * e * in_size  # concat
+    unf += e * in_size + rows * n_ch * 4  # cast to fp32
+    return int(fused), int(unf)
+
+
+def rms_bytes(rows, cols, es=2):
+    s = rows * cols * es
+    fused = 4 * s + cols * es
+    unf = 3 * s + 2 * s + (s + rows * es) + 2 * rows * es + (2 * s + rows * es) + (2 * s + cols * es)
+    return fused, unf
+
+
+def rope_bytes(T, H, D, es=2):
+    q = T * H * D * es
+    return 6 * q, 6 * q + 2 * q + 2 * q + 2 * q
+
+
+def file_hash(*paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "c1": ["norm_pass_amd/csrc/chain.hip", "norm_pass_amd/csrc/device.h"],
+    "c5_large": ["norm_pass_amd/csrc/chain.hip", "norm_pass_amd/csrc/device.h"],
+    "c5_small": ["norm_pass_amd/csrc/chain.hip", "norm_pass_amd/csrc/device.h"],
+    "c2": ["norm_pass_amd/csrc/det_decode.hip", "norm_pass_amd/csrc/device.h"],
+    "c3": ["norm_pass_amd/csrc/add_rmsnorm.hip", "norm_pass_amd/csrc/device.h"],
+    "c4": ["norm_pass_amd/csrc/qkv_rope.hip", "norm_pass_amd/csrc/device.h"],
+}
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, "counters_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(rf"^\|\s*{name}\s*\|\s*([0-9a-f]{{16}})\s*\|\s*([0-9.e+]+)\s*\|", txt, re.M)
+    if not m:
+        return None
+    if m.group(1) != file_hash(*KERNEL_SOURCES[name]):
+        return None
+    return float(m.group(2))
+
+
+# ------------------------------------------------------------------ timing
+
+def time_calls(torch, fn, reps: int, trials: int):
+    """Median per-call seconds over `trials` trials of `reps` back-to-back calls,
+    timed with HIP events on the current stream (the stream every call uses)."""
+    res = []
+    for _ in range(trials):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        e.synchronize()
+        res.append(s.elapsed_time(e) / 1e3 / reps)
+    res.sort()
+    return res[len(res) // 2], res[max(0, len(res) // 10)], res[min(len(res) - 1, (9 * len(res)) // 10)]
+
+
+def pick_reps(torch, fn, target_s=0.003):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 2e-6)
+    return int(min(2000, max(3, target_s / one)))
+
+
+# ------------------------------------------------------------- workloads
+
+def build_workloads(torch, npa, synth, quick: bool):
+    dev = "cuda"
+    W = {}
+    import numpy as np
+
+    def tdev(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "f32":
+            return torch.from_numpy(a).to(dev)
+        if dt == "f16":
+            return torch.from_numpy(a.view(np.float16)).to(dev)
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # C1
+    n1 = 1 << 20
+    a, b = synth.c1_inputs(n1)
+    ta, tb = tdev(a, "f32"), tdev(b, "f32")
+    y1 = torch.empty(n1, device=dev)
+    W["c1"] = dict(
+        desc="fp32 relu(a+b)*0.5, 1,048,576 elements",
+        fused=lambda: npa.fuse_chain(synth.C1_CHAIN, [ta, tb], y1),
+        unfused=lambda: npa.unfused_chain(synth.C1_CHAIN, [ta, tb], y1),
+        bytes=12 * n1, unfused_bytes=28 * n1, launches=3, kernel="chain_vec<float, float, 2")
+    # C2
+    lv = [tdev(x, "f16") for x in synth.c2_inputs()]
+    hw = [(h, w) for h, w, _ in synth.YOLO_LEVELS]
+    st = [s for _, _, s in synth.YOLO_LEVELS]
+    an = np.array(synth.YOLO_ANCHORS, np.float32).reshape(3, 3, 2).tolist()
+    out2 = torch.empty((1, 25200, 85), device=dev)
+    ws2 = torch.empty(npa.det_workspace_bytes(lv), dtype=torch.uint8, device=dev)
+    fb, ub = det_bytes(hw)
+    W["c2"] = dict(
+        desc="YOLO decode fp16 [1,255,80|40|20] -> fp32 [1,25200,85]",
+        fused=lambda: npa.fuse_det_decode(lv, st, an, out2),
+        unfused=lambda: npa.unfused_det_decode(lv, st, an, out2, ws2),
+        bytes=fb, unfused_bytes=ub, launches=23, kernel="det_decode_kernel")
+    # C3
+    rows = 2048 if quick else 16384
+    x, r, w = synth.c3_inputs(rows=rows)
+    tx, tr, tw = tdev(x, "bf16"), tdev(r, "bf16"), tdev(w, "bf16")
+    del x, r
+    h3 = torch.empty_like(tx)
+    o3 = torch.empty_like(tx)
+    ws3 = torch.empty(npa.rmsnorm_workspace_bytes(rows, 4096, torch.bfloat16), dtype=torch.uint8,
+                      device=dev)
+    fb, ub = rms_bytes(rows, 4096)
+    W["c3"] = dict(
+        desc=f"bf16 residual add + RMSNorm [{rows}, 4096], eps 1e-6",
+        fused=lambda: npa.fuse_add_rmsnorm(tx, tr, tw, h3, o3, 1e-6),
+        unfused=lambda: npa.unfused_add_rmsnorm(tx, tr, tw, h3, o3, ws3, 1e-6),
+        bytes=fb, unfused_bytes=ub, launches=6, kernel="rms_vec")
+    # C4
+    T = 2048 if quick else 16384
+    qkv = tdev(synth.c4_inputs(tokens=T), "bf16")
+    q4, k4, v4 = (torch.empty((24, T, 128), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    qs = float(np.float32(1.0 / math.sqrt(128.0)))
+    fb, ub = rope_bytes(T, 24, 128)
+    W["c4"] = dict(
+        desc=f"bf16 QKV split + RoPE + scale, [{T}, 3x24x128] -> 3 x [24, {T}, 128]",
+        fused=lambda: npa.fuse_qkv_rope(qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
+        unfused=lambda: npa.unfused_qkv_rope(qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
+        bytes=fb, unfused_bytes=ub, launches=4, kernel="rope_vec")
+    # C5
+    ops = synth.c5_chain()
+    for name, n in (("c5_small", 1 << 16), ("c5_large", (1 << 24) if quick else (1 << 28))):
+        xin = tdev(synth.c5_inputs(n), "f16")
+        yo = torch.empty_like(xin)
+        W[name] = dict(
+            desc=f"seeded 29-op fp16 chain, {n:,} elements",
+            fused=(lambda xin=xin, yo=yo: npa.fuse_chain(ops, [xin], yo)),
+            unfused=(lambda xin=xin, yo=yo: npa.unfused_chain(ops, [xin], yo)),
+            bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29, kernel="chain_vec<_Float16")
+    return W
+
+
+# ------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(synth, quick: bool):
+    """The oracle, untuned, timed on the host on a bounded sample of every config;
+    the step time is extrapolated from each config's measured oracle rate."""
+    import numpy as np
+    import oracle
+    rates = {}
+    samples = []
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    a, b = synth.c1_inputs()
+    rates["c1"] = 12 * a.size / timed(lambda: oracle.chain(synth.C1_CHAIN, [a, b], 0))
+    samples.append("c1 full")
+    lv = synth.c2_inputs()
+    hw = [(h, w) for h, w, _ in synth.YOLO_LEVELS]
+    anc = np.array(synth.YOLO_ANCHORS, np.float32).reshape(3, 3, 2)
+    rates["c2"] = det_bytes(hw)[0] / timed(
+        lambda: oracle.det_decode(lv, hw, [8.0, 16.0, 32.0], anc, 3, 85, in_dt=1))
+    samples.append("c2 full")
+    rows = 256 if quick else 2048
+    x, r, w = synth.c3_inputs(rows=rows)
+    rates["c3"] = rms_bytes(rows, 4096)[0] / timed(lambda: oracle.add_rmsnorm(x, r, w, 1e-6, 2))
+    samples.append(f"c3 {rows} of 16384 rows")
+    toks = 256 if quick else 2048
+    qkv = synth.c4_inputs(tokens=toks)
+    rates["c4"] = rope_bytes(toks, 24, 128)[0] / timed(
+        lambda: oracle.qkv_rope(qkv, 24, 128, 10000.0, 0.08838834764831845, 2))
+    samples.append(f"c4 {toks} of 16384 tokens")
+    ops = synth.c5_chain()
+    xs = synth.c5_inputs(1 << 16)
+    rates["c5_small"] = 4 * xs.size / timed(lambda: oracle.chain(ops, [xs], 1))
+    samples.append("c5 65,536 full")
+    nl = (1 << 20) if quick else (1 << 23)
+    xl = synth.c5_inputs(nl, seed=77)
+    rates["c5_large"] = 4 * nl / timed(lambda: oracle.chain(ops, [xl], 1))
+    samples.append(f"c5 {nl:,} of 268,435,456 elements")
+    return rates, "; ".join(samples)
+
+
+# ------------------------------------------------------------------- main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--trials", type=int, default=11)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--quick", action="store_true", help="reduced sizes (smoke runs only)")
+    ap.add_argument("--profile", action="store_true",
+                    help="only a few launches of each kernel (for rocprofv3 runs)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the fused chains shard without any exchange, so "
+              "there is no multi-GPU path to run (use --gpus 1).", file=sys.stderr)
+        return 2
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        print("bench.py runs as a single process on one GPU.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import synth
+    import norm_pass_amd as npa
+
+    t_setup = time.perf_counter()
+    npa.np_init(0)
+    props = torch.cuda.get_device_properties(0)
+    W = build_workloads(torch, npa, synth, args.quick)
+    torch.cuda.synchronize()
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s on {props.name} "
+        f"({getattr(props, 'gcnArchName', '?')}, {props.multi_processor_count} CUs)")
+
+    if args.profile:
+        # a copy of known size for counter calibration, then each kernel a few times
+        import numpy as _np  # noqa: F401
+        n = 1 << 28
+        src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            npa.unfused_chain([(synth.LOAD, 0, 0.0)], [src], dst)
+        for name, w in W.items():
+            for _ in range(3):
+                w["fused"]()
+            for _ in range(2):
+                w["unfused"]()
+        torch.cuda.synchronize()
+        log("[bench] profile pass done")
+        return 0
+
+    order = ["c1", "c2", "c3", "c4", "c5_small", "c5_large"]
+    step_fns = [W[k]["fused"] for k in order]
+    step_bytes = sum(W[k]["bytes"] for k in order)
+
+    def step():
+        for f in step_fns:
+            f()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(args.steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = s.elapsed_time(e) / 1e3 / args.steps
+    log(f"[bench] {args.steps} steps: {step_s * 1e6:.1f} us/step (wall {wall:.3f}s)")
+
+    per = {}
+    for k in order:
+        w = W[k]
+        reps = pick_reps(torch, w["fused"])
+        f_med, f_p10, f_p90 = time_calls(torch, w["fused"], reps, args.trials)
+        reps_u = pick_reps(torch, w["unfused"])
+        u_med, _, _ = time_calls(torch, w["unfused"], reps_u, max(5, args.trials // 2))
+        gbps = w["bytes"] / f_med / 1e9
+        per[k] = {
+            "desc": w["desc"], "us_med": round(f_med * 1e6, 3), "us_p10": round(f_p10 * 1e6, 3),
+            "us_p90": round(f_p90 * 1e6, 3), "GBps": round(gbps, 1),
+            "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 1), "bytes": w["bytes"],
+            "unfused": {"launches": w["launches"], "us_med": round(u_med * 1e6, 3),
+                        "GBps": round(w["unfused_bytes"] / u_med / 1e9, 1),
+                        "bytes": w["unfused_bytes"]},
+            "speedup": round(u_med / f_med, 2),
+        }
+        log(f"[bench] {k}: fused {f_med * 1e6:.2f} us ({gbps:.0f} GB/s), "
+            f"unfused {u_med * 1e6:.2f} us x{w['launches']} launches")
+
+    # launch-cost model (NaiveRT write-up): the pages' own instance, then ours
+    pages = cost_model(PAGES_COST_MODEL["t_unfused_ms"], PAGES_COST_MODEL["t_fused_ms"],
+                       PAGES_COST_MODEL["k"])
+    small = per["c5_small"]
+    ours = cost_model(small["unfused"]["us_med"], small["us_med"], 29)
+    reps = 50
+    direct, _, _ = time_calls(torch, lambda: npa.np_empty_launches(29), reps, 5)
+    ours["L_direct_us"] = round(direct * 1e6 / 29, 3)
+    for key in ("L", "T"):
+        ours[key] = round(ours[key], 3)
+
+    # roofline of the dominant kernel of the step
+    dom = max(order, key=lambda k: per[k]["us_med"])
+    d = per[dom]
+    achieved = d["bytes"] / (d["us_med"] * 1e-6) / 1e9
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(dom)}
+
+    cpu = None
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        rates, sample = cpu_baseline(synth, args.quick)
+        est = sum(W[k]["bytes"] / rates[k] for k in order)
+        cpu = {"value": round(step_bytes / est / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "sample": sample,
+               "per_config_GBps": {k: round(v / 1e9, 4) for k, v in rates.items()},
+               "seconds": round(time.perf_counter() - t0, 1)}
+        log(f"[bench] cpu oracle {cpu['value']} GB/s ({cpu['seconds']} s)")
+
+    value = step_bytes / step_s / 1e9
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) + per-call us, fused vs N-launch unfused",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Philox normals; see synth/)",
+        "config": {"workload": "one fused pass over all five chains: C1 fp32 relu(a+b)*0.5 1M; "
+                               "C2 YOLO decode fp16 3 levels; C3 bf16 add+RMSNorm 16384x4096; "
+                               "C4 bf16 QKV split+RoPE+scale 16384x24x128; C5 29-op fp16 chain "
+                               "65,536 and 268,435,456",
+                   "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 1),
+                   "step_bytes": step_bytes, "quick": args.quick},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_config": per,
+        "cost_model": {"pages": {k: round(v, 4) for k, v in pages.items()}, "c5_small_us": ours},
+        "env": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
+                "cus": props.multi_processor_count, "torch": torch.__version__},
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

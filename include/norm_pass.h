@@ -1,0 +1,236 @@
+/*
+ * norm_pass_amd -- single-pass fused kernels for chains of small memory-bound
+ * operators on AMD Instinct MI355X (gfx950).
+ *
+ * The problem (DeepJIT write-up, hotelren.com/news/5350627, section 1.1; the
+ * NaiveRT write-up, zhaixingw.cn/coding/291.html, "the 75% that fusion
+ * saves"): a chain of N small elementwise / normalisation / layout operators,
+ * run as N kernels, pays N launches and N full read/write round trips of its
+ * tensors through HBM. Each call below runs the whole chain as ONE kernel that
+ * reads each input from HBM once and writes each output once. The unfused_*
+ * calls run the same chains as one kernel per operator (the N-launch
+ * baseline the fused calls are measured against).
+ *
+ * Calling convention (the C-ABI operator contract of the page
+ * "CUDA算子与AI运行时：从内存对齐到stream调度的落地实践", gtnt.cn/news/145880,
+ * sections 4.1 and 4.3, and its stream advice in sections 2.2 and 5.2):
+ *  - plain pointers and sizes; no C++ types or exceptions cross this boundary;
+ *  - every call returns an int status: NP_OK (0) on success, a negative code on
+ *    failure, with a thread-local message from np_last_error();
+ *  - every call enqueues its kernel(s) on the caller's stream and returns
+ *    without synchronising; 0 means the legacy null stream (allowed, but it
+ *    serialises with other streams); a fault during execution surfaces at the
+ *    caller's next synchronisation;
+ *  - all device buffers belong to the caller and must stay alive until the
+ *    stream work completes (DeepJIT write-up, section 6.5); the library
+ *    allocates no device memory; host arrays (ops, sizes, strides, anchors) are
+ *    read during the call only;
+ *  - pointers need not be aligned: a buffer that is not 16-byte aligned, or a
+ *    size that is not a multiple of the 16-byte vector width, takes a scalar
+ *    path instead of an error (DeepJIT write-up, sections 4.2 and 6.5);
+ *  - an output may alias an input exactly (same pointer, same shape) for the
+ *    elementwise and norm calls; partial overlap is undefined; the QKV and
+ *    detection calls forbid aliasing;
+ *  - the first call on a device checks that it is a gfx950 GPU (NP_EDEVICE
+ *    otherwise); argument checks run before any HIP call.
+ * Floating point: fp16 / bf16 data are computed in fp32 and rounded once per
+ * stored value, to nearest even (TeleTron write-up, 2kiu.com/news/5927820,
+ * section 3.4: element-wise work in high precision).
+ */
+#ifndef NORM_PASS_H
+#define NORM_PASS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NP_VERSION 1
+
+/* status codes */
+#define NP_OK 0
+#define NP_EINVAL (-1)   /* invalid argument (nothing was launched) */
+#define NP_ELAUNCH (-3)  /* a HIP call or kernel launch failed */
+#define NP_ECOMPILE (-4) /* runtime specialisation failed (generic kernel stays in use) */
+#define NP_EDEVICE (-5)  /* no device, or not a gfx950 device */
+
+typedef enum { NP_F32 = 0, NP_F16 = 1, NP_BF16 = 2 } np_dtype;
+
+/* Elementwise chain ops (DeepJIT write-up, sections 4.1-4.2). The chain keeps one
+ * running fp32 value per element. */
+typedef enum {
+  NP_LOAD = 0,      /* v = input[arg][i]                         */
+  NP_ADD_IN = 1,    /* v = v + input[arg][i]                     */
+  NP_MUL_IN = 2,    /* v = v * input[arg][i]                     */
+  NP_ADD_C = 3,     /* v = v + c                                 */
+  NP_MUL_C = 4,     /* v = v * c                                 */
+  NP_SCALE = 5,     /* v = v * c (same as NP_MUL_C)              */
+  NP_RELU = 6,      /* v = v > 0 ? v : 0 (never -0; NaN -> 0)    */
+  NP_SIGMOID = 7,   /* v = 1 / (1 + exp(-v))                     */
+  NP_EXP = 8,       /* v = exp(v)                                */
+  NP_TANH = 9,      /* v = tanh(v)                               */
+  NP_CAST_F16 = 10, /* v = fp16(v), round to nearest even        */
+  NP_CAST_BF16 = 11 /* v = bf16(v), round to nearest even        */
+} np_op_kind;
+
+typedef struct {
+  int32_t kind; /* np_op_kind */
+  int32_t arg;  /* input index for NP_LOAD / NP_ADD_IN / NP_MUL_IN, else 0 */
+  float c;      /* constant for NP_ADD_C / NP_MUL_C / NP_SCALE, else 0 */
+} np_op;
+
+#define NP_MAX_OPS 32
+#define NP_MAX_INPUTS 4
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Check that `device` is a gfx950 GPU and make the library ready on it.
+ * Optional: the first call on a device does it lazily. Returns NP_EDEVICE if
+ * the device is missing or not gfx950. */
+int np_init(int device);
+
+/* Message for the last failing call on this thread ("" if none). The pointer
+ * stays valid until the next call on this thread. */
+const char* np_last_error(void);
+
+int np_version(void);
+
+/* Release runtime-compiled modules. Every stream that ran a specialised chain
+ * must have been synchronised first (DeepJIT write-up, section 6.4: unloading a
+ * module with work still queued faults). Safe to call more than once. */
+void np_shutdown(void);
+
+/* Generate and compile (without loading) the specialised kernel source that
+ * fuse_chain_prepare would build for this chain; reports the compile time in
+ * milliseconds and the code-object size. Needs no GPU (the DeepJIT write-up,
+ * sections 3.3 and 6.2, quotes tens to hundreds of ms per runtime compile).
+ * Returns NP_OK, NP_EINVAL or NP_ECOMPILE. compile_ms / code_bytes may be NULL. */
+int np_chain_compile(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt, np_dtype out_dt,
+                     int64_t n, double* compile_ms, size_t* code_bytes);
+
+/* --------------------------------------------------------- fused calls */
+
+/*
+ * fuse_chain: one elementwise chain in one kernel (DeepJIT write-up, sections
+ * 3.2-4.2: fused add -> relu -> scale, the fused multi-input chain and its
+ * 16-byte vector form). ops[0] must be NP_LOAD. inputs: n_inputs (1..4) dense
+ * 1-D device arrays of n elements of in_dt, no broadcasting. out: n elements of
+ * out_dt. The running value is fp32; it is rounded only at NP_CAST_* ops and
+ * once at the store. n == 0 returns NP_OK without a launch. Uses a runtime
+ * specialisation prepared by fuse_chain_prepare for this exact op list, dtypes
+ * and n when one exists, else the precompiled generic kernel; never compiles.
+ * Errors: NP_EINVAL for n_ops outside 1..NP_MAX_OPS, an unknown op, an input
+ * index >= n_inputs, a NULL pointer, n < 0.
+ */
+int fuse_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_inputs,
+               np_dtype in_dt, void* out, np_dtype out_dt, int64_t n, hipStream_t stream);
+
+/*
+ * fuse_chain_prepare: specialise a chain at warm-up time (DeepJIT write-up,
+ * sections 3.1 and 3.3: generate source with the sizes, vector width and op list
+ * as constants, compile at run time, cache the module under a hash of source,
+ * architecture and options). n_or_0 == 0 prepares a kernel for any n. Compiles
+ * with hipRTC for gfx950 on the current device; cached per process. Returns
+ * NP_ECOMPILE (the generic kernel remains in use) if compilation fails, and
+ * NP_OK without compiling when NP_DISABLE_RTC=1 is set in the environment.
+ */
+int fuse_chain_prepare(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt,
+                       np_dtype out_dt, int64_t n_or_0);
+
+/*
+ * fuse_det_decode: YOLO-style detection-head decode in one kernel (DeepJIT
+ * write-up, sections 1.1, 2.2 and 5.2: the sigmoid / exp / mul / add / slice /
+ * concat / cast tail of a detector). level_logits[l]: device NCHW tensor
+ * [batch, n_anchors * n_ch, H[l], W[l]] of in_dt, channel a * n_ch + k.
+ * strides[l] (pixels per cell), anchors_wh[(l * n_anchors + a) * 2 + {0,1}]
+ * (anchor w, h in pixels): host arrays. out: device fp32
+ * [batch, sum_l n_anchors * H[l] * W[l], n_ch], rows ordered level, anchor,
+ * y, x; for row (l, a, y, x) and logit t_k:
+ *   out[0] = (sigmoid(t0) + x) * stride   out[1] = (sigmoid(t1) + y) * stride
+ *   out[2] = exp(t2) * anchor_w           out[3] = exp(t3) * anchor_h
+ *   out[k] = sigmoid(t_k) for k >= 4.
+ * Limits: 1 <= n_levels <= 8, 1 <= n_anchors <= 16, 5 <= n_ch <= 1024.
+ * Errors: NP_EINVAL on NULL pointers or out-of-range sizes.
+ */
+int fuse_det_decode(const void* const* level_logits, int n_levels, const int32_t* H,
+                    const int32_t* W, const float* strides, const float* anchors_wh,
+                    int n_anchors, int n_ch, int batch, np_dtype in_dt, float* out,
+                    hipStream_t stream);
+
+/*
+ * fuse_add_rmsnorm: residual add + RMSNorm in one pass (TeleTron write-up,
+ * sections 3.3 and 4.2: per-row reduction then elementwise scaling, fp32
+ * accumulation, eps inside the square root). Row-major contiguous [rows, cols]
+ * of dt:
+ *   h = x + r (rounded to dt, stored to h_out, and used by the norm)
+ *   out = h / sqrt(mean_j(h_j^2) + eps) * w_j
+ * r == NULL: h = x. w == NULL: weight 1. h_out == NULL: h is not stored.
+ * Errors: NP_EINVAL for NULL x/out, rows < 0, cols < 1 or cols > 2^24, eps not
+ * finite and > 0.
+ */
+int fuse_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out, void* out,
+                     int64_t rows, int64_t cols, float eps, np_dtype dt, hipStream_t stream);
+
+/*
+ * fuse_qkv_rope: QKV split + rotate-half RoPE + Q scale in one pass (TeleTron
+ * write-up, section 3.1: the multi-head split, rotary position encoding and
+ * scaling after the QKV projection). qkv: [T, 3, n_heads, head_dim] row-major
+ * (q, k, v outermost per token). q, k, v: [n_heads, T, head_dim]. For position
+ * p = positions[t] (positions == NULL: p = t) and i < head_dim/2:
+ *   inv_i = fp32(base^(-2i/head_dim)), theta = fp32(fp32(p) * inv_i),
+ *   o[i] = u cos(theta) - w sin(theta), o[i + head_dim/2] = w cos + u sin,
+ *   with (u, w) = (x[i], x[i + head_dim/2]); Q = o * q_scale, K = o, V = x.
+ * positions: device int32 [T] or NULL. Limits: head_dim even, <= 512.
+ * Errors: NP_EINVAL for NULL buffers, T < 0, n_heads < 1, bad head_dim,
+ * base <= 0, non-finite q_scale.
+ */
+int fuse_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n_heads,
+                  int head_dim, const int32_t* positions, float base, float q_scale,
+                  np_dtype dt, hipStream_t stream);
+
+/* ------------------------------------------ unfused (N-launch) baselines */
+/* The same chains as one kernel per operator, each kernel reading its operands
+ * from HBM and storing its result in the storage type before the next launch
+ * (NaiveRT write-up: K calls of cost L + T_k each; DeepJIT write-up, section
+ * 1.1: every small kernel reads and writes the whole tensor). Results follow
+ * the unfused definitions: rounding after every operator. */
+
+/* One launch per op after the initial NP_LOAD (a lone load is one copy
+ * launch), in place in `out`. Requires in_dt == out_dt (the storage type). */
+int unfused_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_inputs,
+                  np_dtype in_dt, void* out, np_dtype out_dt, int64_t n, hipStream_t stream);
+
+/* 7 launches per level (permute to rows of n_ch; sigmoid on x, y; sigmoid on
+ * objectness and classes; exp on w, h; times anchor; plus grid; times stride),
+ * then one concat and one cast to fp32: 7 * n_levels + 2 launches.
+ * workspace: device buffer of at least 2 * total_rows * n_ch * sizeof(in_dt)
+ * bytes (total_rows = batch * sum_l n_anchors * H[l] * W[l]). */
+int unfused_det_decode(const void* const* level_logits, int n_levels, const int32_t* H,
+                       const int32_t* W, const float* strides, const float* anchors_wh,
+                       int n_anchors, int n_ch, int batch, np_dtype in_dt, float* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* 6 launches: add; square; row mean; (+eps, 1/sqrt); times rstd; times w.
+ * workspace: at least (rows * cols + 2 * rows) * sizeof(dt) bytes, plus
+ * rows * cols * sizeof(dt) when h_out == NULL. w == NULL skips the last launch. */
+int unfused_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out, void* out,
+                        int64_t rows, int64_t cols, float eps, np_dtype dt, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* 4 launches: split to head-major; RoPE on Q; RoPE on K; scale Q. */
+int unfused_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n_heads,
+                     int head_dim, const int32_t* positions, float base, float q_scale,
+                     np_dtype dt, hipStream_t stream);
+
+/* An empty kernel launched `count` times on the stream (direct measurement of
+ * the per-launch cost, the NaiveRT write-up's "29 empty calls"). */
+int np_empty_launches(int count, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NORM_PASS_H */

@@ -1,0 +1,255 @@
+"""Python binding of libnorm_pass_amd.so (ctypes; argument marshalling only).
+
+Every function here has the name of the C entry point it calls (declared in
+``include/norm_pass.h``) and takes torch tensors on the GPU for the device
+buffers: it passes ``data_ptr()``s, sizes and the current HIP stream, and
+raises :class:`NPError` with the library's message when the call fails. All
+computation happens in the library's HIP kernels; torch only owns memory and
+streams. Importing this module fails loudly when the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnorm_pass_amd.so")
+
+NP_OK, NP_EINVAL, NP_ELAUNCH, NP_ECOMPILE, NP_EDEVICE = 0, -1, -3, -4, -5
+NP_F32, NP_F16, NP_BF16 = 0, 1, 2
+(NP_LOAD, NP_ADD_IN, NP_MUL_IN, NP_ADD_C, NP_MUL_C, NP_SCALE, NP_RELU, NP_SIGMOID, NP_EXP,
+ NP_TANH, NP_CAST_F16, NP_CAST_BF16) = range(12)
+MAX_OPS, MAX_INPUTS = 32, 4
+
+_DT = {torch.float32: NP_F32, torch.float16: NP_F16, torch.bfloat16: NP_BF16}
+_SIZE = {NP_F32: 4, NP_F16: 2, NP_BF16: 2}
+
+
+class NPError(RuntimeError):
+    def __init__(self, code: int, fn: str, msg: str):
+        super().__init__(f"{fn} failed ({code}): {msg}")
+        self.code = code
+
+
+class np_op(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("arg", C.c_int32), ("c", C.c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950)")
+    L = C.CDLL(LIB_PATH)
+    P, I, I64, F, S = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+    OPS = C.POINTER(np_op)
+    sig = {
+        "np_init": [I],
+        "np_version": [],
+        "np_shutdown": [],
+        "np_chain_compile": [OPS, I, I, I, I, I64, C.POINTER(C.c_double), C.POINTER(S)],
+        "fuse_chain": [OPS, I, P, I, I, P, I, I64, P],
+        "fuse_chain_prepare": [OPS, I, I, I, I, I64],
+        "fuse_det_decode": [P, I, P, P, P, P, I, I, I, I, P, P],
+        "fuse_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I, P],
+        "fuse_qkv_rope": [P, P, P, P, I64, I, I, P, F, F, I, P],
+        "unfused_chain": [OPS, I, P, I, I, P, I, I64, P],
+        "unfused_det_decode": [P, I, P, P, P, P, I, I, I, I, P, P, S, P],
+        "unfused_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I, P, S, P],
+        "unfused_qkv_rope": [P, P, P, P, I64, I, I, P, F, F, I, P],
+        "np_empty_launches": [I, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = None if name == "np_shutdown" else C.c_int
+    L.np_last_error.restype = C.c_char_p
+    L.np_last_error.argtypes = []
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(rc: int, fn: str):
+    if rc != NP_OK:
+        raise NPError(rc, fn, _lib.np_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _keep(stream, *tensors):
+    """Tie tensor lifetimes to a non-current stream (caching-allocator safety)."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def _ops(ops):
+    arr = (np_op * len(ops))()
+    for i, (k, a, c) in enumerate(ops):
+        arr[i].kind, arr[i].arg, arr[i].c = int(k), int(a), float(c)
+    return arr, len(ops)
+
+
+def dtype_code(t) -> int:
+    return _DT[t.dtype if isinstance(t, torch.Tensor) else t]
+
+
+# ------------------------------------------------------------------ helpers
+
+def np_init(device: int = 0):
+    _check(_lib.np_init(device), "np_init")
+
+
+def np_version() -> int:
+    return _lib.np_version()
+
+
+def np_shutdown():
+    _lib.np_shutdown()
+
+
+def np_chain_compile(ops, n_inputs: int, in_dt: int, out_dt: int, n: int = 0):
+    """Compile (not load) the specialised source; returns (compile_ms, code_bytes)."""
+    arr, k = _ops(ops)
+    ms = C.c_double(0)
+    nb = C.c_size_t(0)
+    _check(_lib.np_chain_compile(arr, k, n_inputs, in_dt, out_dt, n, C.byref(ms), C.byref(nb)),
+           "np_chain_compile")
+    return ms.value, nb.value
+
+
+def np_empty_launches(count: int, stream=None):
+    _check(_lib.np_empty_launches(count, _stream(stream)), "np_empty_launches")
+
+
+# -------------------------------------------------------------- fused calls
+
+def fuse_chain(ops, inputs, out, stream=None):
+    """out[i] = chain(inputs[0][i], ...); ops = [(kind, arg, const), ...]."""
+    arr, k = _ops(ops)
+    n = out.numel()
+    ptrs = (C.c_void_p * len(inputs))(*[t.data_ptr() for t in inputs])
+    _keep(stream, out, *inputs)
+    _check(_lib.fuse_chain(arr, k, ptrs, len(inputs), dtype_code(inputs[0]), _ptr(out),
+                           dtype_code(out), n, _stream(stream)), "fuse_chain")
+    return out
+
+
+def fuse_chain_prepare(ops, n_inputs: int, in_dt: int, out_dt: int, n: int = 0):
+    arr, k = _ops(ops)
+    _check(_lib.fuse_chain_prepare(arr, k, n_inputs, in_dt, out_dt, n), "fuse_chain_prepare")
+
+
+def _det_args(levels, strides, anchors):
+    n_levels = len(levels)
+    H = (C.c_int32 * n_levels)(*[t.shape[2] for t in levels])
+    W = (C.c_int32 * n_levels)(*[t.shape[3] for t in levels])
+    st = (C.c_float * n_levels)(*[float(s) for s in strides])
+    flat = [float(v) for lvl in anchors for pair in lvl for v in pair]
+    an = (C.c_float * len(flat))(*flat)
+    ptrs = (C.c_void_p * n_levels)(*[t.data_ptr() for t in levels])
+    return ptrs, n_levels, H, W, st, an
+
+
+def det_rows(levels, n_anchors: int) -> int:
+    return sum(n_anchors * t.shape[2] * t.shape[3] for t in levels)
+
+
+def fuse_det_decode(levels, strides, anchors, out, n_anchors: int = 3, n_ch: int = 85,
+                    stream=None):
+    """levels: [batch, n_anchors*n_ch, H, W] tensors; anchors: [[(w, h)] * n_anchors] per level;
+    out: fp32 [batch, rows, n_ch]."""
+    ptrs, nl, H, W, st, an = _det_args(levels, strides, anchors)
+    _keep(stream, out, *levels)
+    _check(_lib.fuse_det_decode(ptrs, nl, H, W, st, an, n_anchors, n_ch, levels[0].shape[0],
+                                dtype_code(levels[0]), _ptr(out), _stream(stream)),
+           "fuse_det_decode")
+    return out
+
+
+def fuse_add_rmsnorm(x, r, w, h_out, out, eps: float = 1e-6, stream=None):
+    rows, cols = x.shape[0], x.shape[-1]
+    _keep(stream, x, r, w, h_out, out)
+    _check(_lib.fuse_add_rmsnorm(_ptr(x), _ptr(r), _ptr(w), _ptr(h_out), _ptr(out), rows, cols,
+                                 eps, dtype_code(x), _stream(stream)), "fuse_add_rmsnorm")
+    return h_out, out
+
+
+def fuse_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
+                  base: float = 10000.0, q_scale: float | None = None, stream=None):
+    if q_scale is None:
+        q_scale = 1.0 / math.sqrt(head_dim)
+    _keep(stream, qkv, q, k, v, positions)
+    _check(_lib.fuse_qkv_rope(_ptr(qkv), _ptr(q), _ptr(k), _ptr(v), qkv.shape[0], n_heads,
+                              head_dim, _ptr(positions), base, q_scale, dtype_code(qkv),
+                              _stream(stream)), "fuse_qkv_rope")
+    return q, k, v
+
+
+# ------------------------------------------------------- unfused baselines
+
+def unfused_chain(ops, inputs, out, stream=None):
+    arr, k = _ops(ops)
+    ptrs = (C.c_void_p * len(inputs))(*[t.data_ptr() for t in inputs])
+    _keep(stream, out, *inputs)
+    _check(_lib.unfused_chain(arr, k, ptrs, len(inputs), dtype_code(inputs[0]), _ptr(out),
+                              dtype_code(out), out.numel(), _stream(stream)), "unfused_chain")
+    return out
+
+
+def det_workspace_bytes(levels, n_anchors: int = 3, n_ch: int = 85) -> int:
+    return 2 * levels[0].shape[0] * det_rows(levels, n_anchors) * n_ch * levels[0].element_size()
+
+
+def unfused_det_decode(levels, strides, anchors, out, workspace, n_anchors: int = 3,
+                       n_ch: int = 85, stream=None):
+    ptrs, nl, H, W, st, an = _det_args(levels, strides, anchors)
+    _keep(stream, out, workspace, *levels)
+    _check(_lib.unfused_det_decode(ptrs, nl, H, W, st, an, n_anchors, n_ch, levels[0].shape[0],
+                                   dtype_code(levels[0]), _ptr(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "unfused_det_decode")
+    return out
+
+
+def rmsnorm_workspace_bytes(rows: int, cols: int, dtype, with_h: bool = True) -> int:
+    es = _SIZE[dtype_code(dtype)]
+    return (rows * cols + 2 * rows + (0 if with_h else rows * cols)) * es
+
+
+def unfused_add_rmsnorm(x, r, w, h_out, out, workspace, eps: float = 1e-6, stream=None):
+    rows, cols = x.shape[0], x.shape[-1]
+    _keep(stream, x, r, w, h_out, out, workspace)
+    _check(_lib.unfused_add_rmsnorm(_ptr(x), _ptr(r), _ptr(w), _ptr(h_out), _ptr(out), rows, cols,
+                                    eps, dtype_code(x), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "unfused_add_rmsnorm")
+    return h_out, out
+
+
+def unfused_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
+                     base: float = 10000.0, q_scale: float | None = None, stream=None):
+    if q_scale is None:
+        q_scale = 1.0 / math.sqrt(head_dim)
+    _keep(stream, qkv, q, k, v, positions)
+    _check(_lib.unfused_qkv_rope(_ptr(qkv), _ptr(q), _ptr(k), _ptr(v), qkv.shape[0], n_heads,
+                                 head_dim, _ptr(positions), base, q_scale, dtype_code(qkv),
+                                 _stream(stream)), "unfused_qkv_rope")
+    return q, k, v

@@ -1,0 +1,439 @@
+// C ABI of the fused-chain library: argument validation, dispatch to the
+// kernels, error reporting. Validation is pure host code that runs before any
+// HIP call, so a rejected call touches no device. Conventions follow the C-ABI
+// operator contract of the page "CUDA算子与AI运行时" (gtnt.cn/news/145880),
+// sections 4.1 and 4.3: raw pointers and sizes in, an int status out, the
+// caller's stream, no synchronisation inside, no exceptions across the ABI.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "internal.h"
+#include "rtc.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return NP_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(NP_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dt(int dt) { return dt == NP_F32 || dt == NP_F16 || dt == NP_BF16; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Per-device gfx950 check, done once per device and cached.
+std::mutex g_dev_mu;
+int g_dev_state[64];  // 0 unknown, 1 gfx950, -1 rejected
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    return fail(NP_EDEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(NP_EDEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (g_dev_state[dev] < 0)
+      return fail(NP_EDEVICE, "device %d is %s, this library is built for gfx950", dev,
+                  prop.gcnArchName);
+  }
+  if (g_dev_state[dev] < 0) return fail(NP_EDEVICE, "device %d is not gfx950", dev);
+  return NP_OK;
+}
+
+int validate_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_inputs,
+                   int in_dt, const void* out, int out_dt, int64_t n) {
+  if (!ops) return fail(NP_EINVAL, "ops is NULL");
+  if (n_ops < 1 || n_ops > NP_MAX_OPS)
+    return fail(NP_EINVAL, "n_ops = %d, must be 1..%d", n_ops, NP_MAX_OPS);
+  if (n_inputs < 1 || n_inputs > NP_MAX_INPUTS)
+    return fail(NP_EINVAL, "n_inputs = %d, must be 1..%d", n_inputs, NP_MAX_INPUTS);
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return fail(NP_EINVAL, "unknown dtype");
+  if (n < 0) return fail(NP_EINVAL, "n = %lld < 0", (long long)n);
+  if (ops[0].kind != NP_LOAD) return fail(NP_EINVAL, "ops[0] must be NP_LOAD");
+  for (int i = 0; i < n_ops; ++i) {
+    const int k = ops[i].kind;
+    if (k < NP_LOAD || k > NP_CAST_BF16) return fail(NP_EINVAL, "ops[%d]: unknown kind %d", i, k);
+    if ((k == NP_LOAD || k == NP_ADD_IN || k == NP_MUL_IN) &&
+        (ops[i].arg < 0 || ops[i].arg >= n_inputs))
+      return fail(NP_EINVAL, "ops[%d]: input index %d out of range", i, ops[i].arg);
+  }
+  if (n == 0) return NP_OK;
+  if (!inputs) return fail(NP_EINVAL, "inputs is NULL");
+  for (int j = 0; j < n_inputs; ++j)
+    if (!inputs[j]) return fail(NP_EINVAL, "inputs[%d] is NULL", j);
+  if (!out) return fail(NP_EINVAL, "out is NULL");
+  return NP_OK;
+}
+
+np::ChainArgs chain_args(const np_op* ops, int n_ops, const void* const* inputs, int n_inputs,
+                         void* out, int64_t n) {
+  np::ChainArgs a{};
+  a.n_ops = n_ops;
+  for (int i = 0; i < n_ops; ++i) {
+    a.kind[i] = ops[i].kind;
+    a.arg[i] = ops[i].arg;
+    a.c[i] = ops[i].c;
+  }
+  for (int j = 0; j < n_inputs; ++j) a.in[j] = inputs[j];
+  a.out = out;
+  a.n = n;
+  return a;
+}
+
+int validate_det(const void* const* lv, int n_levels, const int32_t* H, const int32_t* W,
+                 const float* strides, const float* anchors, int n_anchors, int n_ch, int batch,
+                 int in_dt, const float* out) {
+  if (!lv || !H || !W || !strides || !anchors || !out) return fail(NP_EINVAL, "NULL argument");
+  if (n_levels < 1 || n_levels > 8) return fail(NP_EINVAL, "n_levels = %d, must be 1..8", n_levels);
+  if (n_anchors < 1 || n_anchors > 16)
+    return fail(NP_EINVAL, "n_anchors = %d, must be 1..16", n_anchors);
+  if (n_ch < 5 || n_ch > 1024) return fail(NP_EINVAL, "n_ch = %d, must be 5..1024", n_ch);
+  if (batch < 1) return fail(NP_EINVAL, "batch = %d < 1", batch);
+  if (!valid_dt(in_dt)) return fail(NP_EINVAL, "unknown dtype");
+  int64_t rows = 0;
+  for (int l = 0; l < n_levels; ++l) {
+    if (!lv[l]) return fail(NP_EINVAL, "level_logits[%d] is NULL", l);
+    if (H[l] < 1 || W[l] < 1 || (int64_t)H[l] * W[l] > (1 << 28))
+      return fail(NP_EINVAL, "level %d: bad H x W = %d x %d", l, H[l], W[l]);
+    if (!std::isfinite(strides[l])) return fail(NP_EINVAL, "level %d: stride not finite", l);
+    rows += (int64_t)n_anchors * H[l] * W[l];
+  }
+  if ((int64_t)batch * rows * n_ch >= (int64_t)1 << 40) return fail(NP_EINVAL, "output too large");
+  return NP_OK;
+}
+
+int validate_norm(const void* x, const void* out, const void* h, int64_t rows, int64_t cols,
+                  float eps, int dt) {
+  if (!x || !out) return fail(NP_EINVAL, "x or out is NULL");
+  if (!valid_dt(dt)) return fail(NP_EINVAL, "unknown dtype");
+  if (rows < 0 || rows >= ((int64_t)1 << 31)) return fail(NP_EINVAL, "rows = %lld out of range", (long long)rows);
+  if (cols < 1 || cols > ((int64_t)1 << 24)) return fail(NP_EINVAL, "cols = %lld out of range", (long long)cols);
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(NP_EINVAL, "eps must be finite and > 0");
+  if (h && h == out) return fail(NP_EINVAL, "h_out and out must differ");
+  return NP_OK;
+}
+
+int validate_rope(const void* qkv, const void* q, const void* k, const void* v, int64_t T,
+                  int n_heads, int head_dim, float base, float q_scale, int dt) {
+  if (!qkv || !q || !k || !v) return fail(NP_EINVAL, "NULL buffer");
+  if (!valid_dt(dt)) return fail(NP_EINVAL, "unknown dtype");
+  if (T < 0 || T >= ((int64_t)1 << 31)) return fail(NP_EINVAL, "T out of range");
+  if (n_heads < 1 || n_heads > 4096) return fail(NP_EINVAL, "n_heads = %d out of range", n_heads);
+  if (head_dim < 2 || head_dim > 512 || (head_dim & 1))
+    return fail(NP_EINVAL, "head_dim = %d: must be even and <= 512", head_dim);
+  if (!(base > 0.0f) || !std::isfinite(base)) return fail(NP_EINVAL, "base must be > 0");
+  if (!std::isfinite(q_scale)) return fail(NP_EINVAL, "q_scale not finite");
+  if (qkv == q || qkv == k || qkv == v || q == k || q == v || k == v)
+    return fail(NP_EINVAL, "qkv, q, k, v must not alias");
+  return NP_OK;
+}
+
+// fp32(base^(-2i/head_dim)), evaluated in double and rounded once
+void inv_freq(float base, int head_dim, float* inv) {
+  for (int i = 0; i < head_dim / 2; ++i)
+    inv[i] = (float)std::pow((double)base, -2.0 * (double)i / (double)head_dim);
+}
+
+int fill_det_args(np::DetArgs& a, const void* const* lv, int n_levels, const int32_t* H,
+                  const int32_t* W, const float* strides, const float* anchors, int n_anchors,
+                  int n_ch, int batch, float* out) {
+  a = np::DetArgs{};
+  a.n_levels = n_levels;
+  a.n_anchors = n_anchors;
+  a.n_ch = n_ch;
+  a.batch = batch;
+  a.out = out;
+  int tp = (int)((32768 / (4 * n_ch)) & ~7);  // LDS tile <= 32 KiB
+  if (tp > 64) tp = 64;
+  if (tp < 8) tp = 8;
+  a.tile_cells = tp;
+  int64_t row = 0;
+  int64_t tiles_total = 0;
+  a.tile_start[0] = 0;
+  for (int l = 0; l < n_levels; ++l) {
+    a.H[l] = H[l];
+    a.W[l] = W[l];
+    a.in[l] = lv[l];
+    a.stride[l] = strides[l];
+    for (int j = 0; j < n_anchors * 2; ++j)
+      a.anchor[l * n_anchors * 2 + j] = anchors[l * n_anchors * 2 + j];
+    a.row_off[l] = row;
+    const int64_t hw = (int64_t)H[l] * W[l];
+    row += n_anchors * hw;
+    a.tiles[l] = (int32_t)((hw + tp - 1) / tp);
+    tiles_total += (int64_t)batch * n_anchors * a.tiles[l];
+    if (tiles_total >= ((int64_t)1 << 31)) return fail(NP_EINVAL, "too many tiles");
+    a.tile_start[l + 1] = (int32_t)tiles_total;
+  }
+  a.total_rows = row;
+  return NP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int np_init(int device) {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || device < 0 || device >= n)
+    return fail(NP_EDEVICE, "device %d not available (%d devices)", device, n);
+  e = hipSetDevice(device);
+  if (e != hipSuccess) return fail(NP_EDEVICE, "hipSetDevice: %s", hipGetErrorString(e));
+  int rc = check_device();
+  return rc == NP_OK ? ok() : rc;
+}
+
+const char* np_last_error(void) { return g_err.c_str(); }
+
+int np_version(void) { return NP_VERSION; }
+
+void np_shutdown(void) { np::rtc_clear(); }
+
+int fuse_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_inputs,
+               np_dtype in_dt, void* out, np_dtype out_dt, int64_t n, hipStream_t stream) {
+  int rc = validate_chain(ops, n_ops, inputs, n_inputs, in_dt, out, out_dt, n);
+  if (rc) return rc;
+  if (n == 0) return ok();
+  if ((rc = check_device())) return rc;
+  bool vec = aligned16(out);
+  for (int j = 0; j < n_inputs; ++j) vec = vec && aligned16(inputs[j]);
+  np::ChainArgs a = chain_args(ops, n_ops, inputs, n_inputs, out, n);
+  hipError_t e;
+  if (vec && np::rtc_launch(a, n_inputs, in_dt, out_dt, stream, &e)) {
+    if (e != hipSuccess) return hip_fail(e, "fuse_chain (specialised)");
+    return ok();
+  }
+  e = np::launch_chain(a, in_dt, out_dt, n_inputs, vec, stream);
+  if (e != hipSuccess) return hip_fail(e, "fuse_chain");
+  return ok();
+}
+
+int fuse_chain_prepare(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt,
+                       np_dtype out_dt, int64_t n_or_0) {
+  static const void* dummy[NP_MAX_INPUTS] = {&g_dev_state, &g_dev_state, &g_dev_state,
+                                              &g_dev_state};
+  int rc = validate_chain(ops, n_ops, dummy, n_inputs, in_dt, &g_dev_state, out_dt, n_or_0);
+  if (rc) return rc;
+  const char* dis = std::getenv("NP_DISABLE_RTC");
+  if (dis && std::strcmp(dis, "1") == 0) return ok();
+  if ((rc = check_device())) return rc;
+  std::string log;
+  np::ChainArgs a = chain_args(ops, n_ops, dummy, n_inputs, nullptr, n_or_0);
+  rc = np::rtc_prepare(a, n_inputs, in_dt, out_dt, &log);
+  if (rc == NP_ECOMPILE) return fail(NP_ECOMPILE, "runtime compile failed: %s", log.c_str());
+  if (rc) return fail(rc, "%s", log.c_str());
+  return ok();
+}
+
+int fuse_det_decode(const void* const* level_logits, int n_levels, const int32_t* H,
+                    const int32_t* W, const float* strides, const float* anchors_wh,
+                    int n_anchors, int n_ch, int batch, np_dtype in_dt, float* out,
+                    hipStream_t stream) {
+  int rc = validate_det(level_logits, n_levels, H, W, strides, anchors_wh, n_anchors, n_ch, batch,
+                        in_dt, out);
+  if (rc) return rc;
+  np::DetArgs a;
+  if ((rc = fill_det_args(a, level_logits, n_levels, H, W, strides, anchors_wh, n_anchors, n_ch,
+                          batch, out)))
+    return rc;
+  if ((rc = check_device())) return rc;
+  const int N = 16 / np::dt_size(in_dt);
+  bool vec = true;
+  for (int l = 0; l < n_levels; ++l)
+    vec = vec && aligned16(level_logits[l]) && ((int64_t)H[l] * W[l]) % N == 0;
+  hipError_t e = np::launch_det_decode(a, in_dt, vec, stream);
+  if (e != hipSuccess) return hip_fail(e, "fuse_det_decode");
+  return ok();
+}
+
+int fuse_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out, void* out,
+                     int64_t rows, int64_t cols, float eps, np_dtype dt, hipStream_t stream) {
+  int rc = validate_norm(x, out, h_out, rows, cols, eps, dt);
+  if (rc) return rc;
+  if (rows == 0) return ok();
+  if ((rc = check_device())) return rc;
+  const bool vec = aligned16(x) && aligned16(out) && (!r || aligned16(r)) &&
+                   (!w || aligned16(w)) && (!h_out || aligned16(h_out));
+  hipError_t e = np::launch_add_rmsnorm(x, r, w, h_out, out, rows, cols, eps, dt, vec, stream);
+  if (e != hipSuccess) return hip_fail(e, "fuse_add_rmsnorm");
+  return ok();
+}
+
+int fuse_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n_heads,
+                  int head_dim, const int32_t* positions, float base, float q_scale,
+                  np_dtype dt, hipStream_t stream) {
+  int rc = validate_rope(qkv, q, k, v, T, n_heads, head_dim, base, q_scale, dt);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if ((rc = check_device())) return rc;
+  np::RopeArgs a{};
+  a.qkv = qkv;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.pos = positions;
+  a.T = T;
+  a.H = n_heads;
+  a.D = head_dim;
+  a.q_scale = q_scale;
+  inv_freq(base, head_dim, a.inv);
+  const bool vec = aligned16(qkv) && aligned16(q) && aligned16(k) && aligned16(v);
+  hipError_t e = np::launch_qkv_rope(a, dt, vec, stream);
+  if (e != hipSuccess) return hip_fail(e, "fuse_qkv_rope");
+  return ok();
+}
+
+int unfused_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_inputs,
+                  np_dtype in_dt, void* out, np_dtype out_dt, int64_t n, hipStream_t stream) {
+  int rc = validate_chain(ops, n_ops, inputs, n_inputs, in_dt, out, out_dt, n);
+  if (rc) return rc;
+  if (in_dt != out_dt) return fail(NP_EINVAL, "unfused_chain needs in_dt == out_dt");
+  if (n == 0) return ok();
+  for (int j = 0; j < n_inputs; ++j)
+    if (inputs[j] == out && !(j == ops[0].arg))
+      return fail(NP_EINVAL, "out may alias only the first loaded input");
+  if ((rc = check_device())) return rc;
+  const void* cur = inputs[ops[0].arg];
+  hipError_t e = hipSuccess;
+  if (n_ops == 1) e = np::launch_unary(np::U_COPY, 0.0f, cur, out, n, out_dt, stream);
+  for (int i = 1; i < n_ops && e == hipSuccess; ++i) {
+    const np_op& o = ops[i];
+    if (o.kind == NP_LOAD) {
+      e = np::launch_unary(np::U_COPY, 0.0f, inputs[o.arg], out, n, out_dt, stream);
+    } else if (o.kind == NP_ADD_IN || o.kind == NP_MUL_IN) {
+      e = np::launch_binary(o.kind, cur, inputs[o.arg], out, n, out_dt, stream);
+    } else {
+      e = np::launch_unary(o.kind, o.c, cur, out, n, out_dt, stream);
+    }
+    cur = out;
+  }
+  if (e != hipSuccess) return hip_fail(e, "unfused_chain");
+  return ok();
+}
+
+int unfused_det_decode(const void* const* level_logits, int n_levels, const int32_t* H,
+                       const int32_t* W, const float* strides, const float* anchors_wh,
+                       int n_anchors, int n_ch, int batch, np_dtype in_dt, float* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = validate_det(level_logits, n_levels, H, W, strides, anchors_wh, n_anchors, n_ch, batch,
+                        in_dt, out);
+  if (rc) return rc;
+  int64_t rows = 0;
+  for (int l = 0; l < n_levels; ++l) rows += (int64_t)n_anchors * H[l] * W[l];
+  const int64_t es = np::dt_size(in_dt);
+  const int64_t need = 2 * (int64_t)batch * rows * n_ch * es;
+  if (!workspace || (int64_t)workspace_bytes < need)
+    return fail(NP_EINVAL, "workspace needs %lld bytes", (long long)need);
+  if ((rc = check_device())) return rc;
+  char* ws = static_cast<char*>(workspace);
+  char* cat = ws + (int64_t)batch * rows * n_ch * es;  // second half: concatenated rows
+  const void* parts[8];
+  int64_t part_rows[8];
+  int64_t off = 0;
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < n_levels && e == hipSuccess; ++l) {
+    void* lv = ws + off * n_ch * es;
+    const int h = H[l], w = W[l], A = n_anchors, C = n_ch;
+    const float* an = anchors_wh + (size_t)l * n_anchors * 2;
+    e = np::launch_det_permute(level_logits[l], lv, batch, A, C, h, w, in_dt, stream);
+    if (e == hipSuccess) e = np::launch_det_range_op(lv, batch, A, C, h, w, 0, 2, np::D_SIGMOID, 0, an, in_dt, stream);
+    if (e == hipSuccess) e = np::launch_det_range_op(lv, batch, A, C, h, w, 4, C, np::D_SIGMOID, 0, an, in_dt, stream);
+    if (e == hipSuccess) e = np::launch_det_range_op(lv, batch, A, C, h, w, 2, 4, np::D_EXP, 0, an, in_dt, stream);
+    if (e == hipSuccess) e = np::launch_det_range_op(lv, batch, A, C, h, w, 2, 4, np::D_MUL_ANCHOR, 0, an, in_dt, stream);
+    if (e == hipSuccess) e = np::launch_det_range_op(lv, batch, A, C, h, w, 0, 2, np::D_ADD_GRID, 0, an, in_dt, stream);
+    if (e == hipSuccess) e = np::launch_det_range_op(lv, batch, A, C, h, w, 0, 2, np::D_MUL_C, strides[l], an, in_dt, stream);
+    parts[l] = lv;
+    part_rows[l] = (int64_t)A * h * w;
+    off += (int64_t)batch * A * h * w;
+  }
+  if (e == hipSuccess)
+    e = np::launch_det_concat(parts, part_rows, n_levels, cat, batch, rows, n_ch, in_dt, stream);
+  if (e == hipSuccess) e = np::launch_cast_to_f32(cat, out, (int64_t)batch * rows * n_ch, in_dt, stream);
+  if (e != hipSuccess) return hip_fail(e, "unfused_det_decode");
+  return ok();
+}
+
+int unfused_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out, void* out,
+                        int64_t rows, int64_t cols, float eps, np_dtype dt, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int rc = validate_norm(x, out, h_out, rows, cols, eps, dt);
+  if (rc) return rc;
+  const int64_t es = np::dt_size(dt);
+  const int64_t need = (rows * cols + 2 * rows + (h_out ? 0 : rows * cols)) * es;
+  if (rows == 0) return ok();
+  if (!workspace || (int64_t)workspace_bytes < need)
+    return fail(NP_EINVAL, "workspace needs %lld bytes", (long long)need);
+  if ((rc = check_device())) return rc;
+  char* ws = static_cast<char*>(workspace);
+  void* sq = ws;
+  void* ms = ws + rows * cols * es;
+  void* rs = ws + (rows * cols + rows) * es;
+  void* h = h_out ? h_out : ws + (rows * cols + 2 * rows) * es;
+  const int64_t n = rows * cols;
+  hipError_t e = r ? np::launch_binary(NP_ADD_IN, x, r, h, n, dt, stream)
+                   : np::launch_unary(np::U_COPY, 0.0f, x, h, n, dt, stream);
+  if (e == hipSuccess) e = np::launch_unary(np::U_SQUARE, 0.0f, h, sq, n, dt, stream);
+  if (e == hipSuccess) e = np::launch_row_mean(sq, ms, rows, cols, dt, stream);
+  if (e == hipSuccess) e = np::launch_unary(np::U_RSQRT_EPS, eps, ms, rs, rows, dt, stream);
+  if (e == hipSuccess) e = np::launch_row_scale(h, rs, out, rows, cols, dt, stream);
+  if (e == hipSuccess && w) e = np::launch_col_scale(out, w, out, rows, cols, dt, stream);
+  if (e != hipSuccess) return hip_fail(e, "unfused_add_rmsnorm");
+  return ok();
+}
+
+int unfused_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n_heads,
+                     int head_dim, const int32_t* positions, float base, float q_scale,
+                     np_dtype dt, hipStream_t stream) {
+  int rc = validate_rope(qkv, q, k, v, T, n_heads, head_dim, base, q_scale, dt);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if ((rc = check_device())) return rc;
+  float inv[256];
+  inv_freq(base, head_dim, inv);
+  hipError_t e = np::launch_qkv_split(qkv, q, k, v, T, n_heads, head_dim, dt, stream);
+  if (e == hipSuccess) e = np::launch_rope_inplace(q, T, n_heads, head_dim, positions, inv, dt, stream);
+  if (e == hipSuccess) e = np::launch_rope_inplace(k, T, n_heads, head_dim, positions, inv, dt, stream);
+  if (e == hipSuccess)
+    e = np::launch_unary(NP_MUL_C, q_scale, q, q, T * n_heads * (int64_t)head_dim, dt, stream);
+  if (e != hipSuccess) return hip_fail(e, "unfused_qkv_rope");
+  return ok();
+}
+
+int np_empty_launches(int count, hipStream_t stream) {
+  if (count < 0) return fail(NP_EINVAL, "count < 0");
+  int rc = check_device();
+  if (rc) return rc;
+  for (int i = 0; i < count; ++i) {
+    hipError_t e = np::launch_empty(stream);
+    if (e != hipSuccess) return hip_fail(e, "np_empty_launches");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// Fused residual add + RMSNorm (TeleTron write-up, 2kiu.com/news/5927820,
+// sections 3.3 and 4.2: per-row local reduction, then elementwise scaling, fp32
+// accumulation, one block per row, vector loads of 8 elements).
+//
+// Register path: one workgroup of WAVES wave64s per row; each thread holds VPT
+// 16-byte vectors of the row in registers between the two phases, so x and r
+// are read once and h and out written once:
+//   h = round(x + r) -> store h; sum of h^2 in fp32 per thread -> wave64 DPP
+//   reduction -> one LDS slot per wave -> every thread adds the WAVES partials
+//   in a fixed order -> rstd = 1/sqrt(mean + eps) -> out = h * rstd * w.
+// Generic path (unaligned pointers, odd or very long rows): the same per-row
+// block, element by element, in two passes.
+#include "device.h"
+#include "internal.h"
+
+namespace np {
+namespace {
+
+template <int WAVES>
+__device__ __forceinline__ float block_sum(float v, float* part) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[wave] = v;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) tot += part[i];
+  return tot;
+}
+
+template <typename T, int VPT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void rms_vec(const T* x, const T* r, const T* w, T* h,
+                                                      T* out, int cols, float eps) {
+  constexpr int N = Vec<T>::N;
+  constexpr int THREADS = 64 * WAVES;
+  __shared__ float part[WAVES];
+  const int64_t off = (int64_t)blockIdx.x * cols;
+  const int nvec = cols / N;
+  float hv[VPT][N];
+  float wv[VPT][N];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int vi = threadIdx.x + j * THREADS;
+    if (vi < nvec) {
+      load_vec<T>(x + off + vi * N, hv[j]);
+      if (r) {
+        float rv[N];
+        load_vec<T>(r + off + vi * N, rv);
+#pragma unroll
+        for (int e = 0; e < N; ++e) hv[j][e] += rv[e];
+      }
+      if (w) {
+        load_vec<T>(w + vi * N, wv[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) wv[j][e] = 1.0f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < N; ++e) hv[j][e] = wv[j][e] = 0.0f;
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int vi = threadIdx.x + j * THREADS;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      hv[j][e] = round_via<T>(hv[j][e]);  // the stored h is what the norm sees
+      ss += hv[j][e] * hv[j][e];
+    }
+    if (h && vi < nvec) store_vec<T>(h + off + vi * N, hv[j]);
+  }
+  const float tot = block_sum<WAVES>(ss, part);
+  const float rstd = 1.0f / sqrtf(tot / (float)cols + eps);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int vi = threadIdx.x + j * THREADS;
+    if (vi < nvec) {
+      float o[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) o[e] = hv[j][e] * rstd * wv[j][e];
+      store_vec<T>(out + off + vi * N, o);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rms_generic(const T* x, const T* r, const T* w, T* h,
+                                                   T* out, int cols, float eps) {
+  __shared__ float part[4];
+  const int64_t off = (int64_t)blockIdx.x * cols;
+  float ss = 0.0f;
+  for (int j = threadIdx.x; j < cols; j += 256) {
+    float s = to_f(x[off + j]);
+    if (r) s += to_f(r[off + j]);
+    const float hr = round_via<T>(s);
+    if (h) h[off + j] = from_f<T>(hr);
+    ss += hr * hr;
+  }
+  const float tot = block_sum<4>(ss, part);
+  const float rstd = 1.0f / sqrtf(tot / (float)cols + eps);
+  for (int j = threadIdx.x; j < cols; j += 256) {
+    float hr;
+    if (h) {
+      hr = to_f(h[off + j]);  // written by this thread in pass 1
+    } else {
+      float s = to_f(x[off + j]);
+      if (r) s += to_f(r[off + j]);
+      hr = round_via<T>(s);
+    }
+    const float wj = w ? to_f(w[j]) : 1.0f;
+    out[off + j] = from_f<T>(hr * rstd * wj);
+  }
+}
+
+template <typename T, int VPT>
+void launch_vec(const void* x, const void* r, const void* w, void* h, void* out, int64_t rows,
+                int cols, float eps, hipStream_t s) {
+  hipLaunchKernelGGL((rms_vec<T, VPT, 4>), dim3((unsigned)rows), dim3(256), 0, s,
+                     static_cast<const T*>(x), static_cast<const T*>(r),
+                     static_cast<const T*>(w), static_cast<T*>(h), static_cast<T*>(out), cols,
+                     eps);
+}
+
+template <typename T>
+hipError_t launch_t(const void* x, const void* r, const void* w, void* h, void* out,
+                    int64_t rows, int64_t cols, float eps, bool vec, hipStream_t s) {
+  constexpr int N = Vec<T>::N;
+  const int64_t nvec = cols / N;
+  if (vec && cols % N == 0 && nvec <= 256 * 8) {
+    if (nvec <= 256)
+      launch_vec<T, 1>(x, r, w, h, out, rows, (int)cols, eps, s);
+    else if (nvec <= 512)
+      launch_vec<T, 2>(x, r, w, h, out, rows, (int)cols, eps, s);
+    else if (nvec <= 1024)
+      launch_vec<T, 4>(x, r, w, h, out, rows, (int)cols, eps, s);
+    else
+      launch_vec<T, 8>(x, r, w, h, out, rows, (int)cols, eps, s);
+  } else {
+    hipLaunchKernelGGL((rms_generic<T>), dim3((unsigned)rows), dim3(256), 0, s,
+                       static_cast<const T*>(x), static_cast<const T*>(r),
+                       static_cast<const T*>(w), static_cast<T*>(h), static_cast<T*>(out),
+                       (int)cols, eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_add_rmsnorm(const void* x, const void* r, const void* w, void* h, void* out,
+                              int64_t rows, int64_t cols, float eps, int dt, bool vec,
+                              hipStream_t s) {
+  switch (dt) {
+    case NP_F32: return launch_t<float>(x, r, w, h, out, rows, cols, eps, vec, s);
+    case NP_F16: return launch_t<_Float16>(x, r, w, h, out, rows, cols, eps, vec, s);
+    default: return launch_t<__bf16>(x, r, w, h, out, rows, cols, eps, vec, s);
+  }
+}
+
+}  // namespace np

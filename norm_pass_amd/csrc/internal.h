@@ -1,0 +1,91 @@
+// Host-side interface between the C ABI (abi.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "norm_pass.h"
+
+namespace np {
+
+// Kernel-argument image of an op list (passed by value; < 1 KiB).
+struct ChainArgs {
+  int32_t n_ops;
+  int32_t kind[NP_MAX_OPS];
+  int32_t arg[NP_MAX_OPS];
+  float c[NP_MAX_OPS];
+  const void* in[NP_MAX_INPUTS];
+  void* out;
+  int64_t n;
+};
+
+inline int dt_size(int dt) { return dt == NP_F32 ? 4 : 2; }
+
+// fused elementwise chain (generic interpreter kernel); vec = 16-byte path
+hipError_t launch_chain(const ChainArgs& a, int in_dt, int out_dt, int n_inputs, bool vec,
+                        hipStream_t s);
+
+// detection-head decode
+struct DetArgs {
+  int32_t n_levels, n_anchors, n_ch, batch;
+  int32_t H[8], W[8];
+  int64_t row_off[8];     // first output row of level l (within one batch image)
+  int32_t tiles[8];       // tiles per (batch, anchor) of level l
+  int32_t tile_start[9];  // prefix over levels of batch * n_anchors * tiles[l]
+  int64_t total_rows;     // rows per batch image
+  float stride[8];
+  float anchor[8 * 16 * 2];
+  const void* in[8];
+  float* out;
+  int32_t tile_cells;     // cells per tile
+};
+hipError_t launch_det_decode(const DetArgs& a, int in_dt, bool vec_in, hipStream_t s);
+
+// residual add + RMSNorm
+hipError_t launch_add_rmsnorm(const void* x, const void* r, const void* w, void* h, void* out,
+                              int64_t rows, int64_t cols, float eps, int dt, bool vec,
+                              hipStream_t s);
+
+// QKV split + RoPE + scale
+struct RopeArgs {
+  const void* qkv;
+  void* q;
+  void* k;
+  void* v;
+  const int32_t* pos;
+  int64_t T;
+  int32_t H, D;
+  float q_scale;
+  float inv[256];
+};
+hipError_t launch_qkv_rope(const RopeArgs& a, int dt, bool vec, hipStream_t s);
+
+// unfused single-op kernels (eager semantics: result stored in the storage type)
+enum UnaryExtra { U_SQUARE = 100, U_RSQRT_EPS = 101, U_COPY = 102 };
+hipError_t launch_unary(int kind, float c, const void* in, void* out, int64_t n, int dt,
+                        hipStream_t s);
+hipError_t launch_binary(int kind, const void* a, const void* b, void* out, int64_t n, int dt,
+                         hipStream_t s);
+hipError_t launch_row_mean(const void* in, void* out, int64_t rows, int64_t cols, int dt,
+                           hipStream_t s);
+hipError_t launch_row_scale(const void* in, const void* rs, void* out, int64_t rows,
+                            int64_t cols, int dt, hipStream_t s);
+hipError_t launch_col_scale(const void* in, const void* w, void* out, int64_t rows,
+                            int64_t cols, int dt, hipStream_t s);
+hipError_t launch_qkv_split(const void* qkv, void* q, void* k, void* v, int64_t T, int H, int D,
+                            int dt, hipStream_t s);
+hipError_t launch_rope_inplace(void* x, int64_t T, int H, int D, const int32_t* pos,
+                               const float* inv, int dt, hipStream_t s);
+// detection tail pieces (rows of n_ch in the storage type)
+enum DetOp { D_SIGMOID = 0, D_EXP = 1, D_MUL_ANCHOR = 2, D_ADD_GRID = 3, D_MUL_C = 4 };
+hipError_t launch_det_permute(const void* in, void* rows_out, int batch, int A, int C, int H,
+                              int W, int dt, hipStream_t s);
+hipError_t launch_det_range_op(void* rows, int batch, int A, int C, int H, int W, int k0, int k1,
+                               int op, float c, const float* anchors_a2, int dt, hipStream_t s);
+hipError_t launch_det_concat(const void* const* parts, const int64_t* part_rows, int n_parts,
+                             void* out, int batch, int64_t total_rows, int C, int dt,
+                             hipStream_t s);
+hipError_t launch_cast_to_f32(const void* in, float* out, int64_t n, int dt, hipStream_t s);
+hipError_t launch_empty(hipStream_t s);
+
+}  // namespace np

@@ -1,0 +1,169 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point that include/norm_pass.h
+declares, reject bad arguments with NP_EINVAL and a message before touching any
+device, and its runtime specialiser must generate source that hipRTC compiles
+for gfx950 (compilation needs no GPU).
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def npa():
+    import norm_pass_amd
+    return norm_pass_amd
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "norm_pass.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol(npa):
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(npa.lib(), n), n
+
+
+def test_version(npa):
+    assert npa.np_version() == 1
+
+
+NULL = None
+
+
+def _err(npa):
+    return npa.lib().np_last_error().decode()
+
+
+@pytest.mark.parametrize("ops,n_inputs,n,msg", [
+    ([(synth.RELU, 0, 0)], 1, 4, "NP_LOAD"),
+    ([(synth.LOAD, 2, 0)], 2, 4, "input index"),
+    ([(synth.LOAD, 0, 0), (42, 0, 0)], 1, 4, "unknown kind"),
+    ([(synth.LOAD, 0, 0)], 0, 4, "n_inputs"),
+    ([(synth.LOAD, 0, 0)], 5, 4, "n_inputs"),
+    ([(synth.LOAD, 0, 0)] * 33, 1, 4, "n_ops"),
+    ([(synth.LOAD, 0, 0)], 1, -1, "n = -1"),
+])
+def test_fuse_chain_rejects(npa, ops, n_inputs, n, msg):
+    arr, k = npa._ops(ops)
+    for fn in (npa.lib().fuse_chain, npa.lib().unfused_chain):
+        rc = fn(arr, k, NULL, n_inputs, 0, NULL, 0, n, NULL)
+        assert rc == npa.NP_EINVAL
+        assert msg in _err(npa)
+
+
+def test_fuse_chain_null_buffers(npa):
+    arr, k = npa._ops(synth.C1_CHAIN)
+    ptrs = (C.c_void_p * 2)(0x1000, 0)
+    assert npa.lib().fuse_chain(arr, k, ptrs, 2, 0, C.c_void_p(0x2000), 0, 8, NULL) == -1
+    assert "inputs[1] is NULL" in _err(npa)
+    ptrs = (C.c_void_p * 2)(0x1000, 0x3000)
+    assert npa.lib().fuse_chain(arr, k, ptrs, 2, 0, NULL, 0, 8, NULL) == -1
+    assert "out is NULL" in _err(npa)
+    assert npa.lib().fuse_chain(arr, k, ptrs, 2, 7, C.c_void_p(0x2000), 0, 8, NULL) == -1
+
+
+def test_unfused_chain_requires_storage_type(npa):
+    arr, k = npa._ops(synth.C1_CHAIN)
+    ptrs = (C.c_void_p * 2)(0x1000, 0x3000)
+    assert npa.lib().unfused_chain(arr, k, ptrs, 2, 1, C.c_void_p(0x2000), 0, 8, NULL) == -1
+    assert "in_dt == out_dt" in _err(npa)
+
+
+def test_zero_length_is_a_no_op(npa):
+    # n == 0 needs no buffers and no device
+    arr, k = npa._ops(synth.C1_CHAIN)
+    assert npa.lib().fuse_chain(arr, k, NULL, 2, 0, NULL, 0, 0, NULL) == 0
+
+
+def _det_call(npa, fn, n_levels=1, H=4, W=4, n_anchors=3, n_ch=85, batch=1, dt=1, out=0x4000,
+              lv=0x1000, extra=()):
+    ptrs = (C.c_void_p * max(n_levels, 1))(*([lv] * max(n_levels, 1)))
+    Hs = (C.c_int32 * max(n_levels, 1))(*([H] * max(n_levels, 1)))
+    Ws = (C.c_int32 * max(n_levels, 1))(*([W] * max(n_levels, 1)))
+    st = (C.c_float * max(n_levels, 1))(*([8.0] * max(n_levels, 1)))
+    an = (C.c_float * 256)()
+    return fn(ptrs, n_levels, Hs, Ws, st, an, n_anchors, n_ch, batch, dt,
+              C.c_void_p(out) if out else NULL, *extra)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(n_levels=0), "n_levels"),
+    (dict(n_levels=9), "n_levels"),
+    (dict(n_anchors=0), "n_anchors"),
+    (dict(n_anchors=17), "n_anchors"),
+    (dict(n_ch=4), "n_ch"),
+    (dict(n_ch=1025), "n_ch"),
+    (dict(batch=0), "batch"),
+    (dict(H=0), "bad H x W"),
+    (dict(out=0), "NULL"),
+    (dict(lv=0), "NULL"),
+    (dict(dt=3), "dtype"),
+])
+def test_det_decode_rejects(npa, kw, msg):
+    assert _det_call(npa, npa.lib().fuse_det_decode, extra=(NULL,), **kw) == -1
+    assert msg in _err(npa)
+
+
+def test_unfused_det_decode_needs_workspace(npa):
+    rc = _det_call(npa, npa.lib().unfused_det_decode, extra=(C.c_void_p(0x8000), 100, NULL))
+    assert rc == -1 and "workspace needs" in _err(npa)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((NULL, NULL, NULL, NULL, 0x2000, 4, 8, 1e-6, 2), "NULL"),
+    ((0x1000, NULL, NULL, NULL, 0x2000, -1, 8, 1e-6, 2), "rows"),
+    ((0x1000, NULL, NULL, NULL, 0x2000, 4, 0, 1e-6, 2), "cols"),
+    ((0x1000, NULL, NULL, NULL, 0x2000, 4, (1 << 24) + 1, 1e-6, 2), "cols"),
+    ((0x1000, NULL, NULL, NULL, 0x2000, 4, 8, 0.0, 2), "eps"),
+    ((0x1000, NULL, NULL, NULL, 0x2000, 4, 8, float("inf"), 2), "eps"),
+    ((0x1000, NULL, NULL, NULL, 0x2000, 4, 8, float("nan"), 2), "eps"),
+    ((0x1000, NULL, NULL, 0x2000, 0x2000, 4, 8, 1e-6, 2), "differ"),
+    ((0x1000, NULL, NULL, NULL, 0x2000, 4, 8, 1e-6, 5), "dtype"),
+])
+def test_add_rmsnorm_rejects(npa, args, msg):
+    a = [C.c_void_p(v) if isinstance(v, int) and i < 5 else v for i, v in enumerate(args)]
+    assert npa.lib().fuse_add_rmsnorm(*a, NULL) == -1
+    assert msg in _err(npa)
+
+
+@pytest.mark.parametrize("T,H,D,base,qs,msg", [
+    (-1, 24, 128, 1e4, 0.1, "T out of range"),
+    (4, 0, 128, 1e4, 0.1, "n_heads"),
+    (4, 2, 7, 1e4, 0.1, "head_dim"),
+    (4, 2, 514, 1e4, 0.1, "head_dim"),
+    (4, 2, 128, 0.0, 0.1, "base"),
+    (4, 2, 128, 1e4, float("inf"), "q_scale"),
+])
+def test_qkv_rope_rejects(npa, T, H, D, base, qs, msg):
+    p = [C.c_void_p(0x1000 * (i + 1)) for i in range(4)]
+    for fn in (npa.lib().fuse_qkv_rope, npa.lib().unfused_qkv_rope):
+        assert fn(*p, T, H, D, NULL, base, qs, 2, NULL) == -1
+        assert msg in _err(npa)
+
+
+def test_qkv_rope_rejects_aliasing(npa):
+    p = [C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x2000), C.c_void_p(0x3000)]
+    assert npa.lib().fuse_qkv_rope(*p, 4, 2, 8, NULL, 1e4, 0.5, 2, NULL) == -1
+    assert "alias" in _err(npa)
+
+
+def test_runtime_specialisation_compiles(npa):
+    """The generated source compiles with hipRTC for gfx950 (DeepJIT write-up,
+    sections 3.3 and 6.2: tens to hundreds of ms per runtime compile)."""
+    ms1, b1 = npa.np_chain_compile(synth.C1_CHAIN, 2, npa.NP_F32, npa.NP_F32, 1 << 20)
+    ms2, b2 = npa.np_chain_compile(synth.c5_chain(), 1, npa.NP_F16, npa.NP_F16, 0)
+    assert b1 > 0 and b2 > 0 and ms1 > 0 and ms2 > 0
+    with pytest.raises(npa.NPError):
+        npa.np_chain_compile([(synth.LOAD, 0, 0), (77, 0, 0)], 1, 0, 0, 0)
