@@ -216,6 +216,8 @@ int oracle_chain(const int32_t* kinds, const int32_t* args, const float* consts,
           t = cast_node(t, BF16);
           break;
       }
+      // the running value lives in a binary32 register: beyond its range it is inf
+      if (std::isfinite(t.v) && std::isinf(round_to(t.v, F32))) t.v = std::copysign(INFINITY, t.v);
       if (eager && kinds[j] != LOAD) t = cast_node(t, fo);
     }
     if (exact) exact[i] = t.v;

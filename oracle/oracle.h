@@ -52,7 +52,9 @@ void oracle_round_array(const double* x, int64_t n, int dt, void* out);
  *        7 sigmoid 8 exp 9 tanh 10 cast_f16 11 cast_bf16.
  * inputs: n_inputs pointers to n elements of in_dt. out: n elements of out_dt.
  * eager = 0: fused semantics (exact intermediates, rounding only at cast
- *            nodes and at the output).
+ *            nodes and at the output). The running value has the range of
+ *            binary32 (the write-up's kernels hold it in a float register):
+ *            a value beyond it becomes +-inf.
  * eager = 1: unfused semantics: every op stores its result in out_dt, as a
  *            chain of separate kernels with that storage type does.
  * exact / bound: optional (may be NULL) [n] doubles.

@@ -31,6 +31,16 @@ def test_c1_hand_values(orc):
     assert np.array_equal(y.view(np.uint32), want.view(np.uint32))  # never -0
 
 
+def test_c1_running_value_has_binary32_range(orc):
+    """t = a + b is held in a float register (DeepJIT write-up, section 3.2): a sum
+    beyond the binary32 range is inf even though t * 0.5 would fit."""
+    a = np.array([3e38, -3e38, 1.8e38, 1.7e38], np.float32)
+    b = np.array([3e38, -3e38, 1.8e38, 1.7e38], np.float32)
+    y = orc.chain(C1, [a, b], F32)
+    assert np.isposinf(y[0]) and y[1] == 0 and np.isposinf(y[2])
+    assert y[3] == np.float32(1.7e38)  # 3.4e38 still fits binary32
+
+
 def test_c1_invariants(orc):
     a, b = synth.c1_inputs(1 << 16, seed=7)
     y = orc.chain(C1, [a, b], F32)
