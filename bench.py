@@ -67,6 +67,18 @@ def rope_bytes(T, H, D, es=2):
     return 6 * q, 6 * q + 2 * q + 2 * q + 2 * q
 
 
+# VALU issue slots per element of one chain op, as compiled for gfx950 by the
+# fp16-output fast path (full-rate VALU instruction = 1 slot, v_exp_f32 and
+# v_rcp_f32 = 2 slots, measured): the algorithmic work of an ALU-bound chain.
+VALU_SLOTS = {0: 1, 1: 2, 2: 2, 3: 1, 4: 1, 5: 1, 6: 1, 7: 10, 8: 8, 9: 16, 10: 2, 11: 2}
+VALU_PEAK = 256 * 64 * 2.4e9  # lane-slots/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+
+
+def chain_slots(ops) -> int:
+    """VALU slots per element: every op, plus the final rounding store."""
+    return sum(VALU_SLOTS[k] for k, _, _ in ops) + 1
+
+
 def file_hash(*paths) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -75,29 +87,45 @@ def file_hash(*paths) -> str:
     return h.hexdigest()[:16]
 
 
+_CHAIN_SRC = ["norm_pass_amd/csrc/chain.hip", "norm_pass_amd/csrc/device.h",
+              "norm_pass_amd/csrc/fastmath.h", "norm_pass_amd/csrc/rtc.cpp"]
 KERNEL_SOURCES = {
-    "c1": ["norm_pass_amd/csrc/chain.hip", "norm_pass_amd/csrc/device.h"],
-    "c5_large": ["norm_pass_amd/csrc/chain.hip", "norm_pass_amd/csrc/device.h"],
-    "c5_small": ["norm_pass_amd/csrc/chain.hip", "norm_pass_amd/csrc/device.h"],
+    "c1": _CHAIN_SRC,
+    "c5_large": _CHAIN_SRC,
+    "c5_small": _CHAIN_SRC,
     "c2": ["norm_pass_amd/csrc/det_decode.hip", "norm_pass_amd/csrc/device.h"],
     "c3": ["norm_pass_amd/csrc/add_rmsnorm.hip", "norm_pass_amd/csrc/device.h"],
     "c4": ["norm_pass_amd/csrc/qkv_rope.hip", "norm_pass_amd/csrc/device.h"],
 }
 
 
-def measured_traffic(name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when there is none or the kernel source changed since it was taken."""
+def _counter_row(name: str):
+    """Row `| name | source hash | traffic bytes | ... | valu insts/element |` of
+    the committed rocprofv3 counter summary, if the kernel sources still hash
+    to what they were when the counters were taken."""
     path = os.path.join(PROFILES, "counters_hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    txt = open(path).read()
-    m = re.search(rf"^\|\s*{name}\s*\|\s*([0-9a-f]{{16}})\s*\|\s*([0-9.e+]+)\s*\|", txt, re.M)
-    if not m:
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 3 and cells[0] == name and re.fullmatch(r"[0-9a-f]{16}", cells[1]):
+            return cells if cells[1] == file_hash(*KERNEL_SOURCES[name]) else None
+    return None
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) or None."""
+    row = _counter_row(name)
+    return float(row[2]) if row else None
+
+
+def measured_valu_per_element(name: str):
+    """Dynamic VALU lane-instructions per element (SQ_INSTS_VALU) or None."""
+    row = _counter_row(name)
+    try:
+        return float(row[-1]) if row else None
+    except ValueError:
         return None
-    if m.group(1) != file_hash(*KERNEL_SOURCES[name]):
-        return None
-    return float(m.group(2))
 
 
 # ------------------------------------------------------------------ timing
@@ -117,6 +145,22 @@ def time_calls(torch, fn, reps: int, trials: int):
         res.append(s.elapsed_time(e) / 1e3 / reps)
     res.sort()
     return res[len(res) // 2], res[max(0, len(res) // 10)], res[min(len(res) - 1, (9 * len(res)) // 10)]
+
+
+def time_isolated(torch, fn, reps: int):
+    """Mean per-launch duration with an event pair around every launch: the
+    marker between launches keeps consecutive kernels from overlapping, so this
+    is the kernel's own duration (what rocprofv3's kernel trace reports)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in ev) / reps / 1e3
 
 
 def pick_reps(torch, fn, target_s=0.003):
@@ -148,10 +192,14 @@ def build_workloads(torch, npa, synth, quick: bool):
     a, b = synth.c1_inputs(n1)
     ta, tb = tdev(a, "f32"), tdev(b, "f32")
     y1 = torch.empty(n1, device=dev)
+    # warm-up specialisation of the chains (compiled once, off the timed path)
+    t0 = time.perf_counter()
+    npa.fuse_chain_prepare(synth.C1_CHAIN, 2, npa.NP_F32, npa.NP_F32, n1)
+    compile_ms = {"c1": round((time.perf_counter() - t0) * 1e3, 1)}
     W["c1"] = dict(
         desc="fp32 relu(a+b)*0.5, 1,048,576 elements",
-        fused=lambda: npa.fuse_chain(synth.C1_CHAIN, [ta, tb], y1),
-        unfused=lambda: npa.unfused_chain(synth.C1_CHAIN, [ta, tb], y1),
+        fused=npa.bind("fuse_chain", synth.C1_CHAIN, [ta, tb], y1),
+        unfused=npa.bind("unfused_chain", synth.C1_CHAIN, [ta, tb], y1),
         bytes=12 * n1, unfused_bytes=28 * n1, launches=3, kernel="chain_vec<float, float, 2")
     # C2
     lv = [tdev(x, "f16") for x in synth.c2_inputs()]
@@ -163,8 +211,8 @@ def build_workloads(torch, npa, synth, quick: bool):
     fb, ub = det_bytes(hw)
     W["c2"] = dict(
         desc="YOLO decode fp16 [1,255,80|40|20] -> fp32 [1,25200,85]",
-        fused=lambda: npa.fuse_det_decode(lv, st, an, out2),
-        unfused=lambda: npa.unfused_det_decode(lv, st, an, out2, ws2),
+        fused=npa.bind("fuse_det_decode", lv, st, an, out2),
+        unfused=npa.bind("unfused_det_decode", lv, st, an, out2, ws2),
         bytes=fb, unfused_bytes=ub, launches=23, kernel="det_decode_kernel")
     # C3
     rows = 2048 if quick else 16384
@@ -178,8 +226,8 @@ def build_workloads(torch, npa, synth, quick: bool):
     fb, ub = rms_bytes(rows, 4096)
     W["c3"] = dict(
         desc=f"bf16 residual add + RMSNorm [{rows}, 4096], eps 1e-6",
-        fused=lambda: npa.fuse_add_rmsnorm(tx, tr, tw, h3, o3, 1e-6),
-        unfused=lambda: npa.unfused_add_rmsnorm(tx, tr, tw, h3, o3, ws3, 1e-6),
+        fused=npa.bind("fuse_add_rmsnorm", tx, tr, tw, h3, o3, 1e-6),
+        unfused=npa.bind("unfused_add_rmsnorm", tx, tr, tw, h3, o3, ws3, 1e-6),
         bytes=fb, unfused_bytes=ub, launches=6, kernel="rms_vec")
     # C4
     T = 2048 if quick else 16384
@@ -189,19 +237,23 @@ def build_workloads(torch, npa, synth, quick: bool):
     fb, ub = rope_bytes(T, 24, 128)
     W["c4"] = dict(
         desc=f"bf16 QKV split + RoPE + scale, [{T}, 3x24x128] -> 3 x [24, {T}, 128]",
-        fused=lambda: npa.fuse_qkv_rope(qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
-        unfused=lambda: npa.unfused_qkv_rope(qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
+        fused=npa.bind("fuse_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
+        unfused=npa.bind("unfused_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
         bytes=fb, unfused_bytes=ub, launches=4, kernel="rope_vec")
     # C5
     ops = synth.c5_chain()
+    t0 = time.perf_counter()
+    npa.fuse_chain_prepare(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    compile_ms["c5"] = round((time.perf_counter() - t0) * 1e3, 1)
     for name, n in (("c5_small", 1 << 16), ("c5_large", (1 << 24) if quick else (1 << 28))):
         xin = tdev(synth.c5_inputs(n), "f16")
         yo = torch.empty_like(xin)
         W[name] = dict(
             desc=f"seeded 29-op fp16 chain, {n:,} elements",
-            fused=(lambda xin=xin, yo=yo: npa.fuse_chain(ops, [xin], yo)),
-            unfused=(lambda xin=xin, yo=yo: npa.unfused_chain(ops, [xin], yo)),
+            fused=npa.bind("fuse_chain", ops, [xin], yo),
+            unfused=npa.bind("unfused_chain", ops, [xin], yo),
             bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29, kernel="chain_vec<_Float16")
+    W["_compile_ms"] = compile_ms
     return W
 
 
@@ -261,6 +313,7 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="reduced sizes (smoke runs only)")
     ap.add_argument("--profile", action="store_true",
                     help="only a few launches of each kernel (for rocprofv3 runs)")
+    ap.add_argument("--only", default="", help="profile mode: comma-separated workloads")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: the fused chains shard without any exchange, so "
@@ -280,6 +333,7 @@ def main(argv=None):
     npa.np_init(0)
     props = torch.cuda.get_device_properties(0)
     W = build_workloads(torch, npa, synth, args.quick)
+    compile_ms = W.pop("_compile_ms")
     torch.cuda.synchronize()
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s on {props.name} "
@@ -293,8 +347,11 @@ def main(argv=None):
         dst = torch.empty_like(src)
         for _ in range(3):
             npa.unfused_chain([(synth.LOAD, 0, 0.0)], [src], dst)
+        only = [x for x in args.only.split(",") if x]
         for name, w in W.items():
-            for _ in range(3):
+            if only and name not in only:
+                continue
+            for _ in range(5):
                 w["fused"]()
             for _ in range(2):
                 w["unfused"]()
@@ -345,6 +402,18 @@ def main(argv=None):
         log(f"[bench] {k}: fused {f_med * 1e6:.2f} us ({gbps:.0f} GB/s), "
             f"unfused {u_med * 1e6:.2f} us x{w['launches']} launches")
 
+    # achievable streaming ceiling: a plain 16-byte-per-lane copy of 1 GiB
+    n_copy = 1 << 28
+    csrc = torch.empty(n_copy, dtype=torch.float32, device="cuda").fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cp = npa.bind("unfused_chain", [(synth.LOAD, 0, 0.0)], [csrc], cdst)
+    c_med, _, _ = time_calls(torch, cp, 10, 7)
+    copy_gbps = 2 * 4 * n_copy / c_med / 1e9
+    del csrc, cdst
+    for k in order:
+        per[k]["frac_of_copy"] = round(per[k]["GBps"] / copy_gbps, 3)
+    log(f"[bench] copy ceiling {copy_gbps:.0f} GB/s")
+
     # launch-cost model (NaiveRT write-up): the pages' own instance, then ours
     pages = cost_model(PAGES_COST_MODEL["t_unfused_ms"], PAGES_COST_MODEL["t_fused_ms"],
                        PAGES_COST_MODEL["k"])
@@ -356,13 +425,40 @@ def main(argv=None):
     for key in ("L", "T"):
         ours[key] = round(ours[key], 3)
 
-    # roofline of the dominant kernel of the step
+    # roofline of the dominant kernel of the step: HBM for the streaming
+    # kernels; the 29-op chain is bound by VALU issue (its algorithmic slots
+    # per element far exceed the ~20 that 8 TB/s leaves per fp16 element)
     dom = max(order, key=lambda k: per[k]["us_med"])
     d = per[dom]
-    achieved = d["bytes"] / (d["us_med"] * 1e-6) / 1e9
-    roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(dom)}
+    t_dom = time_isolated(torch, W[dom]["fused"], 20)
+    hbm_frac = d["bytes"] / t_dom / 1e9 / HBM_PEAK_GBPS
+    if dom.startswith("c5"):
+        n_el = d["bytes"] // 4
+        per_el = measured_valu_per_element(dom)
+        src = "rocprofv3 SQ_INSTS_VALU"
+        if per_el is None:
+            per_el, src = float(chain_slots(synth.c5_chain())), "static slot table"
+        achieved = per_el * n_el / t_dom / 1e12
+        roof = {"kernel": dom, "launch_us": round(t_dom * 1e6, 2), "bound": "alu",
+                "achieved": round(achieved, 2),
+                "peak": round(VALU_PEAK / 1e12, 2), "unit": "T VALU lane-instr/s",
+                "frac": round(achieved * 1e12 / VALU_PEAK, 4),
+                "valu_per_element": round(per_el, 2), "valu_count_source": src,
+                "hbm_frac": round(hbm_frac, 4), "traffic": measured_traffic(dom)}
+    else:
+        achieved = d["bytes"] / t_dom / 1e9
+        roof = {"kernel": dom, "launch_us": round(t_dom * 1e6, 2), "bound": "hbm",
+                "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(hbm_frac, 4),
+                "traffic": measured_traffic(dom)}
+    # every kernel's own roofline, for the record
+    for k in order:
+        per[k]["hbm_frac"] = round(per[k]["bytes"] / (per[k]["us_med"] * 1e-6) / 1e9
+                                   / HBM_PEAK_GBPS, 4)
+    for k in ("c5_small", "c5_large"):
+        n_el = per[k]["bytes"] // 4
+        per[k]["valu_frac"] = round(chain_slots(synth.c5_chain()) * n_el
+                                    / (per[k]["us_med"] * 1e-6) / VALU_PEAK, 4)
 
     cpu = None
     if not args.no_cpu:
@@ -392,6 +488,8 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "per_config": per,
         "cost_model": {"pages": {k: round(v, 4) for k, v in pages.items()}, "c5_small_us": ours},
+        "rtc_compile_ms": compile_ms,
+        "copy_ceiling_GBps": round(copy_gbps, 1),
         "env": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count, "torch": torch.__version__},
     }

@@ -112,6 +112,13 @@ void np_shutdown(void);
 int np_chain_compile(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt, np_dtype out_dt,
                      int64_t n, double* compile_ms, size_t* code_bytes);
 
+/* Write the generated kernel source for a chain (what fuse_chain_prepare
+ * compiles) into buf (NUL-terminated, truncated to len); returns the full size
+ * including the NUL, or NP_EINVAL. The DeepJIT write-up, section 5.2, logs each
+ * generated kernel while debugging; this is that hook. */
+int64_t np_chain_source(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt,
+                        np_dtype out_dt, int64_t n, char* buf, size_t len);
+
 /* --------------------------------------------------------- fused calls */
 
 /*
@@ -153,7 +160,8 @@ int fuse_chain_prepare(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt
  *   out[0] = (sigmoid(t0) + x) * stride   out[1] = (sigmoid(t1) + y) * stride
  *   out[2] = exp(t2) * anchor_w           out[3] = exp(t3) * anchor_h
  *   out[k] = sigmoid(t_k) for k >= 4.
- * Limits: 1 <= n_levels <= 8, 1 <= n_anchors <= 16, 5 <= n_ch <= 1024.
+ * Limits: 1 <= n_levels <= 8, 1 <= n_anchors <= 16, 5 <= n_ch <= 1024,
+ * H[l] * W[l] <= 2^22 cells per level.
  * Errors: NP_EINVAL on NULL pointers or out-of-range sizes.
  */
 int fuse_det_decode(const void* const* level_logits, int n_levels, const int32_t* H,

@@ -50,6 +50,7 @@ def _load():
         "np_version": [],
         "np_shutdown": [],
         "np_chain_compile": [OPS, I, I, I, I, I64, C.POINTER(C.c_double), C.POINTER(S)],
+        "np_chain_source": [OPS, I, I, I, I, I64, C.c_char_p, S],
         "fuse_chain": [OPS, I, P, I, I, P, I, I64, P],
         "fuse_chain_prepare": [OPS, I, I, I, I, I64],
         "fuse_det_decode": [P, I, P, P, P, P, I, I, I, I, P, P],
@@ -64,7 +65,8 @@ def _load():
     for name, args in sig.items():
         fn = getattr(L, name)
         fn.argtypes = args
-        fn.restype = None if name == "np_shutdown" else C.c_int
+        fn.restype = (None if name == "np_shutdown" else
+                      C.c_int64 if name == "np_chain_source" else C.c_int)
     L.np_last_error.restype = C.c_char_p
     L.np_last_error.argtypes = []
     return L
@@ -135,26 +137,32 @@ def np_chain_compile(ops, n_inputs: int, in_dt: int, out_dt: int, n: int = 0):
     return ms.value, nb.value
 
 
+def np_chain_source(ops, n_inputs: int, in_dt: int, out_dt: int, n: int = 0) -> str:
+    """The generated kernel source fuse_chain_prepare would compile."""
+    arr, k = _ops(ops)
+    size = _lib.np_chain_source(arr, k, n_inputs, in_dt, out_dt, n, None, 0)
+    if size < 0:
+        _check(int(size), "np_chain_source")
+    buf = C.create_string_buffer(int(size))
+    _lib.np_chain_source(arr, k, n_inputs, in_dt, out_dt, n, buf, size)
+    return buf.value.decode()
+
+
 def np_empty_launches(count: int, stream=None):
     _check(_lib.np_empty_launches(count, _stream(stream)), "np_empty_launches")
 
 
 # -------------------------------------------------------------- fused calls
+# Each call is split into an argument builder (_a_<name>: torch tensors ->
+# ctypes arguments) and the C call itself, so that `bind` can marshal once and
+# hand back a zero-argument callable for tight launch loops.
 
-def fuse_chain(ops, inputs, out, stream=None):
-    """out[i] = chain(inputs[0][i], ...); ops = [(kind, arg, const), ...]."""
+def _a_fuse_chain(ops, inputs, out, stream=None):
     arr, k = _ops(ops)
-    n = out.numel()
     ptrs = (C.c_void_p * len(inputs))(*[t.data_ptr() for t in inputs])
     _keep(stream, out, *inputs)
-    _check(_lib.fuse_chain(arr, k, ptrs, len(inputs), dtype_code(inputs[0]), _ptr(out),
-                           dtype_code(out), n, _stream(stream)), "fuse_chain")
-    return out
-
-
-def fuse_chain_prepare(ops, n_inputs: int, in_dt: int, out_dt: int, n: int = 0):
-    arr, k = _ops(ops)
-    _check(_lib.fuse_chain_prepare(arr, k, n_inputs, in_dt, out_dt, n), "fuse_chain_prepare")
+    return (arr, k, ptrs, len(inputs), dtype_code(inputs[0]), _ptr(out), dtype_code(out),
+            out.numel(), _stream(stream))
 
 
 def _det_args(levels, strides, anchors):
@@ -172,45 +180,97 @@ def det_rows(levels, n_anchors: int) -> int:
     return sum(n_anchors * t.shape[2] * t.shape[3] for t in levels)
 
 
+def _a_fuse_det_decode(levels, strides, anchors, out, n_anchors: int = 3, n_ch: int = 85,
+                       stream=None):
+    ptrs, nl, H, W, st, an = _det_args(levels, strides, anchors)
+    _keep(stream, out, *levels)
+    return (ptrs, nl, H, W, st, an, n_anchors, n_ch, levels[0].shape[0], dtype_code(levels[0]),
+            _ptr(out), _stream(stream))
+
+
+def _a_fuse_add_rmsnorm(x, r, w, h_out, out, eps: float = 1e-6, stream=None):
+    _keep(stream, x, r, w, h_out, out)
+    return (_ptr(x), _ptr(r), _ptr(w), _ptr(h_out), _ptr(out), x.shape[0], x.shape[-1], eps,
+            dtype_code(x), _stream(stream))
+
+
+def _a_fuse_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
+                     base: float = 10000.0, q_scale: float | None = None, stream=None):
+    if q_scale is None:
+        q_scale = 1.0 / math.sqrt(head_dim)
+    _keep(stream, qkv, q, k, v, positions)
+    return (_ptr(qkv), _ptr(q), _ptr(k), _ptr(v), qkv.shape[0], n_heads, head_dim,
+            _ptr(positions), base, q_scale, dtype_code(qkv), _stream(stream))
+
+
+_a_unfused_chain = _a_fuse_chain
+_a_unfused_qkv_rope = _a_fuse_qkv_rope
+
+
+def _a_unfused_det_decode(levels, strides, anchors, out, workspace, n_anchors: int = 3,
+                          n_ch: int = 85, stream=None):
+    a = _a_fuse_det_decode(levels, strides, anchors, out, n_anchors, n_ch, stream)
+    _keep(stream, workspace)
+    return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
+
+
+def _a_unfused_add_rmsnorm(x, r, w, h_out, out, workspace, eps: float = 1e-6, stream=None):
+    a = _a_fuse_add_rmsnorm(x, r, w, h_out, out, eps, stream)
+    _keep(stream, workspace)
+    return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
+
+
+def bind(name: str, *args, **kw):
+    """Marshal the arguments of call `name` once; return a zero-argument callable
+    that performs the C call (and raises NPError on failure) each time."""
+    a = globals()["_a_" + name](*args, **kw)
+    f = getattr(_lib, name)
+
+    def call():
+        rc = f(*a)
+        if rc:
+            _check(rc, name)
+    call.args = a  # keeps the ctypes objects alive
+    return call
+
+
+def fuse_chain(ops, inputs, out, stream=None):
+    """out[i] = chain(inputs[0][i], ...); ops = [(kind, arg, const), ...]."""
+    _check(_lib.fuse_chain(*_a_fuse_chain(ops, inputs, out, stream)), "fuse_chain")
+    return out
+
+
+def fuse_chain_prepare(ops, n_inputs: int, in_dt: int, out_dt: int, n: int = 0):
+    arr, k = _ops(ops)
+    _check(_lib.fuse_chain_prepare(arr, k, n_inputs, in_dt, out_dt, n), "fuse_chain_prepare")
+
+
 def fuse_det_decode(levels, strides, anchors, out, n_anchors: int = 3, n_ch: int = 85,
                     stream=None):
     """levels: [batch, n_anchors*n_ch, H, W] tensors; anchors: [[(w, h)] * n_anchors] per level;
     out: fp32 [batch, rows, n_ch]."""
-    ptrs, nl, H, W, st, an = _det_args(levels, strides, anchors)
-    _keep(stream, out, *levels)
-    _check(_lib.fuse_det_decode(ptrs, nl, H, W, st, an, n_anchors, n_ch, levels[0].shape[0],
-                                dtype_code(levels[0]), _ptr(out), _stream(stream)),
-           "fuse_det_decode")
+    _check(_lib.fuse_det_decode(*_a_fuse_det_decode(levels, strides, anchors, out, n_anchors,
+                                                    n_ch, stream)), "fuse_det_decode")
     return out
 
 
 def fuse_add_rmsnorm(x, r, w, h_out, out, eps: float = 1e-6, stream=None):
-    rows, cols = x.shape[0], x.shape[-1]
-    _keep(stream, x, r, w, h_out, out)
-    _check(_lib.fuse_add_rmsnorm(_ptr(x), _ptr(r), _ptr(w), _ptr(h_out), _ptr(out), rows, cols,
-                                 eps, dtype_code(x), _stream(stream)), "fuse_add_rmsnorm")
+    _check(_lib.fuse_add_rmsnorm(*_a_fuse_add_rmsnorm(x, r, w, h_out, out, eps, stream)),
+           "fuse_add_rmsnorm")
     return h_out, out
 
 
 def fuse_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
                   base: float = 10000.0, q_scale: float | None = None, stream=None):
-    if q_scale is None:
-        q_scale = 1.0 / math.sqrt(head_dim)
-    _keep(stream, qkv, q, k, v, positions)
-    _check(_lib.fuse_qkv_rope(_ptr(qkv), _ptr(q), _ptr(k), _ptr(v), qkv.shape[0], n_heads,
-                              head_dim, _ptr(positions), base, q_scale, dtype_code(qkv),
-                              _stream(stream)), "fuse_qkv_rope")
+    _check(_lib.fuse_qkv_rope(*_a_fuse_qkv_rope(qkv, q, k, v, n_heads, head_dim, positions, base,
+                                                q_scale, stream)), "fuse_qkv_rope")
     return q, k, v
 
 
 # ------------------------------------------------------- unfused baselines
 
 def unfused_chain(ops, inputs, out, stream=None):
-    arr, k = _ops(ops)
-    ptrs = (C.c_void_p * len(inputs))(*[t.data_ptr() for t in inputs])
-    _keep(stream, out, *inputs)
-    _check(_lib.unfused_chain(arr, k, ptrs, len(inputs), dtype_code(inputs[0]), _ptr(out),
-                              dtype_code(out), out.numel(), _stream(stream)), "unfused_chain")
+    _check(_lib.unfused_chain(*_a_unfused_chain(ops, inputs, out, stream)), "unfused_chain")
     return out
 
 
@@ -220,11 +280,8 @@ def det_workspace_bytes(levels, n_anchors: int = 3, n_ch: int = 85) -> int:
 
 def unfused_det_decode(levels, strides, anchors, out, workspace, n_anchors: int = 3,
                        n_ch: int = 85, stream=None):
-    ptrs, nl, H, W, st, an = _det_args(levels, strides, anchors)
-    _keep(stream, out, workspace, *levels)
-    _check(_lib.unfused_det_decode(ptrs, nl, H, W, st, an, n_anchors, n_ch, levels[0].shape[0],
-                                   dtype_code(levels[0]), _ptr(out), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+    _check(_lib.unfused_det_decode(*_a_unfused_det_decode(levels, strides, anchors, out,
+                                                          workspace, n_anchors, n_ch, stream)),
            "unfused_det_decode")
     return out
 
@@ -235,21 +292,13 @@ def rmsnorm_workspace_bytes(rows: int, cols: int, dtype, with_h: bool = True) ->
 
 
 def unfused_add_rmsnorm(x, r, w, h_out, out, workspace, eps: float = 1e-6, stream=None):
-    rows, cols = x.shape[0], x.shape[-1]
-    _keep(stream, x, r, w, h_out, out, workspace)
-    _check(_lib.unfused_add_rmsnorm(_ptr(x), _ptr(r), _ptr(w), _ptr(h_out), _ptr(out), rows, cols,
-                                    eps, dtype_code(x), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(),
-                                    _stream(stream)), "unfused_add_rmsnorm")
+    _check(_lib.unfused_add_rmsnorm(*_a_unfused_add_rmsnorm(x, r, w, h_out, out, workspace, eps,
+                                                            stream)), "unfused_add_rmsnorm")
     return h_out, out
 
 
 def unfused_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
                      base: float = 10000.0, q_scale: float | None = None, stream=None):
-    if q_scale is None:
-        q_scale = 1.0 / math.sqrt(head_dim)
-    _keep(stream, qkv, q, k, v, positions)
-    _check(_lib.unfused_qkv_rope(_ptr(qkv), _ptr(q), _ptr(k), _ptr(v), qkv.shape[0], n_heads,
-                                 head_dim, _ptr(positions), base, q_scale, dtype_code(qkv),
-                                 _stream(stream)), "unfused_qkv_rope")
+    _check(_lib.unfused_qkv_rope(*_a_unfused_qkv_rope(qkv, q, k, v, n_heads, head_dim, positions,
+                                                      base, q_scale, stream)), "unfused_qkv_rope")
     return q, k, v

@@ -20,7 +20,20 @@ def hipcc_command(out: str) -> list[str]:
             *srcs, "-lhiprtc", "-o", out]
 
 
+def write_generated() -> None:
+    """csrc/gen_fastmath.inc: fastmath.h as a C++ raw string literal, so that
+    runtime-specialised kernels contain exactly the library's device functions."""
+    src = open(os.path.join(PKG, "csrc", "fastmath.h")).read()
+    assert ")NPFM\"" not in src
+    text = 'R"NPFM(' + src + ')NPFM"\n'
+    path = os.path.join(PKG, "csrc", "gen_fastmath.inc")
+    if not os.path.exists(path) or open(path).read() != text:
+        with open(path, "w") as f:
+            f.write(text)
+
+
 def build(verbose: bool = False) -> str:
+    write_generated()
     tmp = LIB + ".tmp"
     cmd = hipcc_command(tmp)
     if verbose:

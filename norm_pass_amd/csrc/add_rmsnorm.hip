@@ -4,7 +4,8 @@
 //
 // Register path: one workgroup of WAVES wave64s per row; each thread holds VPT
 // 16-byte vectors of the row in registers between the two phases, so x and r
-// are read once and h and out written once:
+// are read once and h and out written once (non-temporal stores: the outputs
+// are not read again by this kernel):
 //   h = round(x + r) -> store h; sum of h^2 in fp32 per thread -> wave64 DPP
 //   reduction -> one LDS slot per wave -> every thread adds the WAVES partials
 //   in a fixed order -> rstd = 1/sqrt(mean + eps) -> out = h * rstd * w.
@@ -28,7 +29,7 @@ __device__ __forceinline__ float block_sum(float v, float* part) {
   return tot;
 }
 
-template <typename T, int VPT, int WAVES>
+template <typename T, int VPT, int WAVES, bool HAS_R, bool HAS_W, bool HAS_H>
 __global__ __launch_bounds__(64 * WAVES) void rms_vec(const T* x, const T* r, const T* w, T* h,
                                                       T* out, int cols, float eps) {
   constexpr int N = Vec<T>::N;
@@ -43,13 +44,13 @@ __global__ __launch_bounds__(64 * WAVES) void rms_vec(const T* x, const T* r, co
     const int vi = threadIdx.x + j * THREADS;
     if (vi < nvec) {
       load_vec<T>(x + off + vi * N, hv[j]);
-      if (r) {
+      if (HAS_R) {
         float rv[N];
         load_vec<T>(r + off + vi * N, rv);
 #pragma unroll
         for (int e = 0; e < N; ++e) hv[j][e] += rv[e];
       }
-      if (w) {
+      if (HAS_W) {
         load_vec<T>(w + vi * N, wv[j]);
       } else {
 #pragma unroll
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(64 * WAVES) void rms_vec(const T* x, const T* r, co
       hv[j][e] = round_via<T>(hv[j][e]);  // the stored h is what the norm sees
       ss += hv[j][e] * hv[j][e];
     }
-    if (h && vi < nvec) store_vec<T>(h + off + vi * N, hv[j]);
+    if (HAS_H && vi < nvec) store_vec_nt<T>(h + off + vi * N, hv[j]);
   }
   const float tot = block_sum<WAVES>(ss, part);
   const float rstd = 1.0f / sqrtf(tot / (float)cols + eps);
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(64 * WAVES) void rms_vec(const T* x, const T* r, co
       float o[N];
 #pragma unroll
       for (int e = 0; e < N; ++e) o[e] = hv[j][e] * rstd * wv[j][e];
-      store_vec<T>(out + off + vi * N, o);
+      store_vec_nt<T>(out + off + vi * N, o);
     }
   }
 }
@@ -114,13 +115,29 @@ __global__ __launch_bounds__(256) void rms_generic(const T* x, const T* r, const
   }
 }
 
+template <typename T, int VPT, bool HAS_R, bool HAS_W, bool HAS_H>
+void launch_vec3(const void* x, const void* r, const void* w, void* h, void* out, int64_t rows,
+                 int cols, float eps, hipStream_t s) {
+  hipLaunchKernelGGL((rms_vec<T, VPT, 4, HAS_R, HAS_W, HAS_H>), dim3((unsigned)rows), dim3(256), 0,
+                     s, static_cast<const T*>(x), static_cast<const T*>(r),
+                     static_cast<const T*>(w), static_cast<T*>(h), static_cast<T*>(out), cols,
+                     eps);
+}
+
 template <typename T, int VPT>
 void launch_vec(const void* x, const void* r, const void* w, void* h, void* out, int64_t rows,
                 int cols, float eps, hipStream_t s) {
-  hipLaunchKernelGGL((rms_vec<T, VPT, 4>), dim3((unsigned)rows), dim3(256), 0, s,
-                     static_cast<const T*>(x), static_cast<const T*>(r),
-                     static_cast<const T*>(w), static_cast<T*>(h), static_cast<T*>(out), cols,
-                     eps);
+  const int key = (r ? 4 : 0) | (w ? 2 : 0) | (h ? 1 : 0);
+  switch (key) {
+    case 7: launch_vec3<T, VPT, true, true, true>(x, r, w, h, out, rows, cols, eps, s); break;
+    case 6: launch_vec3<T, VPT, true, true, false>(x, r, w, h, out, rows, cols, eps, s); break;
+    case 5: launch_vec3<T, VPT, true, false, true>(x, r, w, h, out, rows, cols, eps, s); break;
+    case 4: launch_vec3<T, VPT, true, false, false>(x, r, w, h, out, rows, cols, eps, s); break;
+    case 3: launch_vec3<T, VPT, false, true, true>(x, r, w, h, out, rows, cols, eps, s); break;
+    case 2: launch_vec3<T, VPT, false, true, false>(x, r, w, h, out, rows, cols, eps, s); break;
+    case 1: launch_vec3<T, VPT, false, false, true>(x, r, w, h, out, rows, cols, eps, s); break;
+    default: launch_vec3<T, VPT, false, false, false>(x, r, w, h, out, rows, cols, eps, s); break;
+  }
 }
 
 template <typename T>

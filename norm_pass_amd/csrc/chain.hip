@@ -8,6 +8,8 @@
 // thread handles U groups of G elements with dwordx4 loads and stores, and the
 // running value stays in fp32 registers; it is rounded only at cast ops and at
 // the final store.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -15,19 +17,21 @@ namespace np {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int64_t kMinVecGroups = 65536;
 
 __device__ __forceinline__ float relu_f(float v) { return v > 0.0f ? v : 0.0f; }
 
 // Apply a unary op of the chain to one value.
+template <bool FAST>
 __device__ __forceinline__ float unary(int kind, float c, float v) {
   switch (kind) {
     case NP_ADD_C: return v + c;
     case NP_MUL_C:
     case NP_SCALE: return v * c;
     case NP_RELU: return relu_f(v);
-    case NP_SIGMOID: return sigmoid_f(v);
-    case NP_EXP: return expf(v);
-    case NP_TANH: return tanhf(v);
+    case NP_SIGMOID: return chain_sigmoid<FAST>(v);
+    case NP_EXP: return chain_exp<FAST>(v);
+    case NP_TANH: return chain_tanh<FAST>(v);
     case NP_CAST_F16: return round_via<_Float16>(v);
     case NP_CAST_BF16: return round_via<__bf16>(v);
     default: return v;
@@ -56,12 +60,12 @@ __device__ __forceinline__ void store_group(T* p, const float (&v)[G]) {
     float t[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) t[i] = v[j * N + i];
-    store_vec<T>(p + j * N, t);
+    store_vec_nt<T>(p + j * N, t);
   }
 }
 
 // Run the op list over a block of values (K values per input).
-template <int NIN, int K>
+template <bool FAST, int NIN, int K>
 __device__ __forceinline__ void run_ops(const ChainArgs& a, const float (&x)[NIN][K],
                                         float (&v)[K]) {
   for (int o = 0; o < a.n_ops; ++o) {
@@ -82,7 +86,7 @@ __device__ __forceinline__ void run_ops(const ChainArgs& a, const float (&x)[NIN
       switch (kind) {
 #define NP_CASE(KIND)                                          \
   case KIND:                                                   \
-    _Pragma("unroll") for (int e = 0; e < K; ++e) v[e] = unary(KIND, c, v[e]); \
+    _Pragma("unroll") for (int e = 0; e < K; ++e) v[e] = unary<FAST>(KIND, c, v[e]); \
     break;
         NP_CASE(NP_ADD_C)
         NP_CASE(NP_MUL_C)
@@ -100,10 +104,16 @@ __device__ __forceinline__ void run_ops(const ChainArgs& a, const float (&x)[NIN
   }
 }
 
+template <typename Tout>
+constexpr bool fast_math_for() {
+  return std::is_same_v<Tout, _Float16>;  // fp16 output
+}
+
 // Vector kernel: thread handles U groups of G elements; the < G leftover
 // elements at the end are handled one per thread by the first threads.
 template <typename Tin, typename Tout, int NIN, int U, int G>
 __global__ __launch_bounds__(kBlock) void chain_vec(ChainArgs a) {
+  constexpr bool FAST = fast_math_for<Tout>();
   const int64_t ngroups = a.n / G;
   const int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
   float x[NIN][U * G];
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void chain_vec(ChainArgs a) {
         for (int e = 0; e < G; ++e) x[j][u * G + e] = 0.0f;
     }
   }
-  run_ops<NIN, U * G>(a, x, v);
+  run_ops<FAST, NIN, U * G>(a, x, v);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t g = base + (int64_t)u * kBlock;
@@ -146,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void chain_vec(ChainArgs a) {
     float vs[1];
 #pragma unroll
     for (int j = 0; j < NIN; ++j) xs[j][0] = to_f(static_cast<const Tin*>(a.in[j])[i]);
-    run_ops<NIN, 1>(a, xs, vs);
+    run_ops<FAST, NIN, 1>(a, xs, vs);
     static_cast<Tout*>(a.out)[i] = from_f<Tout>(vs[0]);
   }
 }
@@ -154,21 +164,23 @@ __global__ __launch_bounds__(kBlock) void chain_vec(ChainArgs a) {
 // Scalar kernel (any alignment): one element per thread.
 template <typename Tin, typename Tout, int NIN>
 __global__ __launch_bounds__(kBlock) void chain_scalar(ChainArgs a) {
+  constexpr bool FAST = fast_math_for<Tout>();
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (i >= a.n) return;
   float xs[NIN][1];
   float vs[1];
 #pragma unroll
   for (int j = 0; j < NIN; ++j) xs[j][0] = to_f(static_cast<const Tin*>(a.in[j])[i]);
-  run_ops<NIN, 1>(a, xs, vs);
+  run_ops<FAST, NIN, 1>(a, xs, vs);
   static_cast<Tout*>(a.out)[i] = from_f<Tout>(vs[0]);
 }
 
 template <typename Tin, typename Tout, int NIN>
 hipError_t launch_typed(const ChainArgs& a, bool vec, hipStream_t s) {
-  if (vec) {
-    constexpr int G = (sizeof(Tin) == 2 || sizeof(Tout) == 2) ? 8 : 4;
-    constexpr int U = 2;
+  constexpr int G = (sizeof(Tin) == 2 || sizeof(Tout) == 2) ? 8 : 4;
+  // below 64 Ki vector groups the chip is better filled by one element per thread
+  if (vec && a.n / G >= kMinVecGroups) {
+    constexpr int U = 1;
     const int64_t ngroups = a.n / G;
     int64_t blocks = (ngroups + (int64_t)kBlock * U - 1) / ((int64_t)kBlock * U);
     if (blocks < 1) blocks = 1;  // the tail still needs threads

@@ -20,20 +20,52 @@ namespace {
 
 constexpr int kBlock = 256;
 
-__device__ __forceinline__ float decode_one(const DetArgs& a, int l, int an, int k, int cell,
-                                            float t) {
-  const int W = a.W[l];
-  if (k == 0) return (sigmoid_f(t) + (float)(cell % W)) * a.stride[l];
-  if (k == 1) return (sigmoid_f(t) + (float)(cell / W)) * a.stride[l];
-  if (k == 2) return expf(t) * a.anchor[(l * a.n_anchors + an) * 2 + 0];
-  if (k == 3) return expf(t) * a.anchor[(l * a.n_anchors + an) * 2 + 1];
-  return sigmoid_f(t);
+// One formula for every channel, so that the lanes of a wave (which hold
+// different channels) do not diverge: channels 2 and 3 need exp(t), all others
+// sigmoid(t) = 1 / (1 + exp(-t)); one exp of +-t serves both.
+//   k = 0: (sigmoid + x) * stride   k = 1: (sigmoid + y) * stride
+//   k = 2: exp * anchor_w           k = 3: exp * anchor_h      k >= 4: sigmoid
+// Per-tile constants (stride, anchor, 1/W) are read once per workgroup.
+struct TileConst {
+  float stride, aw, ah, inv_w;
+  int w;
+};
+
+__device__ __forceinline__ float decode_one(const TileConst& tc, int k, int cell, float t) {
+  const bool is_exp = k == 2 || k == 3;
+  const float e = expf(is_exp ? t : -t);
+  // cell / W and cell % W: (cell + 0.5) / W is >= 0.5 / W from an integer, far
+  // above the float rounding for cell < 2^22, so truncation gives the row
+  const int y = (int)(((float)cell + 0.5f) * tc.inv_w);
+  const int x = cell - y * tc.w;
+  const float grid = k == 0 ? (float)x : k == 1 ? (float)y : 0.0f;
+  const float mul = k < 2 ? tc.stride : 1.0f;
+  const float anc = k == 3 ? tc.ah : tc.aw;
+  return is_exp ? e * anc : (1.0f / (1.0f + e) + grid) * mul;
+}
+
+#ifndef NP_DET_XCD_REMAP
+#define NP_DET_XCD_REMAP 1
+#endif
+
+// Workgroups are dispatched to the 8 XCDs round robin (workgroup b -> XCD
+// b % 8), and each XCD has its own L2. Consecutive tiles share the 128-byte
+// lines of every channel plane (a 16-cell fp16 tile covers 32 bytes of a
+// line), so map the j-th workgroup of XCD x to tile start(x) + j: each XCD
+// processes one contiguous run of tiles and every line is fetched into one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+  constexpr int kXcds = 8;
+  const int x = bid % kXcds;
+  const int j = bid / kXcds;
+  const int per = nb / kXcds;
+  const int rem = nb % kXcds;
+  return x * per + min(x, rem) + j;
 }
 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
   extern __shared__ float tile[];
-  const int bid = blockIdx.x;
+  const int bid = NP_DET_XCD_REMAP ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
   int l = 0;
   while (l + 1 < a.n_levels && bid >= a.tile_start[l + 1]) ++l;
   const int idx = bid - a.tile_start[l];
@@ -49,6 +81,12 @@ __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
   const int cell0 = tl * TP;
   const int ncell = min(TP, HW - cell0);
   const T* plane0 = static_cast<const T*>(a.in[l]) + ((int64_t)(b * A + an) * C) * HW + cell0;
+  TileConst tc;
+  tc.stride = a.stride[l];
+  tc.aw = a.anchor[(l * A + an) * 2 + 0];
+  tc.ah = a.anchor[(l * A + an) * 2 + 1];
+  tc.w = a.W[l];
+  tc.inv_w = 1.0f / (float)tc.w;
 
   // phase 1: channel planes -> decoded values in row layout
   if (VEC) {
@@ -62,7 +100,7 @@ __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         const int c = cg * N + i;
-        tile[c * C + k] = decode_one(a, l, an, k, cell0 + c, t[i]);
+        tile[c * C + k] = decode_one(tc, k, cell0 + c, t[i]);
       }
     }
   } else {
@@ -70,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
       const int k = e / ncell;
       const int c = e - k * ncell;
       const float t = to_f(plane0[(int64_t)k * HW + c]);
-      tile[c * C + k] = decode_one(a, l, an, k, cell0 + c, t);
+      tile[c * C + k] = decode_one(tc, k, cell0 + c, t);
     }
   }
   __syncthreads();
@@ -90,7 +128,7 @@ __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
       q.y = __builtin_bit_cast(uint32_t, tile[o + 1]);
       q.z = __builtin_bit_cast(uint32_t, tile[o + 2]);
       q.w = __builtin_bit_cast(uint32_t, tile[o + 3]);
-      store_raw(dst + o, q);
+      store_raw_nt(dst + o, q);
     }
     for (int i = head + 4 * nvec + threadIdx.x; i < len; i += kBlock) dst[i] = tile[i];
   } else {

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastmath.h"
+
 namespace np {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -55,6 +57,22 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[Vec<T>::N]) {
   *reinterpret_cast<u32x4*>(p) = raw;
 }
 
+// The same store with the non-temporal hint: outputs written once and not read
+// again by the kernel are streamed past the caches (global_store ... nt).
+template <typename T>
+__device__ __forceinline__ void store_vec_nt(T* p, const float (&v)[Vec<T>::N]) {
+  T e[Vec<T>::N];
+#pragma unroll
+  for (int i = 0; i < Vec<T>::N; ++i) e[i] = from_f<T>(v[i]);
+  u32x4 raw;
+  __builtin_memcpy(&raw, e, 16);
+  __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(p));
+}
+
+__device__ __forceinline__ void store_raw_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ u32x4 load_raw(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -86,5 +104,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // Logistic sigmoid with the device library's accurate expf and an IEEE divide.
 __device__ __forceinline__ float sigmoid_f(float t) { return 1.0f / (1.0f + expf(-t)); }
+
+// Chain transcendentals: the device library's accurate functions, or the
+// fastmath.h forms when the chain's output is fp16 (FAST).
+template <bool FAST>
+__device__ __forceinline__ float chain_exp(float v) { return FAST ? np_fast_exp(v) : expf(v); }
+template <bool FAST>
+__device__ __forceinline__ float chain_sigmoid(float v) {
+  return FAST ? np_fast_sigmoid(v) : sigmoid_f(v);
+}
+template <bool FAST>
+__device__ __forceinline__ float chain_tanh(float v) { return FAST ? np_fast_tanh(v) : tanhf(v); }
 
 }  // namespace np

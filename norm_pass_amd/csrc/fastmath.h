@@ -1,0 +1,54 @@
+// Transcendentals for chains whose output is fp16: a few fp32 ulps of error
+// (the fp16 output keeps 11 significand bits), built on the hardware's base-2
+// exponential (v_exp_f32) and reciprocal (v_rcp_f32). This file is compiled
+// into the library and also pasted verbatim into runtime-specialised kernels,
+// so it uses only compiler builtins.
+//
+// exp(x) = 2^(x log2 e): the argument is clamped to [-200, 200] (exp is 0 or
+// inf in binary32 beyond that), the product x * log2(e) is split into its
+// rounded value t and the rounding error err (an FMA recovers it exactly, a
+// second FMA adds the error of the binary32 constant: Cody and Waite's
+// argument splitting), v_exp_f32 evaluates 2^t, and the result is scaled by
+// 2^err ~ 1 + err ln 2 (rounded to binary32, <= 0.5 ulp). Results below 2^-126
+// are flushed to zero by the hardware exponential; an fp16 output cannot hold
+// them anyway. Error <= 2 ulp.
+// sigmoid(x) = 1 / (1 + exp(-x)) with the hardware reciprocal. Error <= 4 ulp.
+// tanh(x): for |x| < 0.625 the odd polynomial x + x^3 P(x^2), P of degree 4
+// fitted to minimise the relative error on [0, 0.625] (a Lawson-weighted least
+// squares fit; 0.07 ulp approximation error); otherwise 1 - 2 / (1 + e^(2|x|)),
+// whose cancellation is at most 3.7x there. Error <= 2 ulp.
+#pragma once
+
+#define NP_FM_INLINE __device__ __forceinline__
+
+NP_FM_INLINE float np_fast_exp(float x) {
+  const float kLog2e = 1.44269502162933349609375f;      // binary32 nearest to log2(e)
+  const float kLog2eLo = 1.925963033500011e-08f;        // log2(e) - kLog2e
+  const float kLn2 = 0.693147180559945309f;
+  const float xc = __builtin_amdgcn_fmed3f(x, -200.0f, 200.0f);
+  const float t = xc * kLog2e;
+  const float err = __builtin_fmaf(xc, kLog2eLo, __builtin_fmaf(xc, kLog2e, -t));
+  return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(err, kLn2, 1.0f);
+}
+
+NP_FM_INLINE float np_fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + np_fast_exp(-x));
+}
+
+NP_FM_INLINE float np_fast_tanh(float x) {
+  const float a = __builtin_fabsf(x);
+  float r;
+  if (a < 0.625f) {  // a branch, not a select: a wave whose lanes agree runs one side
+    const float z = a * a;
+    float p = -0.005704987328499556f;
+    p = __builtin_fmaf(p, z, 0.0206390880048275f);
+    p = __builtin_fmaf(p, z, -0.05373971536755562f);
+    p = __builtin_fmaf(p, z, 0.13331441581249237f);
+    p = __builtin_fmaf(p, z, -0.3333328068256378f);
+    r = __builtin_fmaf(a * z, p, a);
+  } else {
+    const float e = __builtin_amdgcn_exp2f(a * 2.88539008177792681f);  // e^(2a) = 2^(2a log2 e)
+    r = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+  }
+  return __builtin_copysignf(r, x);
+}

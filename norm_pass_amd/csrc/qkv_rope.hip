@@ -2,7 +2,18 @@
 // 2kiu.com/news/5927820, section 3.1: multi-head split, rotary position
 // encoding and scaling after the QKV projection, as one fused group).
 //
-// Input: packed rows [T, 3, H, D]; outputs head-major [H, T, D]. A thread owns
+// Main path (head vectors of exactly 16 chunks of 16 bytes, e.g. D = 128 in
+// bf16): one workgroup per token streams the token's packed row [3, H, D]
+// front to back, one 16-byte chunk per lane, so reads are fully sequential. A
+// head vector then sits in one 16-lane DPP row and the rotation partner of
+// chunk j (j +- 8, the other half) is fetched from the neighbouring lane with
+// row_ror:8 instead of being loaded again. The token's D/2 angles and their
+// sine/cosine are computed once into LDS (also pre-multiplied by q_scale for
+// Q, so Q costs no extra multiply) and shared by all 2H rotated vectors.
+// Writes are whole 256-byte head vectors into the head-major outputs, with the
+// non-temporal hint (nothing reads them back here).
+//
+// Other layouts: packed rows [T, 3, H, D]; outputs head-major [H, T, D]. A thread owns
 // one token t and one 16-byte chunk j of the first half of a head vector (the
 // matching chunk of the second half is its rotation partner). It evaluates the
 // chunk's E angles theta = fp32(pos) * inv_i and their sine/cosine once, then
@@ -17,6 +28,69 @@ namespace np {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kTokBlock = 384;
+
+template <typename T, int NC>
+__global__ __launch_bounds__(kTokBlock) void rope_tok(RopeArgs a) {
+  constexpr int E = Vec<T>::N;  // elements per 16-byte chunk; D == 16 * E here
+  constexpr int HALF = 8 * E;
+  // cos / sin of the token's angles, plain (K) and multiplied by q_scale (Q)
+  __shared__ float tab[4][HALF];
+  const int64_t t = blockIdx.x;
+  const float p = a.pos ? (float)a.pos[t] : (float)t;
+  for (int i = threadIdx.x; i < HALF; i += kTokBlock) {
+    float sv, cv;
+    sincosf(p * a.inv[i], &sv, &cv);  // theta = fp32(pos) * inv_i: one fp32 multiply
+    tab[0][i] = cv;
+    tab[1][i] = sv;
+    tab[2][i] = cv * a.q_scale;
+    tab[3][i] = sv * a.q_scale;
+  }
+  const int total = 3 * a.H * 16;  // chunks in the token's packed row
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.qkv)) + t * total;
+  u32x4 raw[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = threadIdx.x + i * kTokBlock;
+    raw[i] = load_raw(src + (c < total ? c : 0));
+  }
+  __syncthreads();
+  const int l16 = threadIdx.x & 15;
+  const bool second = l16 >= 8;
+  const int f0 = (l16 & 7) * E;
+  const float inv_h = 1.0f / (float)a.H;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = threadIdx.x + i * kTokBlock;
+    const int hv = c >> 4;  // head vector within the token: s * H + h
+    // s = hv / H, exact: (hv + 0.5) / H is at least 0.5 / H away from an integer
+    const int s = (int)(((float)hv + 0.5f) * inv_h);
+    const int h = hv - s * a.H;
+    u32x4 res = raw[i];
+    // the DPP partner read needs every lane of the row: all lanes take part,
+    // V lanes keep their raw chunk (the branch is wave-uniform when H % 4 == 0)
+    T e_in[E];
+    __builtin_memcpy(e_in, &raw[i], 16);
+    float x[E], pr[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = to_f(e_in[e]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) pr[e] = dpp_f<0x128>(x[e]);  // row_ror:8 -> partner half
+    if (s < 2) {
+      const float* cs = tab[s == 0 ? 2 : 0] + f0;
+      const float* sn = tab[s == 0 ? 3 : 1] + f0;
+      T e_out[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        e_out[e] = from_f<T>(second ? x[e] * cs[e] + pr[e] * sn[e] : x[e] * cs[e] - pr[e] * sn[e]);
+      __builtin_memcpy(&res, e_out, 16);
+    }
+    if (c < total) {
+      T* dst = static_cast<T*>(s == 0 ? a.q : s == 1 ? a.k : a.v);
+      store_raw_nt(reinterpret_cast<u32x4*>(dst) + ((int64_t)h * a.T + t) * 16 + l16, res);
+    }
+  }
+}
 
 template <typename T, int HU>
 __global__ __launch_bounds__(kBlock) void rope_vec(RopeArgs a) {
@@ -37,8 +111,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec(RopeArgs a) {
     for (int h = 0; h < a.H; ++h) {
       const u32x4 x0 = load_raw(src + (int64_t)h * a.D + lo);
       const u32x4 x1 = load_raw(src + (int64_t)h * a.D + hi);
-      store_raw(dst + h * hstride + lo, x0);
-      store_raw(dst + h * hstride + hi, x1);
+      store_raw_nt(dst + h * hstride + lo, x0);
+      store_raw_nt(dst + h * hstride + hi, x1);
     }
     return;
   }
@@ -66,8 +140,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec(RopeArgs a) {
         o1[e] = (u[k][e] * cs[e] - w[k][e] * sn[e]) * sc;
         o2[e] = (w[k][e] * cs[e] + u[k][e] * sn[e]) * sc;
       }
-      store_vec<T>(dst + (h + k) * hstride + lo, o1);
-      store_vec<T>(dst + (h + k) * hstride + hi, o2);
+      store_vec_nt<T>(dst + (h + k) * hstride + lo, o1);
+      store_vec_nt<T>(dst + (h + k) * hstride + hi, o2);
     }
   }
   for (; h < a.H; ++h) {
@@ -79,8 +153,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec(RopeArgs a) {
       o1[e] = (u[e] * cs[e] - w[e] * sn[e]) * sc;
       o2[e] = (w[e] * cs[e] + u[e] * sn[e]) * sc;
     }
-    store_vec<T>(dst + h * hstride + lo, o1);
-    store_vec<T>(dst + h * hstride + hi, o2);
+    store_vec_nt<T>(dst + h * hstride + lo, o1);
+    store_vec_nt<T>(dst + h * hstride + hi, o2);
   }
 }
 
@@ -115,12 +189,29 @@ __global__ __launch_bounds__(kBlock) void rope_scalar(RopeArgs a) {
   dst[i + half] = from_f<T>((w * cs + u * sn) * sc);
 }
 
+template <typename T, int NC>
+void launch_tok(const RopeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((rope_tok<T, NC>), dim3((unsigned)a.T), dim3(kTokBlock), 0, s, a);
+}
+
 template <typename T>
 hipError_t launch_t(const RopeArgs& a, bool vec, hipStream_t s) {
   constexpr int E = Vec<T>::N;
   const int half = a.D / 2;
   const int P = half / E;
-  if (vec && half % E == 0 && P > 0 && kBlock % P == 0) {
+  const int nc = (3 * a.H * 16 + kTokBlock - 1) / kTokBlock;
+  if (vec && a.D == 16 * E && nc <= 8) {
+    switch (nc) {
+      case 1: launch_tok<T, 1>(a, s); break;
+      case 2: launch_tok<T, 2>(a, s); break;
+      case 3: launch_tok<T, 3>(a, s); break;
+      case 4: launch_tok<T, 4>(a, s); break;
+      case 5: launch_tok<T, 5>(a, s); break;
+      case 6: launch_tok<T, 6>(a, s); break;
+      case 7: launch_tok<T, 7>(a, s); break;
+      default: launch_tok<T, 8>(a, s); break;
+    }
+  } else if (vec && half % E == 0 && P > 0 && kBlock % P == 0) {
     const int TB = kBlock / P;
     const unsigned gx = (unsigned)((a.T + TB - 1) / TB);
     hipLaunchKernelGGL((rope_vec<T, 4>), dim3(gx, 3), dim3(kBlock), 0, s, a);

@@ -25,6 +25,11 @@
 namespace np {
 namespace {
 
+// fastmath.h, pasted into generated sources (written by the build as a raw string)
+const char* kFastMathSource =
+#include "gen_fastmath.inc"
+    ;
+
 const char* type_name(int dt) {
   return dt == NP_F32 ? "float" : dt == NP_F16 ? "_Float16" : "__bf16";
 }
@@ -35,7 +40,7 @@ std::string hexf(float c) {
   return buf;
 }
 
-std::string op_line(int kind, int arg, float c) {
+std::string op_line(int kind, int arg, float c, bool fast) {
   const std::string x = "x" + std::to_string(arg) + "[e]";
   switch (kind) {
     case NP_LOAD: return "v = " + x + ";";
@@ -45,9 +50,9 @@ std::string op_line(int kind, int arg, float c) {
     case NP_MUL_C:
     case NP_SCALE: return "v = v * " + hexf(c) + ";";
     case NP_RELU: return "v = v > 0.0f ? v : 0.0f;";
-    case NP_SIGMOID: return "v = 1.0f / (1.0f + expf(-v));";
-    case NP_EXP: return "v = expf(v);";
-    case NP_TANH: return "v = tanhf(v);";
+    case NP_SIGMOID: return fast ? "v = np_fast_sigmoid(v);" : "v = 1.0f / (1.0f + expf(-v));";
+    case NP_EXP: return fast ? "v = np_fast_exp(v);" : "v = expf(v);";
+    case NP_TANH: return fast ? "v = np_fast_tanh(v);" : "v = tanhf(v);";
     case NP_CAST_F16: return "v = (float)(_Float16)v;";
     case NP_CAST_BF16: return "v = (float)(__bf16)v;";
   }
@@ -56,9 +61,13 @@ std::string op_line(int kind, int arg, float c) {
 
 struct Entry {
   hipModule_t mod = nullptr;
-  hipFunction_t fn = nullptr;
+  hipFunction_t fn = nullptr;         // vector kernel
+  hipFunction_t fn_scalar = nullptr;  // one element per thread
   size_t src_hash = 0;
 };
+
+// Same threshold as the generic kernel: below it, one element per thread.
+constexpr int64_t kMinVecGroups = 65536;
 
 std::mutex g_mu;
 std::map<std::string, Entry> g_cache;  // spec key -> loaded kernel
@@ -110,32 +119,32 @@ int compile(const std::string& src, std::vector<char>* code, std::string* log) {
 
 std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, int64_t n) {
   const int G = (in_dt != NP_F32 || out_dt != NP_F32) ? 8 : 4;
-  const int U = 2;
+  const bool fast = out_dt == NP_F16;  // same transcendental policy as the generic kernel
   std::ostringstream s;
   s << "// generated: fused elementwise chain, " << a.n_ops << " ops\n"
+    << kFastMathSource << "\n"
     << "typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));\n"
     << "typedef " << type_name(in_dt) << " tin;\n"
     << "typedef " << type_name(out_dt) << " tout;\n"
     << "#define NPS_N " << n << "LL\n"
     << "#define NPS_G " << G << "\n"
-    << "#define NPS_U " << U << "\n"
     << "#define NPS_IN_PER_VEC " << 16 / (in_dt == NP_F32 ? 4 : 2) << "\n"
     << "#define NPS_OUT_PER_VEC " << 16 / (out_dt == NP_F32 ? 4 : 2) << "\n"
     << "__device__ __forceinline__ float chain(";
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "const float* x" << j;
   s << ", int e) {\n  float v = 0.0f;\n";
-  for (int i = 0; i < a.n_ops; ++i) s << "  " << op_line(a.kind[i], a.arg[i], a.c[i]) << "\n";
-  s << "  return v;\n}\n"
-    << "extern \"C\" __global__ __launch_bounds__(256) void np_chain_spec(";
+  for (int i = 0; i < a.n_ops; ++i)
+    s << "  " << op_line(a.kind[i], a.arg[i], a.c[i], fast) << "\n";
+  s << "  return v;\n}\n";
+  // vector kernel: one group of NPS_G elements per thread, dwordx4 accesses,
+  // non-temporal stores; the < NPS_G leftover elements go to the first threads
+  s << "extern \"C\" __global__ __launch_bounds__(256) void np_chain_spec(";
   for (int j = 0; j < n_inputs; ++j) s << "const tin* in" << j << ", ";
   s << "tout* out, long long n_rt) {\n"
     << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
     << "  const long long ngroups = n / NPS_G;\n"
-    << "  const long long base = (long long)blockIdx.x * 256 * NPS_U + threadIdx.x;\n"
-    << "#pragma unroll\n"
-    << "  for (int u = 0; u < NPS_U; ++u) {\n"
-    << "    const long long g = base + (long long)u * 256;\n"
-    << "    if (g >= ngroups) break;\n";
+    << "  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;\n"
+    << "  if (g < ngroups) {\n";
   for (int j = 0; j < n_inputs; ++j) {
     s << "    float x" << j << "[NPS_G];\n"
       << "#pragma unroll\n"
@@ -155,17 +164,27 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
     << "#pragma unroll\n"
     << "    for (int q = 0; q < NPS_G / NPS_OUT_PER_VEC; ++q) {\n"
     << "      u32x4 raw; __builtin_memcpy(&raw, o + q * NPS_OUT_PER_VEC, 16);\n"
-    << "      *(u32x4*)(out + g * NPS_G + q * NPS_OUT_PER_VEC) = raw;\n"
+    << "      __builtin_nontemporal_store(raw, (u32x4*)(out + g * NPS_G + q * NPS_OUT_PER_VEC));\n"
     << "    }\n"
     << "  }\n"
     << "  const long long tail0 = ngroups * NPS_G;\n"
-    << "  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;\n"
-    << "  if (gid < n - tail0) {\n"
-    << "    const long long i = tail0 + gid;\n";
+    << "  if (g < n - tail0) {\n"
+    << "    const long long i = tail0 + g;\n";
   for (int j = 0; j < n_inputs; ++j) s << "    float x" << j << "[1] = {(float)in" << j << "[i]};\n";
   s << "    out[i] = (tout)chain(";
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "x" << j;
   s << ", 0);\n  }\n}\n";
+  // scalar kernel: one element per thread (small n, where it fills the chip better)
+  s << "extern \"C\" __global__ __launch_bounds__(256) void np_chain_spec_scalar(";
+  for (int j = 0; j < n_inputs; ++j) s << "const tin* in" << j << ", ";
+  s << "tout* out, long long n_rt) {\n"
+    << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
+    << "  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;\n"
+    << "  if (i >= n) return;\n";
+  for (int j = 0; j < n_inputs; ++j) s << "  float x" << j << "[1] = {(float)in" << j << "[i]};\n";
+  s << "  out[i] = (tout)chain(";
+  for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "x" << j;
+  s << ", 0);\n}\n";
   return s.str();
 }
 
@@ -201,7 +220,8 @@ int rtc_prepare(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, std::st
   Entry e;
   e.src_hash = h;
   if (hipModuleLoadData(&e.mod, code.data()) != hipSuccess ||
-      hipModuleGetFunction(&e.fn, e.mod, "np_chain_spec") != hipSuccess) {
+      hipModuleGetFunction(&e.fn, e.mod, "np_chain_spec") != hipSuccess ||
+      hipModuleGetFunction(&e.fn_scalar, e.mod, "np_chain_spec_scalar") != hipSuccess) {
     *log = "module load failed";
     if (e.mod) (void)hipModuleUnload(e.mod);
     return NP_ELAUNCH;
@@ -215,6 +235,9 @@ bool rtc_launch(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, hipStre
                 hipError_t* err) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
+  const int G = (in_dt != NP_F32 || out_dt != NP_F32) ? 8 : 4;
+  const int64_t ngroups = a.n / G;
+  const bool scalar = ngroups < kMinVecGroups;
   hipFunction_t fn = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_mu);
@@ -222,11 +245,10 @@ bool rtc_launch(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, hipStre
     auto it = g_cache.find(spec_key(a, n_inputs, in_dt, out_dt, a.n, dev));
     if (it == g_cache.end()) it = g_cache.find(spec_key(a, n_inputs, in_dt, out_dt, 0, dev));
     if (it == g_cache.end()) return false;
-    fn = it->second.fn;
+    fn = scalar ? it->second.fn_scalar : it->second.fn;
   }
-  const int G = (in_dt != NP_F32 || out_dt != NP_F32) ? 8 : 4;
-  const int64_t ngroups = a.n / G;
-  int64_t blocks = (ngroups + 512 - 1) / 512;
+  const int64_t work = scalar ? a.n : ngroups;
+  int64_t blocks = (work + 255) / 256;
   if (blocks < 1) blocks = 1;
   void* params[NP_MAX_INPUTS + 2];
   const void* ins[NP_MAX_INPUTS];
@@ -255,6 +277,28 @@ void rtc_clear() {
 }
 
 }  // namespace np
+
+extern "C" int64_t np_chain_source(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt,
+                                   np_dtype out_dt, int64_t n, char* buf, size_t len) {
+  if (!ops || n_ops < 1 || n_ops > NP_MAX_OPS || n_inputs < 1 || n_inputs > NP_MAX_INPUTS ||
+      n < 0)
+    return NP_EINVAL;
+  np::ChainArgs a{};
+  a.n_ops = n_ops;
+  for (int i = 0; i < n_ops; ++i) {
+    if (ops[i].kind < NP_LOAD || ops[i].kind > NP_CAST_BF16) return NP_EINVAL;
+    a.kind[i] = ops[i].kind;
+    a.arg[i] = ops[i].arg;
+    a.c[i] = ops[i].c;
+  }
+  const std::string src = np::rtc_source(a, n_inputs, in_dt, out_dt, n);
+  if (buf && len > 0) {
+    const size_t m = src.size() < len - 1 ? src.size() : len - 1;
+    std::memcpy(buf, src.data(), m);
+    buf[m] = '\0';
+  }
+  return (int64_t)src.size() + 1;
+}
 
 extern "C" int np_chain_compile(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt,
                                 np_dtype out_dt, int64_t n, double* compile_ms,

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kBlock) void unary_kernel(int kind, float c, const 
       load_vec<T>(in + gid * N, v);
 #pragma unroll
       for (int e = 0; e < N; ++e) v[e] = unary_op(kind, c, v[e]);
-      store_vec<T>(out + gid * N, v);
+      store_vec_nt<T>(out + gid * N, v);
     }
     const int64_t i = nv * N + gid;
     if (gid < n - nv * N) out[i] = from_f<T>(unary_op(kind, c, to_f(in[i])));
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kBlock) void binary_kernel(int kind, const T* a, co
       load_vec<T>(b + gid * N, vb);
 #pragma unroll
       for (int e = 0; e < N; ++e) va[e] = binary_op(kind, va[e], vb[e]);
-      store_vec<T>(out + gid * N, va);
+      store_vec_nt<T>(out + gid * N, va);
     }
     const int64_t i = nv * N + gid;
     if (gid < n - nv * N) out[i] = from_f<T>(binary_op(kind, to_f(a[i]), to_f(b[i])));
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kBlock) void bcast_mul_kernel(const T* in, const T*
 #pragma unroll
       for (int e = 0; e < N; ++e) v[e] *= w[e];
     }
-    store_vec<T>(out + e0, v);
+    store_vec_nt<T>(out + e0, v);
   } else {
     if (gid >= rows * cols) return;
     const int64_t i = gid / cols;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kBlock) void qkv_split_kernel(const T* qkv, T* q, T
   const T* src = qkv + ((t * 3 + s) * H + h) * (int64_t)D + c * N;
   T* dst = (s == 0 ? q : s == 1 ? k : v) + ((int64_t)h * T_ + t) * D + c * N;
   if (vec)
-    store_raw(dst, load_raw(src));
+    store_raw_nt(dst, load_raw(src));
   else
     *dst = *src;
 }
@@ -186,8 +186,8 @@ __global__ __launch_bounds__(kBlock) void rope_inplace_kernel(T* x, int64_t T_, 
         o1[e] = u[e] * cs[e] - w[e] * sn[e];
         o2[e] = w[e] * cs[e] + u[e] * sn[e];
       }
-      store_vec<T>(row + j * E, o1);
-      store_vec<T>(row + half + j * E, o2);
+      store_vec_nt<T>(row + j * E, o1);
+      store_vec_nt<T>(row + half + j * E, o2);
     } else {
       const float u = to_f(row[j]);
       const float w = to_f(row[half + j]);

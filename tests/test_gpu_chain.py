@@ -108,7 +108,7 @@ def test_c5_small_full(npa, orc, fn):
     assert stats["n"] == 65536
 
 
-@pytest.mark.parametrize("n", [1, 7, 9, 1000, 65543])
+@pytest.mark.parametrize("n", [1, 7, 9, 1000, 65543, (1 << 19) + 8 * 3 + 5])
 def test_c5_ragged(npa, orc, n):
     _c5(npa, orc, synth.c5_inputs(n, seed=n), synth.c5_chain())
 
@@ -176,11 +176,13 @@ def test_random_short_chains(npa, orc, seed):
 
 
 def test_c5_specialised(npa, orc):
+    """Runtime-specialised kernels: one element per thread (small n) and 16-byte groups."""
     ops = synth.c5_chain()
     npa.fuse_chain_prepare(ops, 1, npa.NP_F16, npa.NP_F16, 0)
     try:
         _c5(npa, orc, synth.c5_inputs(65536), ops)
         _c5(npa, orc, synth.c5_inputs(1031, seed=9), ops)
+        _c5(npa, orc, synth.c5_inputs((1 << 20) + 5, seed=10), ops)
     finally:
         torch.cuda.synchronize()
         npa.np_shutdown()

@@ -62,11 +62,19 @@ def test_shapes_bf16(npa, orc, T, H, D, fn):
     _check(npa, orc, qkv, H, D, "bf16", qs=float(np.float32(1 / math.sqrt(D))), fn=fn)
 
 
-@pytest.mark.parametrize("dt", ["f16", "f32"])
-def test_other_dtypes(npa, orc, dt):
-    qkv = synth.c4_inputs(tokens=40, heads=3, head_dim=128, seed=5, dtype=dt)
-    _check(npa, orc, qkv, 3, 128, dt)
-    _check(npa, orc, qkv, 3, 128, dt, fn="unfused")
+@pytest.mark.parametrize("dt,D", [("f16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)])
+def test_other_dtypes(npa, orc, dt, D):
+    qkv = synth.c4_inputs(tokens=40, heads=3, head_dim=D, seed=5, dtype=dt)
+    qs = float(np.float32(1 / math.sqrt(D)))
+    _check(npa, orc, qkv, 3, D, dt, qs=qs)
+    _check(npa, orc, qkv, 3, D, dt, qs=qs, fn="unfused")
+
+
+@pytest.mark.parametrize("H", [1, 5, 8, 64, 65])
+def test_head_counts(npa, orc, H):
+    """Whole-token path for 1..64 heads (partial last chunk batch), generic beyond."""
+    qkv = synth.c4_inputs(tokens=9, heads=H, head_dim=128, seed=H)
+    _check(npa, orc, qkv, H, 128, "bf16")
 
 
 def test_positions_array_and_misaligned(npa, orc):
