@@ -163,6 +163,23 @@ def time_isolated(torch, fn, reps: int):
     return sum(s.elapsed_time(e) for s, e in ev) / reps / 1e3
 
 
+def graph_time(torch, npa, spec, reps: int, trials: int):
+    """Per-replay seconds of one call's launches captured in one HIP graph
+    (bound inside the capture, so the launches go to the capturing stream)."""
+    name, args = spec
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        npa.bind(name, *args)()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        npa.bind(name, *args)()
+    med, _, _ = time_calls(torch, g.replay, reps, trials)
+    torch.cuda.synchronize()
+    return med
+
+
 def pick_reps(torch, fn, target_s=0.003):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -200,6 +217,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         desc="fp32 relu(a+b)*0.5, 1,048,576 elements",
         fused=npa.bind("fuse_chain", synth.C1_CHAIN, [ta, tb], y1),
         unfused=npa.bind("unfused_chain", synth.C1_CHAIN, [ta, tb], y1),
+        unfused_spec=("unfused_chain", (synth.C1_CHAIN, [ta, tb], y1)),
         bytes=12 * n1, unfused_bytes=28 * n1, launches=3, kernel="chain_vec<float, float, 2")
     # C2
     lv = [tdev(x, "f16") for x in synth.c2_inputs()]
@@ -213,6 +231,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         desc="YOLO decode fp16 [1,255,80|40|20] -> fp32 [1,25200,85]",
         fused=npa.bind("fuse_det_decode", lv, st, an, out2),
         unfused=npa.bind("unfused_det_decode", lv, st, an, out2, ws2),
+        unfused_spec=("unfused_det_decode", (lv, st, an, out2, ws2)),
         bytes=fb, unfused_bytes=ub, launches=23, kernel="det_decode_kernel")
     # C3
     rows = 2048 if quick else 16384
@@ -235,6 +254,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         desc=f"bf16 residual add + RMSNorm [{rows}, 4096], eps 1e-6",
         fused=npa.bind("fuse_add_rmsnorm", tx, tr, tw, h3, o3, 1e-6),
         unfused=npa.bind("unfused_add_rmsnorm", tx, tr, tw, h3, o3, ws3, 1e-6),
+        unfused_spec=("unfused_add_rmsnorm", (tx, tr, tw, h3, o3, ws3, 1e-6)),
         bytes=fb, unfused_bytes=ub, launches=6, kernel="rms_vec")
     # C4
     T = 2048 if quick else 16384
@@ -252,6 +272,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         desc=f"bf16 QKV split + RoPE + scale, [{T}, 3x24x128] -> 3 x [24, {T}, 128]",
         fused=npa.bind("fuse_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
         unfused=npa.bind("unfused_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
+        unfused_spec=("unfused_qkv_rope", (qkv, q4, k4, v4, 24, 128, None, 10000.0, qs)),
         bytes=fb, unfused_bytes=ub, launches=4, kernel="rope_vec")
     # C5
     ops = synth.c5_chain()
@@ -265,6 +286,7 @@ def build_workloads(torch, npa, synth, quick: bool):
             desc=f"seeded 29-op fp16 chain, {n:,} elements",
             fused=npa.bind("fuse_chain", ops, [xin], yo),
             unfused=npa.bind("unfused_chain", ops, [xin], yo),
+            unfused_spec=("unfused_chain", (ops, [xin], yo)),
             bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29, kernel="chain_vec<_Float16")
     W["_compile_ms"] = compile_ms
     return W
@@ -402,6 +424,9 @@ def main(argv=None):
         f_med, f_p10, f_p90 = time_calls(torch, w["fused"], reps, args.trials)
         reps_u = pick_reps(torch, w["unfused"])
         u_med, _, _ = time_calls(torch, w["unfused"], reps_u, max(5, args.trials // 2))
+        # the same unfused launches captured once in a HIP graph and replayed:
+        # launch cost removed, every intermediate HBM round trip kept
+        g_med = graph_time(torch, npa, w["unfused_spec"], reps_u, max(5, args.trials // 2))
         gbps = w["bytes"] / f_med / 1e9
         cold = None
         if "cold" in w:
@@ -421,13 +446,15 @@ def main(argv=None):
             "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 1), "bytes": w["bytes"],
             "unfused": {"launches": w["launches"], "us_med": round(u_med * 1e6, 3),
                         "GBps": round(w["unfused_bytes"] / u_med / 1e9, 1),
-                        "bytes": w["unfused_bytes"]},
+                        "bytes": w["unfused_bytes"],
+                        "graph_us_med": round(g_med * 1e6, 3)},
             "speedup": round(u_med / f_med, 2),
         }
         if cold:
             per[k]["cold"] = cold
         log(f"[bench] {k}: fused {f_med * 1e6:.2f} us ({gbps:.0f} GB/s), "
-            f"unfused {u_med * 1e6:.2f} us x{w['launches']} launches"
+            f"unfused {u_med * 1e6:.2f} us x{w['launches']} launches "
+            f"(graph {g_med * 1e6:.2f} us)"
             + (f", cold {cold['us_med']:.2f} us ({cold['GBps']:.0f} GB/s)" if cold else ""))
 
     # achievable streaming ceiling: a plain 16-byte-per-lane copy of 1 GiB

@@ -64,11 +64,13 @@ def lib():
         L.oracle_det_decode.argtypes = [P, C.c_int, P, P, P, P, C.c_int, C.c_int, C.c_int,
                                         C.c_int, P, C.c_int]
         L.oracle_add_rmsnorm.argtypes = [P, P, P, P, P, i64, i64, C.c_float, C.c_int, C.c_int, P]
+        L.oracle_add_layernorm.argtypes = [P, P, P, P, P, P, i64, i64, C.c_float, C.c_int,
+                                           C.c_int, P]
         L.oracle_qkv_rope.argtypes = [P, P, P, P, i64, C.c_int, C.c_int, P, C.c_float,
                                       C.c_float, C.c_int, C.c_int, P, P, P, P]
         L.oracle_rope_inv_freq.argtypes = [C.c_float, C.c_int, P]
         for f in ("oracle_chain", "oracle_det_decode", "oracle_add_rmsnorm", "oracle_qkv_rope",
-                  "oracle_rope_inv_freq"):
+                  "oracle_rope_inv_freq", "oracle_add_layernorm"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -190,6 +192,21 @@ def add_rmsnorm(x, r, w, eps: float, dt: int, eager: bool = False, want_exact: b
     rc = lib().oracle_add_rmsnorm(_p(x), _p(rr), _p(ww), _p(h), _p(out), rows, cols, eps, dt,
                                   int(eager), _p(exact))
     _check(rc, "oracle_add_rmsnorm")
+    return (h, out, exact) if want_exact else (h, out)
+
+
+def add_layernorm(x, r, gamma, beta, eps: float, dt: int, eager: bool = False,
+                  want_exact: bool = False):
+    """Residual-add + LayerNorm over rows of x [rows, cols]; returns (h, out[, exact])."""
+    x = _raw(x)
+    rows, cols = x.shape
+    rr, gg, bb = (None if a is None else _raw(a) for a in (r, gamma, beta))
+    h = np.empty((rows, cols), _NP[dt])
+    out = np.empty((rows, cols), _NP[dt])
+    exact = np.empty((rows, cols), np.float64) if want_exact else None
+    rc = lib().oracle_add_layernorm(_p(x), _p(rr), _p(gg), _p(bb), _p(h), _p(out), rows, cols,
+                                    eps, dt, int(eager), _p(exact))
+    _check(rc, "oracle_add_layernorm")
     return (h, out, exact) if want_exact else (h, out)
 
 

@@ -322,6 +322,61 @@ int oracle_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out,
   return 0;
 }
 
+int oracle_add_layernorm(const void* x, const void* r, const void* gamma, const void* beta,
+                         void* h_out, void* out, int64_t rows, int64_t cols, float eps, int dt,
+                         int eager, double* exact) {
+  if (!x || !out || rows < 0 || cols <= 0 || !valid_dt(dt)) return -1;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return -1;
+  const Fmt& f = fmt_of(dt);
+  std::vector<double> h((size_t)cols);
+  for (int64_t i = 0; i < rows; ++i) {
+    const int64_t base = i * cols;
+    for (int64_t j = 0; j < cols; ++j) {
+      double s = load(x, dt, base + j) + (r ? load(r, dt, base + j) : 0.0);
+      h[j] = round_to(s, f);  // the stored residual sum is what the norm sees
+      if (h_out) store(h_out, dt, base + j, h[j]);
+    }
+    if (!eager) {
+      long double sum = 0.0L;
+      for (int64_t j = 0; j < cols; ++j) sum += (long double)h[j];
+      const long double mu = sum / (long double)cols;
+      long double sq = 0.0L;
+      for (int64_t j = 0; j < cols; ++j) {
+        const long double d = (long double)h[j] - mu;
+        sq += d * d;
+      }
+      const long double rstd = 1.0L / std::sqrt(sq / (long double)cols + (long double)eps);
+      for (int64_t j = 0; j < cols; ++j) {
+        const long double g = gamma ? (long double)load(gamma, dt, j) : 1.0L;
+        const long double b = beta ? (long double)load(beta, dt, j) : 0.0L;
+        const double e = (double)(((long double)h[j] - mu) * rstd * g + b);
+        if (exact) exact[base + j] = e;
+        store(out, dt, base + j, round_to(e, f));
+      }
+    } else {
+      long double sum = 0.0L;
+      for (int64_t j = 0; j < cols; ++j) sum += (long double)h[j];
+      const double mu = round_to((double)(sum / (long double)cols), f);
+      std::vector<double> d((size_t)cols);
+      long double sq = 0.0L;
+      for (int64_t j = 0; j < cols; ++j) {
+        d[j] = round_to(h[j] - mu, f);
+        sq += (long double)round_to(d[j] * d[j], f);
+      }
+      const double var = round_to((double)(sq / (long double)cols), f);
+      const double rs = round_to((double)(1.0L / std::sqrt((long double)var + (long double)eps)), f);
+      for (int64_t j = 0; j < cols; ++j) {
+        double y = round_to(d[j] * rs, f);
+        if (gamma) y = round_to(y * load(gamma, dt, j), f);
+        const double e = beta ? y + load(beta, dt, j) : y;
+        if (exact) exact[base + j] = e;
+        store(out, dt, base + j, round_to(e, f));
+      }
+    }
+  }
+  return 0;
+}
+
 int oracle_rope_inv_freq(float base, int head_dim, float* inv) {
   if (!(base > 0.0f) || head_dim <= 0 || (head_dim & 1) || !inv) return -1;
   for (int i = 0; i < head_dim / 2; ++i)

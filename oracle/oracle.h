@@ -93,6 +93,21 @@ int oracle_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out,
                        int64_t rows, int64_t cols, float eps, int dt, int eager, double* exact);
 
 /*
+ * Residual-add + LayerNorm (DeepJIT write-up, section 4.3: one block per row,
+ * mean and variance of the row, normalise, affine gamma / beta; the runtime
+ * page "CUDA算子与AI运行时", section 4.1, states the same definition):
+ * h = x + r (stored, rounded to dt), mu = mean(h), var = mean((h - mu)^2)
+ * (population variance), out = (h - mu) / sqrt(var + eps) * gamma + beta.
+ * r / gamma / beta / h_out may be NULL (no residual, gamma 1, beta 0, h not
+ * stored). eager = 1: the nine-kernel unfused form (add; row mean; subtract
+ * the mean; square; row mean; +eps and 1/sqrt; multiply by rstd; multiply by
+ * gamma; add beta), each result stored in dt.
+ */
+int oracle_add_layernorm(const void* x, const void* r, const void* gamma, const void* beta,
+                         void* h_out, void* out, int64_t rows, int64_t cols, float eps, int dt,
+                         int eager, double* exact);
+
+/*
  * QKV split + rotate-half RoPE + Q scale (TeleTron write-up, section 3.1: the
  * QKV projection epilogue of multi-head split, rotary position encoding and
  * scaling). qkv: [T, 3, n_heads, head_dim]; q, k, v: [n_heads, T, head_dim].
