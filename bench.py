@@ -62,6 +62,14 @@ def rms_bytes(rows, cols, es=2):
     return fused, unf
 
 
+def ln_bytes(rows, cols, es=2):
+    s = rows * cols * es
+    fused = 4 * s + 2 * cols * es
+    # add 3S; mean S; subtract 2S; square 2S; mean S; rsqrt; x rstd 2S; x gamma 2S; + beta 2S
+    unf = 15 * s + 8 * rows * es + 2 * cols * es
+    return fused, unf
+
+
 def rope_bytes(T, H, D, es=2):
     q = T * H * D * es
     return 6 * q, 6 * q + 2 * q + 2 * q + 2 * q
@@ -96,6 +104,7 @@ KERNEL_SOURCES = {
     "c2": ["norm_pass_amd/csrc/det_decode.hip", "norm_pass_amd/csrc/device.h"],
     "c3": ["norm_pass_amd/csrc/add_rmsnorm.hip", "norm_pass_amd/csrc/device.h"],
     "c4": ["norm_pass_amd/csrc/qkv_rope.hip", "norm_pass_amd/csrc/device.h"],
+    "ln": ["norm_pass_amd/csrc/add_layernorm.hip", "norm_pass_amd/csrc/device.h"],
 }
 
 
@@ -256,6 +265,20 @@ def build_workloads(torch, npa, synth, quick: bool):
         unfused=npa.bind("unfused_add_rmsnorm", tx, tr, tw, h3, o3, ws3, 1e-6),
         unfused_spec=("unfused_add_rmsnorm", (tx, tr, tw, h3, o3, ws3, 1e-6)),
         bytes=fb, unfused_bytes=ub, launches=6, kernel="rms_vec")
+    # LayerNorm (the next row on the same machinery): same shape as C3, not in the step
+    gam = tdev(synth.normal((4096,), 1013, "bf16", mean=1.0, std=0.1), "bf16")
+    bet = tdev(synth.normal((4096,), 1014, "bf16", std=0.1), "bf16")
+    hl = torch.empty_like(tx)
+    ol = torch.empty_like(tx)
+    wsl = torch.empty(npa.layernorm_workspace_bytes(rows, 4096, torch.bfloat16),
+                      dtype=torch.uint8, device=dev)
+    fb, ub = ln_bytes(rows, 4096)
+    W["ln"] = dict(
+        desc=f"bf16 residual add + LayerNorm [{rows}, 4096], eps 1e-5 (not in the step)",
+        fused=npa.bind("fuse_add_layernorm", tx, tr, gam, bet, hl, ol, 1e-5),
+        unfused=npa.bind("unfused_add_layernorm", tx, tr, gam, bet, hl, ol, wsl, 1e-5),
+        unfused_spec=("unfused_add_layernorm", (tx, tr, gam, bet, hl, ol, wsl, 1e-5)),
+        bytes=fb, unfused_bytes=ub, launches=9, kernel="ln_vec")
     # C4
     T = 2048 if quick else 16384
     qkv = tdev(synth.c4_inputs(tokens=T), "bf16")
@@ -418,7 +441,8 @@ def main(argv=None):
     log(f"[bench] {args.steps} steps: {step_s * 1e6:.1f} us/step (wall {wall:.3f}s)")
 
     per = {}
-    for k in order:
+    extra = [k for k in W if k not in order]
+    for k in order + extra:
         w = W[k]
         reps = pick_reps(torch, w["fused"])
         f_med, f_p10, f_p90 = time_calls(torch, w["fused"], reps, args.trials)
@@ -465,7 +489,7 @@ def main(argv=None):
     c_med, _, _ = time_calls(torch, cp, 10, 7)
     copy_gbps = 2 * 4 * n_copy / c_med / 1e9
     del csrc, cdst
-    for k in order:
+    for k in order + extra:
         per[k]["frac_of_copy"] = round(per[k]["GBps"] / copy_gbps, 3)
     log(f"[bench] copy ceiling {copy_gbps:.0f} GB/s")
 
@@ -507,7 +531,7 @@ def main(argv=None):
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(hbm_frac, 4),
                 "traffic": measured_traffic(dom)}
     # every kernel's own roofline, for the record
-    for k in order:
+    for k in order + extra:
         per[k]["hbm_frac"] = round(per[k]["bytes"] / (per[k]["us_med"] * 1e-6) / 1e9
                                    / HBM_PEAK_GBPS, 4)
     for k in ("c5_small", "c5_large"):

@@ -184,6 +184,23 @@ int fuse_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out, v
                      int64_t rows, int64_t cols, float eps, np_dtype dt, hipStream_t stream);
 
 /*
+ * fuse_add_layernorm: residual add + LayerNorm in one pass (DeepJIT write-up,
+ * section 4.3: one block per row computing the row's mean and variance,
+ * normalising and applying gamma / beta, instead of separate mean, variance and
+ * normalise kernels; the runtime page, section 4.1, gives the same formula).
+ * Row-major contiguous [rows, cols] of dt:
+ *   h = x + r (rounded to dt, stored to h_out, and used by the norm)
+ *   mu = mean_j(h_j), var = mean_j((h_j - mu)^2)  (population variance,
+ *   computed as a second pass over the row, not as E[h^2] - mu^2)
+ *   out = (h - mu) / sqrt(var + eps) * gamma_j + beta_j
+ * r == NULL: h = x. gamma == NULL: 1. beta == NULL: 0. h_out == NULL: not stored.
+ * Errors as fuse_add_rmsnorm.
+ */
+int fuse_add_layernorm(const void* x, const void* r, const void* gamma, const void* beta,
+                       void* h_out, void* out, int64_t rows, int64_t cols, float eps, np_dtype dt,
+                       hipStream_t stream);
+
+/*
  * fuse_qkv_rope: QKV split + rotate-half RoPE + Q scale in one pass (TeleTron
  * write-up, section 3.1: the multi-head split, rotary position encoding and
  * scaling after the QKV projection). qkv: [T, 3, n_heads, head_dim] row-major
@@ -228,6 +245,15 @@ int unfused_det_decode(const void* const* level_logits, int n_levels, const int3
 int unfused_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out, void* out,
                         int64_t rows, int64_t cols, float eps, np_dtype dt, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/* 9 launches: add; row mean; subtract the mean; square; row mean; (+eps,
+ * 1/sqrt); times rstd; times gamma; plus beta (gamma / beta launches skipped
+ * when NULL). workspace: at least (rows * cols + 3 * rows) * sizeof(dt) bytes,
+ * plus rows * cols * sizeof(dt) when h_out == NULL. */
+int unfused_add_layernorm(const void* x, const void* r, const void* gamma, const void* beta,
+                          void* h_out, void* out, int64_t rows, int64_t cols, float eps,
+                          np_dtype dt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* 4 launches: split to head-major; RoPE on Q; RoPE on K; scale Q. */
 int unfused_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n_heads,

@@ -56,6 +56,8 @@ def _load():
         "fuse_det_decode": [P, I, P, P, P, P, I, I, I, I, P, P],
         "fuse_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I, P],
         "fuse_qkv_rope": [P, P, P, P, I64, I, I, P, F, F, I, P],
+        "fuse_add_layernorm": [P, P, P, P, P, P, I64, I64, F, I, P],
+        "unfused_add_layernorm": [P, P, P, P, P, P, I64, I64, F, I, P, S, P],
         "unfused_chain": [OPS, I, P, I, I, P, I, I64, P],
         "unfused_det_decode": [P, I, P, P, P, P, I, I, I, I, P, P, S, P],
         "unfused_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I, P, S, P],
@@ -203,6 +205,19 @@ def _a_fuse_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
             _ptr(positions), base, q_scale, dtype_code(qkv), _stream(stream))
 
 
+def _a_fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps: float = 1e-5, stream=None):
+    _keep(stream, x, r, gamma, beta, h_out, out)
+    return (_ptr(x), _ptr(r), _ptr(gamma), _ptr(beta), _ptr(h_out), _ptr(out), x.shape[0],
+            x.shape[-1], eps, dtype_code(x), _stream(stream))
+
+
+def _a_unfused_add_layernorm(x, r, gamma, beta, h_out, out, workspace, eps: float = 1e-5,
+                             stream=None):
+    a = _a_fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps, stream)
+    _keep(stream, workspace)
+    return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
+
+
 _a_unfused_chain = _a_fuse_chain
 _a_unfused_qkv_rope = _a_fuse_qkv_rope
 
@@ -222,7 +237,11 @@ def _a_unfused_add_rmsnorm(x, r, w, h_out, out, workspace, eps: float = 1e-6, st
 
 def bind(name: str, *args, **kw):
     """Marshal the arguments of call `name` once; return a zero-argument callable
-    that performs the C call (and raises NPError on failure) each time."""
+    that performs the C call (and raises NPError on failure) each time.
+
+    The callable holds references to every tensor argument (and to the ctypes
+    objects built from them): the marshalled pointers stay valid for as long as
+    the callable exists, whatever happens to the caller's own names."""
     a = globals()["_a_" + name](*args, **kw)
     f = getattr(_lib, name)
 
@@ -230,7 +249,8 @@ def bind(name: str, *args, **kw):
         rc = f(*a)
         if rc:
             _check(rc, name)
-    call.args = a  # keeps the ctypes objects alive
+    call.args = a
+    call.keep = (args, kw)
     return call
 
 
@@ -265,6 +285,12 @@ def fuse_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
     _check(_lib.fuse_qkv_rope(*_a_fuse_qkv_rope(qkv, q, k, v, n_heads, head_dim, positions, base,
                                                 q_scale, stream)), "fuse_qkv_rope")
     return q, k, v
+
+
+def fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps: float = 1e-5, stream=None):
+    _check(_lib.fuse_add_layernorm(*_a_fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps,
+                                                          stream)), "fuse_add_layernorm")
+    return h_out, out
 
 
 # ------------------------------------------------------- unfused baselines
@@ -302,3 +328,16 @@ def unfused_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
     _check(_lib.unfused_qkv_rope(*_a_unfused_qkv_rope(qkv, q, k, v, n_heads, head_dim, positions,
                                                       base, q_scale, stream)), "unfused_qkv_rope")
     return q, k, v
+
+
+def layernorm_workspace_bytes(rows: int, cols: int, dtype, with_h: bool = True) -> int:
+    es = _SIZE[dtype_code(dtype)]
+    return (rows * cols + 3 * rows + (0 if with_h else rows * cols)) * es
+
+
+def unfused_add_layernorm(x, r, gamma, beta, h_out, out, workspace, eps: float = 1e-5,
+                          stream=None):
+    _check(_lib.unfused_add_layernorm(*_a_unfused_add_layernorm(x, r, gamma, beta, h_out, out,
+                                                                workspace, eps, stream)),
+           "unfused_add_layernorm")
+    return h_out, out

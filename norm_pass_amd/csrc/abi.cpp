@@ -290,6 +290,22 @@ int fuse_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out, v
   return ok();
 }
 
+int fuse_add_layernorm(const void* x, const void* r, const void* gamma, const void* beta,
+                       void* h_out, void* out, int64_t rows, int64_t cols, float eps, np_dtype dt,
+                       hipStream_t stream) {
+  int rc = validate_norm(x, out, h_out, rows, cols, eps, dt);
+  if (rc) return rc;
+  if (rows == 0) return ok();
+  if ((rc = check_device())) return rc;
+  const bool vec = aligned16(x) && aligned16(out) && (!r || aligned16(r)) &&
+                   (!gamma || aligned16(gamma)) && (!beta || aligned16(beta)) &&
+                   (!h_out || aligned16(h_out));
+  hipError_t e =
+      np::launch_add_layernorm(x, r, gamma, beta, h_out, out, rows, cols, eps, dt, vec, stream);
+  if (e != hipSuccess) return hip_fail(e, "fuse_add_layernorm");
+  return ok();
+}
+
 int fuse_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n_heads,
                   int head_dim, const int32_t* positions, float base, float q_scale,
                   np_dtype dt, hipStream_t stream) {
@@ -409,6 +425,41 @@ int unfused_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out
   if (e == hipSuccess) e = np::launch_row_scale(h, rs, out, rows, cols, dt, stream);
   if (e == hipSuccess && w) e = np::launch_col_scale(out, w, out, rows, cols, dt, stream);
   if (e != hipSuccess) return hip_fail(e, "unfused_add_rmsnorm");
+  return ok();
+}
+
+int unfused_add_layernorm(const void* x, const void* r, const void* gamma, const void* beta,
+                          void* h_out, void* out, int64_t rows, int64_t cols, float eps,
+                          np_dtype dt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  int rc = validate_norm(x, out, h_out, rows, cols, eps, dt);
+  if (rc) return rc;
+  const int64_t es = np::dt_size(dt);
+  const int64_t need = (rows * cols + 3 * rows + (h_out ? 0 : rows * cols)) * es;
+  if (rows == 0) return ok();
+  if (!workspace || (int64_t)workspace_bytes < need)
+    return fail(NP_EINVAL, "workspace needs %lld bytes", (long long)need);
+  if ((rc = check_device())) return rc;
+  char* ws = static_cast<char*>(workspace);
+  const int64_t n = rows * cols;
+  void* d = ws;                              // h - mean
+  void* mu = ws + n * es;                    // [rows] mean
+  void* var = ws + (n + rows) * es;          // [rows] variance
+  void* rs = ws + (n + 2 * rows) * es;       // [rows] 1/sqrt(var + eps)
+  void* h = h_out ? h_out : ws + (n + 3 * rows) * es;
+  // add; row mean; subtract; square (into out, overwritten later); row mean;
+  // +eps and 1/sqrt; times rstd; times gamma; plus beta
+  hipError_t e = r ? np::launch_binary(NP_ADD_IN, x, r, h, n, dt, stream)
+                   : np::launch_unary(np::U_COPY, 0.0f, x, h, n, dt, stream);
+  if (e == hipSuccess) e = np::launch_row_mean(h, mu, rows, cols, dt, stream);
+  if (e == hipSuccess) e = np::launch_row_sub(h, mu, d, rows, cols, dt, stream);
+  if (e == hipSuccess) e = np::launch_unary(np::U_SQUARE, 0.0f, d, out, n, dt, stream);
+  if (e == hipSuccess) e = np::launch_row_mean(out, var, rows, cols, dt, stream);
+  if (e == hipSuccess) e = np::launch_unary(np::U_RSQRT_EPS, eps, var, rs, rows, dt, stream);
+  if (e == hipSuccess) e = np::launch_row_scale(d, rs, out, rows, cols, dt, stream);
+  if (e == hipSuccess && gamma) e = np::launch_col_scale(out, gamma, out, rows, cols, dt, stream);
+  if (e == hipSuccess && beta) e = np::launch_col_add(out, beta, out, rows, cols, dt, stream);
+  if (e != hipSuccess) return hip_fail(e, "unfused_add_layernorm");
   return ok();
 }
 

@@ -17,18 +17,6 @@
 namespace np {
 namespace {
 
-template <int WAVES>
-__device__ __forceinline__ float block_sum(float v, float* part) {
-  v = wave_sum(v);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) part[wave] = v;
-  __syncthreads();
-  float tot = 0.0f;
-#pragma unroll
-  for (int i = 0; i < WAVES; ++i) tot += part[i];
-  return tot;
-}
-
 template <typename T, int VPT, int WAVES, bool HAS_R, bool HAS_W, bool HAS_H>
 __global__ __launch_bounds__(64 * WAVES) void rms_vec(const T* x, const T* r, const T* w, T* h,
                                                       T* out, int cols, float eps) {

@@ -102,6 +102,21 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Sum over a workgroup of WAVES waves: wave_sum, one LDS slot per wave, then
+// every thread adds the WAVES partials in a fixed order (deterministic). `part`
+// must hold WAVES floats and must not be reused by a later call in the same
+// kernel without a barrier; uniform control flow only.
+template <int WAVES>
+__device__ __forceinline__ float block_sum(float v, float* part) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < WAVES; ++i) tot += part[i];
+  return tot;
+}
+
 // Logistic sigmoid with the device library's accurate expf and an IEEE divide.
 __device__ __forceinline__ float sigmoid_f(float t) { return 1.0f / (1.0f + expf(-t)); }
 

@@ -46,6 +46,11 @@ hipError_t launch_add_rmsnorm(const void* x, const void* r, const void* w, void*
                               int64_t rows, int64_t cols, float eps, int dt, bool vec,
                               hipStream_t s);
 
+// residual add + LayerNorm
+hipError_t launch_add_layernorm(const void* x, const void* r, const void* g, const void* b,
+                                void* h, void* out, int64_t rows, int64_t cols, float eps, int dt,
+                                bool vec, hipStream_t s);
+
 // QKV split + RoPE + scale
 struct RopeArgs {
   const void* qkv;
@@ -72,6 +77,10 @@ hipError_t launch_row_scale(const void* in, const void* rs, void* out, int64_t r
                             int64_t cols, int dt, hipStream_t s);
 hipError_t launch_col_scale(const void* in, const void* w, void* out, int64_t rows,
                             int64_t cols, int dt, hipStream_t s);
+hipError_t launch_row_sub(const void* in, const void* m, void* out, int64_t rows, int64_t cols,
+                          int dt, hipStream_t s);
+hipError_t launch_col_add(const void* in, const void* b, void* out, int64_t rows, int64_t cols,
+                          int dt, hipStream_t s);
 hipError_t launch_qkv_split(const void* qkv, void* q, void* k, void* v, int64_t T, int H, int D,
                             int dt, hipStream_t s);
 hipError_t launch_rope_inplace(void* x, int64_t T, int H, int D, const int32_t* pos,

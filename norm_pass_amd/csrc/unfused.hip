@@ -101,10 +101,18 @@ __global__ __launch_bounds__(kBlock) void row_mean_kernel(const T* in, T* out, i
   }
 }
 
-// out[i, j] = in[i, j] * s[i]  (ROW = true)   or   in[i, j] * s[j]  (ROW = false)
-template <typename T, bool ROW>
-__global__ __launch_bounds__(kBlock) void bcast_mul_kernel(const T* in, const T* s, T* out,
-                                                           int64_t rows, int64_t cols, bool vec) {
+// out[i, j] = in[i, j] (op) s[i]  (ROW = true)   or   in[i, j] (op) s[j]  (ROW = false),
+// op = multiply / add / subtract
+enum BcastOp { B_MUL = 0, B_ADD = 1, B_SUB = 2 };
+
+template <int OP>
+__device__ __forceinline__ float bop(float a, float b) {
+  return OP == B_MUL ? a * b : OP == B_ADD ? a + b : a - b;
+}
+
+template <typename T, bool ROW, int OP>
+__global__ __launch_bounds__(kBlock) void bcast_kernel(const T* in, const T* s, T* out,
+                                                       int64_t rows, int64_t cols, bool vec) {
   constexpr int N = Vec<T>::N;
   const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (vec) {  // cols % N == 0
@@ -118,19 +126,19 @@ __global__ __launch_bounds__(kBlock) void bcast_mul_kernel(const T* in, const T*
     if (ROW) {
       const float f = to_f(s[i]);
 #pragma unroll
-      for (int e = 0; e < N; ++e) v[e] *= f;
+      for (int e = 0; e < N; ++e) v[e] = bop<OP>(v[e], f);
     } else {
       float w[N];
       load_vec<T>(s + j, w);
 #pragma unroll
-      for (int e = 0; e < N; ++e) v[e] *= w[e];
+      for (int e = 0; e < N; ++e) v[e] = bop<OP>(v[e], w[e]);
     }
     store_vec_nt<T>(out + e0, v);
   } else {
     if (gid >= rows * cols) return;
     const int64_t i = gid / cols;
     const int64_t j = gid - i * cols;
-    out[gid] = from_f<T>(to_f(in[gid]) * to_f(s[ROW ? i : j]));
+    out[gid] = from_f<T>(bop<OP>(to_f(in[gid]), to_f(s[ROW ? i : j])));
   }
 }
 
@@ -321,7 +329,7 @@ hipError_t launch_row_mean(const void* in, void* out, int64_t rows, int64_t cols
   });
 }
 
-template <bool ROW>
+template <bool ROW, int OP>
 hipError_t bcast(const void* in, const void* sc, void* out, int64_t rows, int64_t cols, int dt,
                  hipStream_t s) {
   return by_dt(dt, [&](auto tag) {
@@ -329,7 +337,7 @@ hipError_t bcast(const void* in, const void* sc, void* out, int64_t rows, int64_
     const bool vec = aligned16(in) && aligned16(out) && cols % Vec<T>::N == 0 &&
                      (ROW || aligned16(sc));
     const int64_t work = vec ? rows * cols / Vec<T>::N : rows * cols;
-    hipLaunchKernelGGL((bcast_mul_kernel<T, ROW>), dim3((unsigned)blocks_for(work)),
+    hipLaunchKernelGGL((bcast_kernel<T, ROW, OP>), dim3((unsigned)blocks_for(work)),
                        dim3(kBlock), 0, s, static_cast<const T*>(in),
                        static_cast<const T*>(sc), static_cast<T*>(out), rows, cols, vec);
     return hipGetLastError();
@@ -338,12 +346,22 @@ hipError_t bcast(const void* in, const void* sc, void* out, int64_t rows, int64_
 
 hipError_t launch_row_scale(const void* in, const void* rs, void* out, int64_t rows,
                             int64_t cols, int dt, hipStream_t s) {
-  return bcast<true>(in, rs, out, rows, cols, dt, s);
+  return bcast<true, B_MUL>(in, rs, out, rows, cols, dt, s);
 }
 
 hipError_t launch_col_scale(const void* in, const void* w, void* out, int64_t rows,
                             int64_t cols, int dt, hipStream_t s) {
-  return bcast<false>(in, w, out, rows, cols, dt, s);
+  return bcast<false, B_MUL>(in, w, out, rows, cols, dt, s);
+}
+
+hipError_t launch_row_sub(const void* in, const void* m, void* out, int64_t rows, int64_t cols,
+                          int dt, hipStream_t s) {
+  return bcast<true, B_SUB>(in, m, out, rows, cols, dt, s);
+}
+
+hipError_t launch_col_add(const void* in, const void* b, void* out, int64_t rows, int64_t cols,
+                          int dt, hipStream_t s) {
+  return bcast<false, B_ADD>(in, b, out, rows, cols, dt, s);
 }
 
 hipError_t launch_qkv_split(const void* qkv, void* q, void* k, void* v, int64_t T_, int H, int D,

@@ -25,12 +25,13 @@ def npa():
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "norm_pass.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|void|const char\*)\s+(\w+)\s*\(", src,
+                                 flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol(npa):
     names = declared_functions()
-    assert len(names) >= 15
+    assert len(names) >= 18 and "np_chain_source" in names
     for n in names:
         assert hasattr(npa.lib(), n), n
 
@@ -167,3 +168,11 @@ def test_runtime_specialisation_compiles(npa):
     assert b1 > 0 and b2 > 0 and ms1 > 0 and ms2 > 0
     with pytest.raises(npa.NPError):
         npa.np_chain_compile([(synth.LOAD, 0, 0), (77, 0, 0)], 1, 0, 0, 0)
+
+
+def test_add_layernorm_rejects(npa):
+    p = [C.c_void_p(0x1000), None, None, None, None, C.c_void_p(0x2000)]
+    assert npa.lib().fuse_add_layernorm(*p, 4, 8, 0.0, 2, NULL) == -1
+    assert "eps" in _err(npa)
+    assert npa.lib().unfused_add_layernorm(*p, 4, 8, 1e-5, 2, NULL, 0, NULL) == -1
+    assert "workspace" in _err(npa)

@@ -74,3 +74,23 @@ def test_graph_unfused_det_decode(npa):
     ref = out.clone()
     _replays_match(lambda: npa.unfused_det_decode(lv, [8.0, 16.0], an, out, ws), out, ref,
                    lambda: None)
+
+
+def test_bind_keeps_its_tensors_alive(npa):
+    """bind() marshals device pointers once; the tensors behind them must live as
+    long as the returned callable (no launch here: only the references)."""
+    import gc
+    import weakref
+
+    def make():
+        x = torch.zeros(1 << 10, dtype=torch.float16, device="cuda")
+        y = torch.empty_like(x)
+        return npa.bind("fuse_chain", [(synth.LOAD, 0, 0.0)], [x], y), weakref.ref(x), \
+            weakref.ref(y)
+
+    call, wx, wy = make()
+    gc.collect()
+    assert wx() is not None and wy() is not None
+    del call
+    gc.collect()
+    assert wx() is None and wy() is None
