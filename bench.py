@@ -75,11 +75,11 @@ def rope_bytes(T, H, D, es=2):
     return 6 * q, 6 * q + 2 * q + 2 * q + 2 * q
 
 
-# VALU issue slots per element of one chain op, as compiled for gfx950 by the
-# fp16-output fast path (full-rate VALU instruction = 1 slot, v_exp_f32 and
-# v_rcp_f32 = 2 slots, measured): the algorithmic work of an ALU-bound chain.
-VALU_SLOTS = {0: 1, 1: 2, 2: 2, 3: 1, 4: 1, 5: 1, 6: 1, 7: 10, 8: 8, 9: 16, 10: 2, 11: 2}
-VALU_PEAK = 256 * 64 * 2.4e9  # lane-slots/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+# VALU instructions per element of one chain op in the fp16-output specialised
+# kernel (static count of its gfx950 code, one side of tanh's branch): the
+# fallback when no rocprofv3 SQ_INSTS_VALU count for the current sources exists.
+VALU_SLOTS = {0: 1, 1: 2, 2: 2, 3: 1, 4: 1, 5: 1, 6: 1, 7: 8, 8: 7, 9: 10, 10: 2, 11: 2}
+VALU_PEAK = 256 * 64 * 2.4e9  # lane-instr/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
 
 
 def chain_slots(ops) -> int:
@@ -409,7 +409,7 @@ def main(argv=None):
         for name, w in W.items():
             if only and name not in only:
                 continue
-            for _ in range(5):
+            for _ in range(20):  # warm clocks: rocprofv3 averages every dispatch
                 w["fused"]()
             for _ in range(2):
                 w["unfused"]()
