@@ -69,8 +69,11 @@ def lib():
         L.oracle_qkv_rope.argtypes = [P, P, P, P, i64, C.c_int, C.c_int, P, C.c_float,
                                       C.c_float, C.c_int, C.c_int, P, P, P, P]
         L.oracle_rope_inv_freq.argtypes = [C.c_float, C.c_int, P]
+        L.oracle_channel_shuffle.argtypes = [P, P, i64, i64, i64, i64, i64, C.c_int, C.c_int]
+        L.oracle_transpose021.argtypes = [P, P, i64, i64, i64, i64, C.c_int]
         for f in ("oracle_chain", "oracle_det_decode", "oracle_add_rmsnorm", "oracle_qkv_rope",
-                  "oracle_rope_inv_freq", "oracle_add_layernorm"):
+                  "oracle_rope_inv_freq", "oracle_add_layernorm", "oracle_channel_shuffle",
+                  "oracle_transpose021"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -231,3 +234,39 @@ def qkv_rope(qkv, n_heads: int, head_dim: int, base: float, q_scale: float, dt: 
                                base, q_scale, dt, int(eager), *[_p(e) for e in extra])
     _check(rc, "oracle_qkv_rope")
     return (q, k, v, *extra) if want_bound else (q, k, v)
+
+
+# --------------------------------------------------------------------------
+# layout: ChannelShuffle and the batched transpose behind it
+# --------------------------------------------------------------------------
+
+def _bytes_view(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a)
+
+
+def channel_shuffle(x: np.ndarray, groups: int, layout: int = 0) -> np.ndarray:
+    """ChannelShuffle of a 4-D array (NCHW for layout 0, NHWC for layout 1),
+    bit for bit in x's dtype (see oracle.h)."""
+    x = _bytes_view(x)
+    if x.ndim != 4:
+        raise ValueError("channel_shuffle: x must be 4-D")
+    if layout == 0:
+        N, Cc, H, W = x.shape
+    else:
+        N, H, W, Cc = x.shape
+    out = np.empty_like(x)
+    _check(lib().oracle_channel_shuffle(_p(x), _p(out), N, Cc, H, W, groups, layout,
+                                        x.dtype.itemsize), "channel_shuffle")
+    return out
+
+
+def transpose021(x: np.ndarray) -> np.ndarray:
+    """[B, R, S, E] -> [B, S, R, E], bit for bit (see oracle.h)."""
+    x = _bytes_view(x)
+    if x.ndim != 4:
+        raise ValueError("transpose021: x must be 4-D [B, R, S, E]")
+    B, R, S, E = x.shape
+    out = np.empty((B, S, R, E), x.dtype)
+    _check(lib().oracle_transpose021(_p(x), _p(out), B, R, S, E, x.dtype.itemsize),
+           "transpose021")
+    return out

@@ -454,3 +454,52 @@ int oracle_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n
 }
 
 }  // extern "C"
+
+int oracle_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64_t H,
+                           int64_t W, int64_t groups, int layout, int elem_bytes) {
+  if (!in || !out || N < 0 || C < 0 || H < 0 || W < 0 || groups <= 0 || elem_bytes < 1 ||
+      elem_bytes > 16 || (layout != 0 && layout != 1))
+    return -1;
+  if (C % groups != 0) return -1;
+  const int64_t per = C / groups;  // channels per group
+  const unsigned char* src = static_cast<const unsigned char*>(in);
+  unsigned char* dst = static_cast<unsigned char*>(out);
+  const size_t es = (size_t)elem_bytes;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t g = 0; g < groups; ++g)
+      for (int64_t i = 0; i < per; ++i) {
+        const int64_t c_in = g * per + i;
+        const int64_t c_out = i * groups + g;
+        for (int64_t y = 0; y < H; ++y)
+          for (int64_t x = 0; x < W; ++x) {
+            int64_t a, b;  // element offsets of (n, c, y, x) in the input and output
+            if (layout == 0) {
+              a = ((n * C + c_in) * H + y) * W + x;
+              b = ((n * C + c_out) * H + y) * W + x;
+            } else {
+              a = ((n * H + y) * W + x) * C + c_in;
+              b = ((n * H + y) * W + x) * C + c_out;
+            }
+            std::memcpy(dst + (size_t)b * es, src + (size_t)a * es, es);
+          }
+      }
+  return 0;
+}
+
+int oracle_transpose021(const void* in, void* out, int64_t B, int64_t R, int64_t S, int64_t E,
+                        int elem_bytes) {
+  if (!in || !out || B < 0 || R < 0 || S < 0 || E < 0 || elem_bytes < 1 || elem_bytes > 16)
+    return -1;
+  const unsigned char* src = static_cast<const unsigned char*>(in);
+  unsigned char* dst = static_cast<unsigned char*>(out);
+  const size_t es = (size_t)elem_bytes;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t r = 0; r < R; ++r)
+      for (int64_t s = 0; s < S; ++s)
+        for (int64_t e = 0; e < E; ++e) {
+          const int64_t a = ((b * R + r) * S + s) * E + e;
+          const int64_t o = ((b * S + s) * R + r) * E + e;
+          std::memcpy(dst + (size_t)o * es, src + (size_t)a * es, es);
+        }
+  return 0;
+}

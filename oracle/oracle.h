@@ -125,6 +125,26 @@ int oracle_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n
 /* fp32 inverse-frequency table inv_i = fp32(base^(-2i/head_dim)), i < head_dim/2 */
 int oracle_rope_inv_freq(float base, int head_dim, float* inv);
 
+/*
+ * ChannelShuffle (runtime page "CUDA算子与AI运行时", gtnt.cn/news/145880,
+ * section 2: the channels of an [N, C, H, W] tensor viewed as [groups,
+ * C/groups], the two axes swapped, viewed back as C channels). Output channel
+ * i*groups + g holds input channel g*(C/groups) + i, for g < groups,
+ * i < C/groups. layout 0 = NCHW, 1 = NHWC ([N, H, W, C], the same channel
+ * permutation applied to each pixel). Elements are elem_bytes (1..16) bytes,
+ * copied bit for bit. Returns -1 unless groups divides C.
+ */
+int oracle_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64_t H,
+                           int64_t W, int64_t groups, int layout, int elem_bytes);
+
+/*
+ * Batched transpose of the middle two axes (the strided transpose the same
+ * section describes): in [B, R, S, E] -> out [B, S, R, E], i.e.
+ * out[b][s][r][e] = in[b][r][s][e], elements of elem_bytes (1..16) bytes.
+ */
+int oracle_transpose021(const void* in, void* out, int64_t B, int64_t R, int64_t S, int64_t E,
+                        int elem_bytes);
+
 #ifdef __cplusplus
 }
 #endif
