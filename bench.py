@@ -105,6 +105,9 @@ KERNEL_SOURCES = {
     "c3": ["norm_pass_amd/csrc/add_rmsnorm.hip", "norm_pass_amd/csrc/device.h"],
     "c4": ["norm_pass_amd/csrc/qkv_rope.hip", "norm_pass_amd/csrc/device.h"],
     "ln": ["norm_pass_amd/csrc/add_layernorm.hip", "norm_pass_amd/csrc/device.h"],
+    "tr": ["norm_pass_amd/csrc/layout.hip", "norm_pass_amd/csrc/device.h"],
+    "shuffle_nchw": ["norm_pass_amd/csrc/layout.hip", "norm_pass_amd/csrc/device.h"],
+    "shuffle_nhwc": ["norm_pass_amd/csrc/layout.hip", "norm_pass_amd/csrc/device.h"],
 }
 
 
@@ -311,6 +314,53 @@ def build_workloads(torch, npa, synth, quick: bool):
             unfused=npa.bind("unfused_chain", ops, [xin], yo),
             unfused_spec=("unfused_chain", (ops, [xin], yo)),
             bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29, kernel="chain_vec<_Float16")
+    # Layout (the runtime page's strided transpose / ChannelShuffle; not in the
+    # step): the LDS-staged kernels against the naive strided copy, and torch's
+    # own permute().contiguous() for context. Three buffer sets each for the
+    # cold figure.
+    def layout(name, desc, x_np, dt, shape, fused_name, naive_name, extra_args, torch_fn,
+               kernel):
+        x = tdev(x_np, dt)
+        sets = [(x, torch.empty_like(x))]
+        for _ in range(2):
+            y = torch.empty_like(x)
+            y.copy_(x)
+            sets.append((y, torch.empty_like(x)))
+        xo = sets[0][1]
+        nbytes = x.numel() * x.element_size()
+        W[name] = dict(
+            cold=[npa.bind(fused_name, a_, b_, *extra_args) for a_, b_ in sets],
+            desc=desc,
+            fused=npa.bind(fused_name, x, xo, *extra_args),
+            unfused=npa.bind(naive_name, x, xo, *extra_args),
+            unfused_spec=(naive_name, (x, xo) + tuple(extra_args)),
+            torch=lambda: torch_fn(x), bytes=2 * nbytes, unfused_bytes=2 * nbytes,
+            launches=1, kernel=kernel,
+            plan=npa.np_transpose_plan(x.data_ptr(), xo.data_ptr(), shape, x.element_size()))
+
+    B_, R_, S_, E_ = synth.TRANSPOSE_2D
+    if quick:
+        B_, R_, S_, E_ = 1, 2048, 2048, 1
+    layout("tr", f"fp32 [{R_}, {S_}] transpose (not in the step; baseline: naive strided copy)",
+           synth.transpose_inputs((B_, R_, S_, E_)), "f32", (B_, R_, S_, E_),
+           "fuse_transpose021", "naive_transpose021", (),
+           lambda t: t.transpose(1, 2).contiguous(), "tr_tile<4, true>")
+    N_, C_, H_, Wd = synth.SHUFFLE_NCHW
+    if quick:
+        N_ = 64
+    g = synth.SHUFFLE_GROUPS
+    for lay, nm in ((0, "shuffle_nchw"), (1, "shuffle_nhwc")):
+        xs = synth.shuffle_inputs((N_, C_, H_, Wd), layout=lay)
+        if lay == 0:
+            shp = (N_, g, C_ // g, H_ * Wd)
+            tf = (lambda t: t.view(N_, g, C_ // g, H_, Wd).transpose(1, 2).contiguous())
+        else:
+            shp = (N_ * H_ * Wd, g, C_ // g, 1)
+            tf = (lambda t: t.view(N_, H_, Wd, g, C_ // g).transpose(3, 4).contiguous())
+        layout(nm, f"fp16 ChannelShuffle {nm[8:].upper()} [{N_}, {C_}, {H_}, {Wd}], groups {g} "
+                   "(not in the step; baseline: naive strided copy)",
+               xs, "f16", shp, "fuse_channel_shuffle", "naive_channel_shuffle", (g, lay), tf,
+               "tr_items<16>" if lay == 0 else "tr_small<2, true>")
     W["_compile_ms"] = compile_ms
     return W
 
@@ -476,6 +526,10 @@ def main(argv=None):
         }
         if cold:
             per[k]["cold"] = cold
+        if "torch" in w:
+            t_med, _, _ = time_calls(torch, w["torch"], reps, max(5, args.trials // 2))
+            per[k]["torch_us_med"] = round(t_med * 1e6, 3)
+            per[k]["plan"] = w["plan"]
         log(f"[bench] {k}: fused {f_med * 1e6:.2f} us ({gbps:.0f} GB/s), "
             f"unfused {u_med * 1e6:.2f} us x{w['launches']} launches "
             f"(graph {g_med * 1e6:.2f} us)"

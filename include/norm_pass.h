@@ -264,6 +264,72 @@ int unfused_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int 
  * the per-launch cost, the NaiveRT write-up's "29 empty calls"). */
 int np_empty_launches(int count, hipStream_t stream);
 
+/* ---- layout: strided transpose and ChannelShuffle --------------------------
+ *
+ * The runtime page "CUDA算子与AI运行时" (gtnt.cn/news/145880), sections 2 and
+ * 2.1: ChannelShuffle is a reshape + transpose; done as an element-by-element
+ * strided copy one side of every access is scattered, and the operator should
+ * instead stage tiles on chip so that reads and writes are both contiguous.
+ * All four calls copy bits (any element type of elem_bytes = 1..16 bytes),
+ * so results are exact. Buffers are device memory owned by the caller, dense
+ * row-major; in and out must not overlap (NP_EINVAL). Any alignment works:
+ * misaligned pointers or pitches take narrower items, never an error.
+ */
+typedef enum { NP_NCHW = 0, NP_NHWC = 1 } np_layout;
+
+/*
+ * fuse_transpose021: in [B, R, S, E] -> out [B, S, R, E],
+ * out[b][s][r][e] = in[b][r][s][e]. The E elements of one (r, s) pair (a unit
+ * of E * elem_bytes bytes) move together. Kernel choice (host side, from the
+ * shape and alignment): units of 1/2/4/8/16 bytes in matrices larger than
+ * 16 KB go through LDS tiles of 256-byte rows; matrices of <= 16 KB move as
+ * whole chunks through LDS; larger units are copied unit by unit in output
+ * order. Limits: R, S, E < 2^31, B < 2^40, total <= 2^46 bytes; when neither
+ * LDS kernel applies, one [R, S] matrix must hold < 2^31 items.
+ * Errors: NP_EINVAL for negative sizes, elem_bytes outside 1..16, NULL or
+ * overlapping buffers (unless the tensor is empty); nothing is launched then.
+ */
+int fuse_transpose021(const void* in, void* out, int64_t B, int64_t R, int64_t S, int64_t E,
+                      int elem_bytes, hipStream_t stream);
+
+/*
+ * naive_transpose021: the same result with one thread per output element and
+ * its input element found by index arithmetic (a generic strided copy, the
+ * pages' "direct" version); the baseline the tiled kernels are measured
+ * against. Same arguments and errors; one [R, S] matrix must hold < 2^31
+ * elements.
+ */
+int naive_transpose021(const void* in, void* out, int64_t B, int64_t R, int64_t S, int64_t E,
+                       int elem_bytes, hipStream_t stream);
+
+/*
+ * fuse_channel_shuffle: ChannelShuffle of a 4-D tensor with `groups` groups
+ * (the runtime page, section 2: channels viewed as [groups, C / groups],
+ * the two axes swapped): output channel i * groups + g holds input channel
+ * g * (C / groups) + i. layout NP_NCHW: [N, C, H, W], the transpose of
+ * [N, groups, C / groups, H * W]; NP_NHWC: [N, H, W, C], the transpose of
+ * [N * H * W, groups, C / groups, 1].
+ * Errors: as fuse_transpose021, and NP_EINVAL unless groups >= 1 divides C.
+ */
+int fuse_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64_t H, int64_t W,
+                         int64_t groups, int layout, int elem_bytes, hipStream_t stream);
+
+/* naive_channel_shuffle: the same through naive_transpose021. */
+int naive_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64_t H, int64_t W,
+                          int64_t groups, int layout, int elem_bytes, hipStream_t stream);
+
+/*
+ * np_transpose_plan: which kernel fuse_transpose021 (naive = 0) or
+ * naive_transpose021 (naive = 1) would launch for these pointers and sizes,
+ * without launching anything or touching a device (pointers are only looked
+ * at for their alignment). Returns item_bytes | kernel << 8 | vec << 12 with
+ * kernel 1 = LDS tiles, 2 = whole matrices through LDS, 3 = item by item, and
+ * vec = 1 when both sides move as 16-byte vectors; 0 for an empty tensor; a
+ * negative status on invalid arguments (as fuse_transpose021).
+ */
+int np_transpose_plan(const void* in, const void* out, int64_t B, int64_t R, int64_t S,
+                      int64_t E, int elem_bytes, int naive);
+
 #ifdef __cplusplus
 }
 #endif

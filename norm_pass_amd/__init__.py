@@ -63,6 +63,11 @@ def _load():
         "unfused_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I, P, S, P],
         "unfused_qkv_rope": [P, P, P, P, I64, I, I, P, F, F, I, P],
         "np_empty_launches": [I, P],
+        "fuse_transpose021": [P, P, I64, I64, I64, I64, I, P],
+        "naive_transpose021": [P, P, I64, I64, I64, I64, I, P],
+        "fuse_channel_shuffle": [P, P, I64, I64, I64, I64, I64, I, I, P],
+        "naive_channel_shuffle": [P, P, I64, I64, I64, I64, I64, I, I, P],
+        "np_transpose_plan": [P, P, I64, I64, I64, I64, I, I],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -222,6 +227,55 @@ _a_unfused_chain = _a_fuse_chain
 _a_unfused_qkv_rope = _a_fuse_qkv_rope
 
 
+def _dense(*ts):
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("layout calls need contiguous (dense row-major) tensors")
+
+
+def _tr_shape(x, shape):
+    if shape is None:
+        if x.dim() != 4:
+            raise ValueError("pass shape=(B, R, S, E) for a tensor that is not 4-D")
+        shape = tuple(x.shape)
+    B, R, S, E = shape
+    if B * R * S * E != x.numel():
+        raise ValueError(f"shape {shape} does not match {x.numel()} elements")
+    return B, R, S, E
+
+
+def _a_fuse_transpose021(x, out, shape=None, stream=None):
+    _dense(x, out)
+    B, R, S, E = _tr_shape(x, shape)
+    if out.numel() != x.numel() or out.element_size() != x.element_size():
+        raise ValueError("out must hold as many elements of the same size as x")
+    _keep(stream, x, out)
+    return (_ptr(x), _ptr(out), B, R, S, E, x.element_size(), _stream(stream))
+
+
+_a_naive_transpose021 = _a_fuse_transpose021
+
+_LAYOUTS = {"nchw": 0, "nhwc": 1, 0: 0, 1: 1}
+
+
+def _a_fuse_channel_shuffle(x, out, groups: int, layout="nchw", stream=None):
+    _dense(x, out)
+    if x.dim() != 4:
+        raise ValueError("channel_shuffle needs a 4-D tensor")
+    lay = _LAYOUTS[layout]
+    if lay == 0:
+        N, Cc, H, W = x.shape
+    else:
+        N, H, W, Cc = x.shape
+    if out.numel() != x.numel() or out.element_size() != x.element_size():
+        raise ValueError("out must hold as many elements of the same size as x")
+    _keep(stream, x, out)
+    return (_ptr(x), _ptr(out), N, Cc, H, W, groups, lay, x.element_size(), _stream(stream))
+
+
+_a_naive_channel_shuffle = _a_fuse_channel_shuffle
+
+
 def _a_unfused_det_decode(levels, strides, anchors, out, workspace, n_anchors: int = 3,
                           n_ch: int = 85, stream=None):
     a = _a_fuse_det_decode(levels, strides, anchors, out, n_anchors, n_ch, stream)
@@ -291,6 +345,48 @@ def fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps: float = 1e-5, stream=
     _check(_lib.fuse_add_layernorm(*_a_fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps,
                                                           stream)), "fuse_add_layernorm")
     return h_out, out
+
+
+def fuse_transpose021(x, out, shape=None, stream=None):
+    """out[b, s, r, e] = x[b, r, s, e] for x of shape (B, R, S, E) (x.shape if
+    4-D, else pass shape); any dtype, copied bit for bit."""
+    _check(_lib.fuse_transpose021(*_a_fuse_transpose021(x, out, shape, stream)),
+           "fuse_transpose021")
+    return out
+
+
+def naive_transpose021(x, out, shape=None, stream=None):
+    _check(_lib.naive_transpose021(*_a_naive_transpose021(x, out, shape, stream)),
+           "naive_transpose021")
+    return out
+
+
+def fuse_channel_shuffle(x, out, groups: int, layout="nchw", stream=None):
+    _check(_lib.fuse_channel_shuffle(*_a_fuse_channel_shuffle(x, out, groups, layout, stream)),
+           "fuse_channel_shuffle")
+    return out
+
+
+def naive_channel_shuffle(x, out, groups: int, layout="nchw", stream=None):
+    _check(_lib.naive_channel_shuffle(*_a_naive_channel_shuffle(x, out, groups, layout, stream)),
+           "naive_channel_shuffle")
+    return out
+
+
+TR_KERNELS = {1: "tile", 2: "small", 3: "items"}
+
+
+def np_transpose_plan(in_ptr: int, out_ptr: int, shape, elem_bytes: int, naive: bool = False):
+    """The kernel fuse_transpose021 / naive_transpose021 would launch for these
+    addresses and sizes (host only): {"kernel", "item", "vec"} or None if empty."""
+    B, R, S, E = shape
+    rc = _lib.np_transpose_plan(C.c_void_p(in_ptr), C.c_void_p(out_ptr), B, R, S, E, elem_bytes,
+                                int(naive))
+    if rc < 0:
+        _check(rc, "np_transpose_plan")
+    if rc == 0:
+        return None
+    return {"kernel": TR_KERNELS[(rc >> 8) & 15], "item": rc & 255, "vec": bool(rc >> 12 & 1)}
 
 
 # ------------------------------------------------------- unfused baselines

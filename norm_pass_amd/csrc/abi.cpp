@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -196,6 +197,182 @@ int fill_det_args(np::DetArgs& a, const void* const* lv, int n_levels, const int
     a.tile_start[l + 1] = (int32_t)tiles_total;
   }
   a.total_rows = row;
+  return NP_OK;
+}
+
+
+// ---- layout: batched transpose [B, R, S, E] -> [B, S, R, E] ----------------
+
+enum TrKernel { TR_TILE = 1, TR_SMALL = 2, TR_ITEMS = 3 };
+
+struct TrPlan {
+  int kernel = 0;
+  int item = 1;      // bytes per load / store item
+  bool vec = false;  // 16-byte vectors on both sides
+  int64_t B = 0, R = 0, S = 0, Ei = 0;  // shape in items (Ei items per unit)
+  int64_t per_chunk = 1;                 // matrices per block (TR_SMALL)
+};
+
+int pow2_item(uint64_t v) {  // largest power of two <= 16 dividing v
+  int w = 16;
+  while (w > 1 && (v % (uint64_t)w) != 0) w >>= 1;
+  return w;
+}
+
+int validate_transpose(const void* in, const void* out, int64_t B, int64_t R, int64_t S,
+                       int64_t E, int elem_bytes, int64_t* total) {
+  if (B < 0 || R < 0 || S < 0 || E < 0)
+    return fail(NP_EINVAL, "negative size (B=%lld R=%lld S=%lld E=%lld)", (long long)B,
+                (long long)R, (long long)S, (long long)E);
+  if (elem_bytes < 1 || elem_bytes > 16)
+    return fail(NP_EINVAL, "elem_bytes = %d, must be 1..16", elem_bytes);
+  const int64_t lim = (int64_t)1 << 31;
+  if (R >= lim || S >= lim || E >= lim || B >= ((int64_t)1 << 40))
+    return fail(NP_EINVAL, "size out of range (R, S, E < 2^31, B < 2^40)");
+  // total bytes <= 2^46 (64 TiB): checked one factor at a time
+  long double t = (long double)B * R * S * E * elem_bytes;
+  if (t > (long double)((int64_t)1 << 46)) return fail(NP_EINVAL, "tensor larger than 2^46 bytes");
+  *total = B * R * S * E * elem_bytes;
+  if (*total == 0) return NP_OK;
+  if (!in || !out) return fail(NP_EINVAL, "NULL buffer");
+  const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out;
+  if (a < b + (uint64_t)*total && b < a + (uint64_t)*total)
+    return fail(NP_EINVAL, "in and out overlap (a transpose cannot run in place)");
+  return NP_OK;
+}
+
+TrPlan plan_transpose(const void* in, const void* out, int64_t B, int64_t R, int64_t S, int64_t E,
+                      int elem_bytes, bool naive) {
+  TrPlan p;
+  const uint64_t u = (uint64_t)E * elem_bytes;  // unit bytes
+  const uint64_t addr = (uint64_t)(uintptr_t)in | (uint64_t)(uintptr_t)out;
+  if (!naive && (R == 1 || S == 1)) {  // no axis to swap: a contiguous copy
+    const uint64_t total = (uint64_t)B * R * S * u;
+    p.item = pow2_item(total | addr);
+    p.kernel = TR_ITEMS;
+    p.B = (int64_t)(total / p.item);
+    p.R = p.S = p.Ei = 1;
+    return p;
+  }
+  p.item = pow2_item((naive ? (uint64_t)elem_bytes : u) | addr);
+  p.B = B;
+  p.R = R;
+  p.S = S;
+  p.Ei = (int64_t)(u / p.item);
+  if (naive) {
+    p.kernel = TR_ITEMS;
+    return p;
+  }
+  const uint64_t mat = (uint64_t)R * S * u;
+  if (mat <= np::kSmallChunkBytes) {
+    p.kernel = TR_SMALL;
+    const uint64_t k_max = np::kSmallChunkBytes / mat;
+    uint64_t g = 16;
+    while (g > 1 && (mat * (16 / g)) % 16 != 0) g >>= 1;  // g = gcd(mat, 16)
+    const uint64_t step = 16 / g;                          // matrices per 16-byte multiple
+    if (k_max >= step && (addr & 15) == 0) {
+      p.per_chunk = (int64_t)(k_max / step * step);
+      p.vec = true;
+    } else {
+      p.per_chunk = (int64_t)k_max;
+    }
+    return p;
+  }
+  if ((uint64_t)p.item == u) {
+    p.kernel = TR_TILE;
+    p.vec = (addr & 15) == 0 && (S * (int64_t)u) % 16 == 0 && (R * (int64_t)u) % 16 == 0;
+    return p;
+  }
+  p.kernel = TR_ITEMS;
+  return p;
+}
+
+int run_transpose(const void* in, void* out, int64_t B, int64_t R, int64_t S, int64_t E,
+                  int elem_bytes, bool naive, hipStream_t stream, const char* who) {
+  int64_t total = 0;
+  int rc = validate_transpose(in, out, B, R, S, E, elem_bytes, &total);
+  if (rc) return rc;
+  if (total == 0) return ok();
+  const TrPlan p = plan_transpose(in, out, B, R, S, E, elem_bytes, naive);
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  const int64_t mat_items = p.R * p.S * p.Ei;
+  if (p.kernel == TR_ITEMS && mat_items > lim)
+    return fail(NP_EINVAL, "%s: one [R, S] matrix holds %lld items of %d bytes (limit 2^31 - 1)",
+                who, (long long)mat_items, p.item);
+  if ((rc = check_device())) return rc;
+  const uint8_t* src = static_cast<const uint8_t*>(in);
+  uint8_t* dst = static_cast<uint8_t*>(out);
+  const int64_t mat_bytes = mat_items * p.item;
+  hipError_t e = hipSuccess;
+  if (p.kernel == TR_TILE) {
+    const int64_t T = np::tile_side(p.item);
+    const int64_t n_rt = (p.R + T - 1) / T, n_st = (p.S + T - 1) / T;
+    const int64_t per_b = n_rt * n_st;
+    if (per_b > lim) return fail(NP_EINVAL, "%s: too many tiles per matrix", who);
+    np::TileArgs a{};
+    a.R = (uint32_t)p.R;
+    a.S = (uint32_t)p.S;
+    a.tiles_per_b = np::make_fastdiv((uint32_t)per_b);
+    a.n_st = np::make_fastdiv((uint32_t)n_st);
+    const int64_t b_step = std::max<int64_t>(1, lim / per_b);
+    for (int64_t b0 = 0; b0 < p.B && e == hipSuccess; b0 += b_step) {
+      const int64_t nb = std::min(b_step, p.B - b0);
+      e = np::launch_tr_tile(src + b0 * mat_bytes, dst + b0 * mat_bytes, a,
+                             (uint32_t)(nb * per_b), p.item, p.vec, stream);
+    }
+  } else if (p.kernel == TR_SMALL) {
+    np::SmallArgs a{};
+    a.R = (uint32_t)p.R;
+    a.S = (uint32_t)p.S;
+    a.per_chunk = (uint32_t)p.per_chunk;
+    a.mat_items = np::make_fastdiv((uint32_t)mat_items);
+    a.re = np::make_fastdiv((uint32_t)(p.R * p.Ei));
+    a.e = np::make_fastdiv((uint32_t)p.Ei);
+    const int64_t b_step = lim / p.per_chunk * p.per_chunk;  // keeps 32-bit block math
+    for (int64_t b0 = 0; b0 < p.B && e == hipSuccess; b0 += b_step) {
+      const int64_t nb = std::min(b_step, p.B - b0);
+      a.B = (uint32_t)nb;
+      e = np::launch_tr_small(src + b0 * mat_bytes, dst + b0 * mat_bytes, a,
+                              (uint32_t)((nb + p.per_chunk - 1) / p.per_chunk), p.item, p.vec,
+                              stream);
+    }
+  } else {
+    np::ItemArgs a{};
+    a.e = np::make_fastdiv((uint32_t)p.Ei);
+    a.r = np::make_fastdiv((uint32_t)p.R);
+    a.s = np::make_fastdiv((uint32_t)p.S);
+    // whole matrices per launch, fewer than 2^31 items
+    const int64_t b_step = std::max<int64_t>(1, lim / mat_items);
+    for (int64_t b0 = 0; b0 < p.B && e == hipSuccess; b0 += b_step) {
+      const int64_t nb = std::min(b_step, p.B - b0);
+      a.n_items = (uint32_t)(nb * mat_items);
+      e = np::launch_tr_items(src + b0 * mat_bytes, dst + b0 * mat_bytes, a, p.item, stream);
+    }
+  }
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
+int shuffle_shape(int64_t N, int64_t C, int64_t H, int64_t W, int64_t groups, int layout,
+                  int64_t* B, int64_t* R, int64_t* S, int64_t* E) {
+  if (N < 0 || C < 0 || H < 0 || W < 0)
+    return fail(NP_EINVAL, "negative size (N=%lld C=%lld H=%lld W=%lld)", (long long)N,
+                (long long)C, (long long)H, (long long)W);
+  if (groups < 1 || (C % groups) != 0)
+    return fail(NP_EINVAL, "groups = %lld must be >= 1 and divide C = %lld", (long long)groups,
+                (long long)C);
+  if (layout != NP_NCHW && layout != NP_NHWC) return fail(NP_EINVAL, "unknown layout %d", layout);
+  if (H > ((int64_t)1 << 31) || W > ((int64_t)1 << 31) || N > ((int64_t)1 << 40))
+    return fail(NP_EINVAL, "size out of range");
+  *R = groups;
+  *S = C / groups;
+  if (layout == NP_NCHW) {
+    *B = N;
+    *E = H * W;
+  } else {
+    *B = N * H * W;
+    *E = 1;
+  }
   return NP_OK;
 }
 
@@ -490,6 +667,43 @@ int np_empty_launches(int count, hipStream_t stream) {
     if (e != hipSuccess) return hip_fail(e, "np_empty_launches");
   }
   return ok();
+}
+
+int fuse_transpose021(const void* in, void* out, int64_t B, int64_t R, int64_t S, int64_t E,
+                      int elem_bytes, hipStream_t stream) {
+  return run_transpose(in, out, B, R, S, E, elem_bytes, false, stream, "fuse_transpose021");
+}
+
+int naive_transpose021(const void* in, void* out, int64_t B, int64_t R, int64_t S, int64_t E,
+                       int elem_bytes, hipStream_t stream) {
+  return run_transpose(in, out, B, R, S, E, elem_bytes, true, stream, "naive_transpose021");
+}
+
+int fuse_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64_t H, int64_t W,
+                         int64_t groups, int layout, int elem_bytes, hipStream_t stream) {
+  int64_t B, R, S, E;
+  int rc = shuffle_shape(N, C, H, W, groups, layout, &B, &R, &S, &E);
+  if (rc) return rc;
+  return run_transpose(in, out, B, R, S, E, elem_bytes, false, stream, "fuse_channel_shuffle");
+}
+
+int naive_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64_t H, int64_t W,
+                          int64_t groups, int layout, int elem_bytes, hipStream_t stream) {
+  int64_t B, R, S, E;
+  int rc = shuffle_shape(N, C, H, W, groups, layout, &B, &R, &S, &E);
+  if (rc) return rc;
+  return run_transpose(in, out, B, R, S, E, elem_bytes, true, stream, "naive_channel_shuffle");
+}
+
+int np_transpose_plan(const void* in, const void* out, int64_t B, int64_t R, int64_t S,
+                      int64_t E, int elem_bytes, int naive) {
+  int64_t total = 0;
+  int rc = validate_transpose(in, out, B, R, S, E, elem_bytes, &total);
+  if (rc) return rc;
+  if (total == 0) return ok();
+  const TrPlan p = plan_transpose(in, out, B, R, S, E, elem_bytes, naive != 0);
+  ok();
+  return p.item | (p.kernel << 8) | (p.vec ? 1 << 12 : 0);
 }
 
 }  // extern "C"

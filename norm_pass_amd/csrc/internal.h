@@ -94,6 +94,40 @@ hipError_t launch_det_range_op(void* rows, int batch, int A, int C, int H, int W
 hipError_t launch_det_concat(const void* const* parts, const int64_t* part_rows, int n_parts,
                              void* out, int batch, int64_t total_rows, int C, int dt,
                              hipStream_t s);
+// layout: batched transpose [B, R, S, E] -> [B, S, R, E] of byte-sized items
+// n / d for any n < 2^32: q = (umulhi(n, m) + n) >> s with the round-up
+// multiplier m = floor(2^32 (2^s - d) / d) + 1, s = ceil(log2 d) (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const uint64_t m = (((1ull << 32) * ((1ull << s) - d)) / d) + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+struct TileArgs {  // units of 1..16 bytes, T x T tiles
+  uint32_t R, S;
+  FastDiv tiles_per_b, n_st;
+};
+constexpr uint32_t kSmallChunkBytes = 16384;
+struct SmallArgs {  // whole matrices per block; B = matrices in this launch
+  uint32_t B, R, S, per_chunk;
+  FastDiv mat_items, re, e;  // items per matrix, R * E, E
+};
+struct ItemArgs {  // one thread per item; B * S * R * E items
+  uint32_t n_items;
+  FastDiv e, r, s;
+};
+int tile_side(int unit_bytes);
+hipError_t launch_tr_tile(const void* in, void* out, const TileArgs& a, uint32_t n_tiles,
+                          int unit_bytes, bool vec, hipStream_t s);
+hipError_t launch_tr_small(const void* in, void* out, const SmallArgs& a, uint32_t grid,
+                           int item_bytes, bool vec, hipStream_t s);
+hipError_t launch_tr_items(const void* in, void* out, const ItemArgs& a, int item_bytes,
+                           hipStream_t s);
+
 hipError_t launch_cast_to_f32(const void* in, float* out, int64_t n, int dt, hipStream_t s);
 hipError_t launch_empty(hipStream_t s);
 

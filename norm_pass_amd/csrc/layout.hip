@@ -1,0 +1,301 @@
+// Layout kernels: the batched transpose of the two middle axes
+// [B, R, S, E] -> [B, S, R, E], and through it ChannelShuffle (runtime page
+// "CUDA算子与AI运行时", sections 2 and 2.1: a strided transpose done element by
+// element in output order reads addresses that lie far apart; staging tiles in
+// on-chip memory keeps both the reads and the writes contiguous).
+//
+// A "unit" is the E elements that move together (u = E * elem_bytes bytes);
+// an "item" (type W) is what one load or store moves. Kernels:
+//   tr_tile<W>   the unit is the item, u in {1, 2, 4, 8, 16}: T x T unit tiles
+//                pass through LDS; a tile row is 256 bytes (128 for u = 1).
+//                16-byte loads run along S in the input, 16-byte stores along R
+//                in the output.
+//   tr_small<W>  one R x S matrix fits in 16 KB: a chunk of whole matrices is
+//                contiguous in both tensors, so it is loaded with 16-byte loads
+//                into LDS and written back permuted with 16-byte stores.
+//   tr_items<W>  one thread per item in output order, its input item found by
+//                index arithmetic. With 16-byte items and units of >= 64 bytes
+//                both sides are runs of whole units; with element-sized items
+//                it is the naive strided copy the fused kernels are measured
+//                against.
+// Index arithmetic inside a launch is 32-bit (the host splits the batch axis
+// so that a launch covers fewer than 2^31 items); divisions by runtime
+// constants use multiply-high reciprocals.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.h"
+#include "internal.h"
+
+namespace np {
+
+namespace {
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.s);
+}
+
+template <int U>
+struct Item;
+template <>
+struct Item<1> { typedef uint8_t T; };
+template <>
+struct Item<2> { typedef uint16_t T; };
+template <>
+struct Item<4> { typedef uint32_t T; };
+template <>
+struct Item<8> { typedef uint64_t T; };
+template <>
+struct Item<16> { typedef u32x4 T; };
+
+template <int U>
+struct TileGeom {
+  static constexpr int T = U == 1 ? 128 : 256 / U;   // units per tile side
+  static constexpr int ROWB = T * U;                 // bytes of one tile row
+  static constexpr int VPR = ROWB / 16;              // 16-byte vectors per row
+  static constexpr int RPP = 256 / VPR;              // rows per pass of 256 threads
+  static constexpr int IPV = 16 / U;                 // units per vector
+  // LDS row pitch: one pad word (keeps a column's units in different banks);
+  // 8- and 16-byte units pad by their own size so LDS accesses stay aligned.
+  static constexpr int PITCH = ROWB + (U <= 4 ? 4 : U);
+  static constexpr int LDS = T * PITCH;
+};
+
+// Store 16 bytes into LDS at an address aligned to the unit size only.
+template <int U>
+__device__ __forceinline__ void lds_put16(uint8_t* p, u32x4 v) {
+  if constexpr (U >= 16) {
+    *reinterpret_cast<u32x4*>(p) = v;
+  } else if constexpr (U == 8) {
+    reinterpret_cast<uint64_t*>(p)[0] = (uint64_t)v.x | ((uint64_t)v.y << 32);
+    reinterpret_cast<uint64_t*>(p)[1] = (uint64_t)v.z | ((uint64_t)v.w << 32);
+  } else {
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+    q[0] = v.x;
+    q[1] = v.y;
+    q[2] = v.z;
+    q[3] = v.w;
+  }
+}
+
+template <int U, bool VEC>
+__global__ __launch_bounds__(256) void tr_tile(const uint8_t* __restrict__ in,
+                                               uint8_t* __restrict__ out, TileArgs a) {
+  typedef TileGeom<U> G;
+  typedef typename Item<U>::T W;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS];
+  const uint32_t tile = blockIdx.x;
+  const uint32_t b = fdiv(tile, a.tiles_per_b);
+  const uint32_t rem = tile - b * a.tiles_per_b.d;
+  const uint32_t rt = fdiv(rem, a.n_st);
+  const uint32_t st = rem - rt * a.n_st.d;
+  const uint32_t r0 = rt * G::T, s0 = st * G::T;
+  const int nr = (int)min((uint32_t)G::T, a.R - r0);
+  const int ns = (int)min((uint32_t)G::T, a.S - s0);
+  const uint8_t* src = in + ((uint64_t)b * a.R + r0) * a.S * U + (uint64_t)s0 * U;
+  uint8_t* dst = out + ((uint64_t)b * a.S + s0) * a.R * U + (uint64_t)r0 * U;
+  const uint64_t in_pitch = (uint64_t)a.S * U, out_pitch = (uint64_t)a.R * U;
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+    // Row pitches and tile edges are whole 16-byte vectors on both sides.
+    const int lr = tid / G::VPR, lv = tid % G::VPR;
+#pragma unroll
+    for (int p = 0; p < G::T / G::RPP; ++p) {
+      const int i = p * G::RPP + lr;
+      if (i < nr && lv * G::IPV < ns)
+        lds_put16<U>(lds + i * G::PITCH + lv * 16, load_raw(src + i * in_pitch + lv * 16));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < G::T / G::RPP; ++p) {
+      const int j = p * G::RPP + lr;  // output row s - s0
+      if (j < ns && lv * G::IPV < nr) {
+        W e[G::IPV];
+#pragma unroll
+        for (int k = 0; k < G::IPV; ++k)
+          e[k] = *reinterpret_cast<const W*>(lds + (lv * G::IPV + k) * G::PITCH + j * U);
+        u32x4 v;
+        __builtin_memcpy(&v, e, 16);
+        store_raw_nt(dst + j * out_pitch + lv * 16, v);
+      }
+    }
+  } else {
+    for (int idx = tid; idx < G::T * G::T; idx += 256) {
+      const int i = idx / G::T, c = idx % G::T;
+      if (i < nr && c < ns)
+        *reinterpret_cast<W*>(lds + i * G::PITCH + c * U) =
+            *reinterpret_cast<const W*>(src + i * in_pitch + c * U);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G::T * G::T; idx += 256) {
+      const int j = idx / G::T, c = idx % G::T;
+      if (j < ns && c < nr)
+        *reinterpret_cast<W*>(dst + j * out_pitch + c * U) =
+            *reinterpret_cast<const W*>(lds + c * G::PITCH + j * U);
+    }
+  }
+}
+
+// Whole matrices through LDS. Items of W bytes, E items per unit, R x S units
+// per matrix; the block handles matrices [blockIdx.x * per_chunk, ...).
+template <int W, bool VEC>
+__global__ __launch_bounds__(256) void tr_small(const uint8_t* __restrict__ in,
+                                                uint8_t* __restrict__ out, SmallArgs a) {
+  typedef typename Item<W>::T It;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kSmallChunkBytes];
+  const uint32_t m0 = blockIdx.x * a.per_chunk;
+  const uint32_t mats = min(a.per_chunk, a.B - m0);
+  const uint32_t R = a.R, S = a.S, E = a.e.d;
+  const uint32_t n_items = mats * a.mat_items.d;
+  const uint64_t base = (uint64_t)m0 * a.mat_items.d * W;
+  const uint8_t* src = in + base;
+  uint8_t* dst = out + base;
+  const uint32_t tid = threadIdx.x;
+  constexpr uint32_t IPV = 16 / W;
+  // load: contiguous
+  uint32_t n_vec = 0;
+  if constexpr (VEC) {
+    n_vec = n_items / IPV;
+    for (uint32_t v = tid; v < n_vec; v += 256)
+      *reinterpret_cast<u32x4*>(lds + v * 16) = load_raw(src + (uint64_t)v * 16);
+  }
+  for (uint32_t i = n_vec * IPV + tid; i < n_items; i += 256)
+    *reinterpret_cast<It*>(lds + i * W) = *reinterpret_cast<const It*>(src + (uint64_t)i * W);
+  __syncthreads();
+  // store: output item j of the chunk is (m, s, r, e) in output order
+  auto input_item = [&](uint32_t j, uint32_t& m, uint32_t& s, uint32_t& r, uint32_t& e) {
+    m = fdiv(j, a.mat_items);
+    uint32_t t = j - m * a.mat_items.d;
+    s = fdiv(t, a.re);
+    t -= s * a.re.d;
+    r = fdiv(t, a.e);
+    e = t - r * E;
+  };
+  if constexpr (VEC) {
+    for (uint32_t v = tid; v < n_vec; v += 256) {
+      uint32_t m, s, r, e;
+      input_item(v * IPV, m, s, r, e);
+      It x[IPV];
+#pragma unroll
+      for (uint32_t k = 0; k < IPV; ++k) {
+        x[k] = *reinterpret_cast<const It*>(lds + (((m * R + r) * S + s) * E + e) * W);
+        if (++e == E) {
+          e = 0;
+          if (++r == R) {
+            r = 0;
+            if (++s == S) {
+              s = 0;
+              ++m;
+            }
+          }
+        }
+      }
+      u32x4 o;
+      __builtin_memcpy(&o, x, 16);
+      store_raw_nt(dst + (uint64_t)v * 16, o);
+    }
+  }
+  for (uint32_t j = n_vec * IPV + tid; j < n_items; j += 256) {
+    uint32_t m, s, r, e;
+    input_item(j, m, s, r, e);
+    *reinterpret_cast<It*>(dst + (uint64_t)j * W) =
+        *reinterpret_cast<const It*>(lds + (((m * R + r) * S + s) * E + e) * W);
+  }
+}
+
+// One thread per output item.
+template <int W>
+__global__ __launch_bounds__(256) void tr_items(const uint8_t* __restrict__ in,
+                                                uint8_t* __restrict__ out, ItemArgs a) {
+  typedef typename Item<W>::T It;
+  const uint32_t j = blockIdx.x * 256u + threadIdx.x;
+  if (j >= a.n_items) return;
+  const uint32_t q = fdiv(j, a.e);  // output unit
+  const uint32_t e = j - q * a.e.d;
+  const uint32_t t = fdiv(q, a.r);
+  const uint32_t r = q - t * a.r.d;
+  const uint32_t b = fdiv(t, a.s);
+  const uint32_t s = t - b * a.s.d;
+  const uint32_t src = ((b * a.r.d + r) * a.s.d + s) * a.e.d + e;
+  *reinterpret_cast<It*>(out + (uint64_t)j * W) =
+      *reinterpret_cast<const It*>(in + (uint64_t)src * W);
+}
+
+template <int U>
+hipError_t launch_tile_u(const uint8_t* in, uint8_t* out, const TileArgs& a, uint32_t n_tiles,
+                         bool vec, hipStream_t s) {
+  if (vec)
+    hipLaunchKernelGGL((tr_tile<U, true>), dim3(n_tiles), dim3(256), 0, s, in, out, a);
+  else
+    hipLaunchKernelGGL((tr_tile<U, false>), dim3(n_tiles), dim3(256), 0, s, in, out, a);
+  return hipGetLastError();
+}
+
+template <int W>
+hipError_t launch_small_w(const uint8_t* in, uint8_t* out, const SmallArgs& a, uint32_t grid,
+                          bool vec, hipStream_t s) {
+  if (vec)
+    hipLaunchKernelGGL((tr_small<W, true>), dim3(grid), dim3(256), 0, s, in, out, a);
+  else
+    hipLaunchKernelGGL((tr_small<W, false>), dim3(grid), dim3(256), 0, s, in, out, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int tile_side(int unit_bytes) {
+  switch (unit_bytes) {
+    case 1: return TileGeom<1>::T;
+    case 2: return TileGeom<2>::T;
+    case 4: return TileGeom<4>::T;
+    case 8: return TileGeom<8>::T;
+    case 16: return TileGeom<16>::T;
+    default: return 0;
+  }
+}
+
+hipError_t launch_tr_tile(const void* in, void* out, const TileArgs& a, uint32_t n_tiles,
+                          int unit_bytes, bool vec, hipStream_t s) {
+  const uint8_t* i = static_cast<const uint8_t*>(in);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  switch (unit_bytes) {
+    case 1: return launch_tile_u<1>(i, o, a, n_tiles, vec, s);
+    case 2: return launch_tile_u<2>(i, o, a, n_tiles, vec, s);
+    case 4: return launch_tile_u<4>(i, o, a, n_tiles, vec, s);
+    case 8: return launch_tile_u<8>(i, o, a, n_tiles, vec, s);
+    case 16: return launch_tile_u<16>(i, o, a, n_tiles, vec, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_tr_small(const void* in, void* out, const SmallArgs& a, uint32_t grid,
+                           int item_bytes, bool vec, hipStream_t s) {
+  const uint8_t* i = static_cast<const uint8_t*>(in);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  switch (item_bytes) {
+    case 1: return launch_small_w<1>(i, o, a, grid, vec, s);
+    case 2: return launch_small_w<2>(i, o, a, grid, vec, s);
+    case 4: return launch_small_w<4>(i, o, a, grid, vec, s);
+    case 8: return launch_small_w<8>(i, o, a, grid, vec, s);
+    case 16: return launch_small_w<16>(i, o, a, grid, vec, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_tr_items(const void* in, void* out, const ItemArgs& a, int item_bytes,
+                           hipStream_t s) {
+  const uint8_t* i = static_cast<const uint8_t*>(in);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  const dim3 grid((a.n_items + 255u) / 256u);
+  switch (item_bytes) {
+    case 1: hipLaunchKernelGGL(tr_items<1>, grid, dim3(256), 0, s, i, o, a); break;
+    case 2: hipLaunchKernelGGL(tr_items<2>, grid, dim3(256), 0, s, i, o, a); break;
+    case 4: hipLaunchKernelGGL(tr_items<4>, grid, dim3(256), 0, s, i, o, a); break;
+    case 8: hipLaunchKernelGGL(tr_items<8>, grid, dim3(256), 0, s, i, o, a); break;
+    case 16: hipLaunchKernelGGL(tr_items<16>, grid, dim3(256), 0, s, i, o, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace np

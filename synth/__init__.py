@@ -81,6 +81,20 @@ def uniform_f32(n: int, seed: int, lo: float, hi: float) -> np.ndarray:
     return _fill(n, seed, draw)
 
 
+def random_bytes(n: int, seed: int) -> np.ndarray:
+    """n uniformly distributed bytes (uint8), Philox-keyed per chunk like the
+    float draws (inputs of the bit-copying layout calls)."""
+    out = np.empty(n, np.uint8)
+    nch = (n + CHUNK - 1) // CHUNK
+    keys = np.random.SeedSequence(seed).spawn(max(nch, 1))
+    for i in range(nch):
+        g = np.random.Generator(np.random.Philox(keys[i]))
+        lo = i * CHUNK
+        hi = min(n, lo + CHUNK)
+        out[lo:hi] = np.frombuffer(g.bytes(hi - lo), np.uint8)
+    return out
+
+
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 array -> bf16 bit patterns (uint16), round to nearest even."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -221,3 +235,27 @@ def chain_str(ops) -> str:
         else:
             parts.append(name)
     return " -> ".join(parts)
+
+
+# --------------------------------------------------------------------------
+# Layout workloads (the runtime page "CUDA算子与AI运行时", gtnt.cn/news/145880,
+# section 2: ChannelShuffle of an [N, C, H, W] activation, and the strided
+# transpose it reduces to). Channel counts and resolution follow ShuffleNet V2
+# 1.0x (Ma et al., ECCV 2018), stage 2 at 224 x 224 input: 116 channels at
+# 28 x 28, two groups.
+# --------------------------------------------------------------------------
+
+TRANSPOSE_2D = (1, 8192, 8192, 1)        # fp32 [8192, 8192] -> its transpose
+SHUFFLE_NCHW = (1024, 116, 28, 28)       # fp16, groups 2
+SHUFFLE_GROUPS = 2
+
+
+def transpose_inputs(shape=TRANSPOSE_2D, seed: int = 1006, dtype: str = "f32"):
+    return normal(shape, seed, dtype)
+
+
+def shuffle_inputs(shape=SHUFFLE_NCHW, seed: int = 1007, dtype: str = "f16", layout: int = 0):
+    """N(0, 1) activations of ShuffleNet-V2 stage-2 shape, NCHW (layout 0) or
+    NHWC (layout 1)."""
+    n, c, h, w = shape
+    return normal((n, c, h, w) if layout == 0 else (n, h, w, c), seed, dtype)

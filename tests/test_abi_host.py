@@ -176,3 +176,59 @@ def test_add_layernorm_rejects(npa):
     assert "eps" in _err(npa)
     assert npa.lib().unfused_add_layernorm(*p, 4, 8, 1e-5, 2, NULL, 0, NULL) == -1
     assert "workspace" in _err(npa)
+
+
+# ---- layout calls: validation and kernel choice (host only) ----------------
+
+_LAY = [(1 << 40), (1 << 42)]
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((-1, 4, 4, 1, 4), "negative"),
+    ((1, 4, 4, 1, 0), "elem_bytes"),
+    ((1, 4, 4, 1, 17), "elem_bytes"),
+    ((1, 1 << 31, 4, 1, 4), "out of range"),
+    ((1 << 20, 1 << 20, 1 << 20, 1, 4), "2^46"),
+])
+def test_transpose_rejects(npa, args, msg):
+    B, R, S, E, es = args
+    for fn in (npa.lib().fuse_transpose021, npa.lib().naive_transpose021):
+        assert fn(C.c_void_p(_LAY[0]), C.c_void_p(_LAY[1]), B, R, S, E, es, NULL) == -1
+        assert msg in _err(npa)
+
+
+def test_transpose_rejects_null_and_overlap(npa):
+    f = npa.lib().fuse_transpose021
+    assert f(NULL, C.c_void_p(0x1000), 1, 4, 4, 1, 4, NULL) == -1 and "NULL" in _err(npa)
+    # [0x1000, 0x1040) and [0x1020, 0x1060) overlap
+    assert f(C.c_void_p(0x1000), C.c_void_p(0x1020), 1, 4, 4, 1, 4, NULL) == -1
+    assert "overlap" in _err(npa)
+    assert f(C.c_void_p(0x1000), C.c_void_p(0x1040), 1, 4, 4, 1, 4, NULL) != -1 or \
+        "overlap" not in _err(npa)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((2, 6, 4, 4, 4, 0), "divide"),
+    ((2, 6, 4, 4, 0, 0), "groups"),
+    ((2, 6, 4, 4, 2, 7), "layout"),
+    ((2, -6, 4, 4, 2, 0), "negative"),
+])
+def test_channel_shuffle_rejects(npa, args, msg):
+    for fn in (npa.lib().fuse_channel_shuffle, npa.lib().naive_channel_shuffle):
+        assert fn(C.c_void_p(_LAY[0]), C.c_void_p(_LAY[1]), *args, 2, NULL) == -1
+        assert msg in _err(npa)
+
+
+def test_transpose_plans(npa):
+    """The kernel the planner picks for each case the GPU parity tests run."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "layout_cases", os.path.join(ROOT, "tests", "test_gpu_layout.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    for shape, es, off, plan in mod.CASES:
+        got = npa.np_transpose_plan(_LAY[0] + off[0], _LAY[1] + off[1], shape, es)
+        assert got == plan, (shape, es, got)
+        naive = npa.np_transpose_plan(_LAY[0] + off[0], _LAY[1] + off[1], shape, es, True)
+        assert naive["kernel"] == "items"
+    assert npa.np_transpose_plan(_LAY[0], _LAY[1], (0, 3, 3, 1), 4) is None
