@@ -282,9 +282,10 @@ typedef enum { NP_NCHW = 0, NP_NHWC = 1 } np_layout;
  * out[b][s][r][e] = in[b][r][s][e]. The E elements of one (r, s) pair (a unit
  * of E * elem_bytes bytes) move together. Kernel choice (host side, from the
  * shape and alignment): units of 1/2/4/8/16 bytes in matrices larger than
- * 16 KB go through LDS tiles of 256-byte rows; matrices of <= 16 KB move as
- * whole chunks through LDS; larger units are copied unit by unit in output
- * order. Limits: R, S, E < 2^31, B < 2^40, total <= 2^46 bytes; when neither
+ * 16 KB go through LDS tiles of 512-byte rows (256 / 128 for 2- / 1-byte
+ * units), in diagonal tile order when a row pitch is a power of two of at
+ * least 4 KiB; matrices of <= 16 KB move as whole chunks through LDS; larger
+ * units are copied unit by unit in output order. Limits: R, S, E < 2^31, B < 2^40, total <= 2^46 bytes; when neither
  * LDS kernel applies, one [R, S] matrix must hold < 2^31 items.
  * Errors: NP_EINVAL for negative sizes, elem_bytes outside 1..16, NULL or
  * overlapping buffers (unless the tensor is empty); nothing is launched then.
@@ -322,10 +323,11 @@ int naive_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64
  * np_transpose_plan: which kernel fuse_transpose021 (naive = 0) or
  * naive_transpose021 (naive = 1) would launch for these pointers and sizes,
  * without launching anything or touching a device (pointers are only looked
- * at for their alignment). Returns item_bytes | kernel << 8 | vec << 12 with
- * kernel 1 = LDS tiles, 2 = whole matrices through LDS, 3 = item by item, and
- * vec = 1 when both sides move as 16-byte vectors; 0 for an empty tensor; a
- * negative status on invalid arguments (as fuse_transpose021).
+ * at for their alignment). Returns item_bytes | kernel << 8 | vec << 12 |
+ * diagonal << 13 with kernel 1 = LDS tiles, 2 = whole matrices through LDS,
+ * 3 = item by item, vec = 1 when both sides move as 16-byte vectors and
+ * diagonal = 1 for the diagonal tile order; 0 for an empty tensor; a negative
+ * status on invalid arguments (as fuse_transpose021).
  */
 int np_transpose_plan(const void* in, const void* out, int64_t B, int64_t R, int64_t S,
                       int64_t E, int elem_bytes, int naive);

@@ -378,7 +378,8 @@ TR_KERNELS = {1: "tile", 2: "small", 3: "items"}
 
 def np_transpose_plan(in_ptr: int, out_ptr: int, shape, elem_bytes: int, naive: bool = False):
     """The kernel fuse_transpose021 / naive_transpose021 would launch for these
-    addresses and sizes (host only): {"kernel", "item", "vec"} or None if empty."""
+    addresses and sizes (host only): {"kernel", "item", "vec", "diag"} or None if
+    empty."""
     B, R, S, E = shape
     rc = _lib.np_transpose_plan(C.c_void_p(in_ptr), C.c_void_p(out_ptr), B, R, S, E, elem_bytes,
                                 int(naive))
@@ -386,7 +387,8 @@ def np_transpose_plan(in_ptr: int, out_ptr: int, shape, elem_bytes: int, naive: 
         _check(rc, "np_transpose_plan")
     if rc == 0:
         return None
-    return {"kernel": TR_KERNELS[(rc >> 8) & 15], "item": rc & 255, "vec": bool(rc >> 12 & 1)}
+    return {"kernel": TR_KERNELS[(rc >> 8) & 15], "item": rc & 255, "vec": bool(rc >> 12 & 1),
+            "diag": bool(rc >> 13 & 1)}
 
 
 # ------------------------------------------------------- unfused baselines

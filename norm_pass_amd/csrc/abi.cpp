@@ -211,6 +211,7 @@ struct TrPlan {
   bool vec = false;  // 16-byte vectors on both sides
   int64_t B = 0, R = 0, S = 0, Ei = 0;  // shape in items (Ei items per unit)
   int64_t per_chunk = 1;                 // matrices per block (TR_SMALL)
+  bool diagonal = false;                 // diagonal tile order (TR_TILE)
 };
 
 int pow2_item(uint64_t v) {  // largest power of two <= 16 dividing v
@@ -281,6 +282,10 @@ TrPlan plan_transpose(const void* in, const void* out, int64_t B, int64_t R, int
   if ((uint64_t)p.item == u) {
     p.kernel = TR_TILE;
     p.vec = (addr & 15) == 0 && (S * (int64_t)u) % 16 == 0 && (R * (int64_t)u) % 16 == 0;
+    // A row pitch that is a power of two of >= 4 KiB maps the rows of one tile
+    // column onto the same memory channels; the diagonal order spreads them.
+    auto pow2_pitch = [](int64_t b) { return b >= 4096 && (b & (b - 1)) == 0; };
+    p.diagonal = pow2_pitch(S * (int64_t)u) || pow2_pitch(R * (int64_t)u);
     return p;
   }
   p.kernel = TR_ITEMS;
@@ -313,7 +318,9 @@ int run_transpose(const void* in, void* out, int64_t B, int64_t R, int64_t S, in
     a.R = (uint32_t)p.R;
     a.S = (uint32_t)p.S;
     a.tiles_per_b = np::make_fastdiv((uint32_t)per_b);
+    a.n_rt = np::make_fastdiv((uint32_t)n_rt);
     a.n_st = np::make_fastdiv((uint32_t)n_st);
+    a.diagonal = p.diagonal ? 1u : 0u;
     const int64_t b_step = std::max<int64_t>(1, lim / per_b);
     for (int64_t b0 = 0; b0 < p.B && e == hipSuccess; b0 += b_step) {
       const int64_t nb = std::min(b_step, p.B - b0);
@@ -703,7 +710,7 @@ int np_transpose_plan(const void* in, const void* out, int64_t B, int64_t R, int
   if (total == 0) return ok();
   const TrPlan p = plan_transpose(in, out, B, R, S, E, elem_bytes, naive != 0);
   ok();
-  return p.item | (p.kernel << 8) | (p.vec ? 1 << 12 : 0);
+  return p.item | (p.kernel << 8) | (p.vec ? 1 << 12 : 0) | (p.diagonal ? 1 << 13 : 0);
 }
 
 }  // extern "C"

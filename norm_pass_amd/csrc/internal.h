@@ -109,7 +109,8 @@ inline FastDiv make_fastdiv(uint32_t d) {
 }
 struct TileArgs {  // units of 1..16 bytes, T x T tiles
   uint32_t R, S;
-  FastDiv tiles_per_b, n_st;
+  uint32_t diagonal;  // diagonal tile order (power-of-two pitches)
+  FastDiv tiles_per_b, n_rt, n_st;
 };
 constexpr uint32_t kSmallChunkBytes = 16384;
 struct SmallArgs {  // whole matrices per block; B = matrices in this launch

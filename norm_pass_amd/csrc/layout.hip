@@ -7,9 +7,9 @@
 // A "unit" is the E elements that move together (u = E * elem_bytes bytes);
 // an "item" (type W) is what one load or store moves. Kernels:
 //   tr_tile<W>   the unit is the item, u in {1, 2, 4, 8, 16}: T x T unit tiles
-//                pass through LDS; a tile row is 256 bytes (128 for u = 1).
-//                16-byte loads run along S in the input, 16-byte stores along R
-//                in the output.
+//                pass through LDS; a tile row is 512 bytes (256 for u = 2, 128
+//                for u = 1). 16-byte loads run along S in the input, 16-byte
+//                stores along R in the output.
 //   tr_small<W>  one R x S matrix fits in 16 KB: a chunk of whole matrices is
 //                contiguous in both tensors, so it is loaded with 16-byte loads
 //                into LDS and written back permuted with 16-byte stores.
@@ -50,15 +50,18 @@ struct Item<16> { typedef u32x4 T; };
 
 template <int U>
 struct TileGeom {
-  static constexpr int T = U == 1 ? 128 : 256 / U;   // units per tile side
-  static constexpr int ROWB = T * U;                 // bytes of one tile row
+  // A tile row is 512 bytes for units of >= 4 bytes (256 for 2, 128 for 1):
+  // long enough that each row read or written is a few whole DRAM bursts.
+  static constexpr int ROWB = U >= 4 ? 512 : 128 * U;
+  static constexpr int T = ROWB / U;                 // units per tile side
+  static constexpr int NT = ROWB >= 512 ? 512 : 256; // threads per block
   static constexpr int VPR = ROWB / 16;              // 16-byte vectors per row
-  static constexpr int RPP = 256 / VPR;              // rows per pass of 256 threads
+  static constexpr int RPP = NT / VPR;               // rows per pass of NT threads
   static constexpr int IPV = 16 / U;                 // units per vector
   // LDS row pitch: one pad word (keeps a column's units in different banks);
   // 8- and 16-byte units pad by their own size so LDS accesses stay aligned.
   static constexpr int PITCH = ROWB + (U <= 4 ? 4 : U);
-  static constexpr int LDS = T * PITCH;
+  static constexpr int LDS = T * PITCH;              // 66,048 bytes at most (U = 4)
 };
 
 // Store 16 bytes into LDS at an address aligned to the unit size only.
@@ -79,16 +82,28 @@ __device__ __forceinline__ void lds_put16(uint8_t* p, u32x4 v) {
 }
 
 template <int U, bool VEC>
-__global__ __launch_bounds__(256) void tr_tile(const uint8_t* __restrict__ in,
-                                               uint8_t* __restrict__ out, TileArgs a) {
+__global__ __launch_bounds__(TileGeom<U>::NT) void tr_tile(const uint8_t* __restrict__ in,
+                                                           uint8_t* __restrict__ out, TileArgs a) {
   typedef TileGeom<U> G;
   typedef typename Item<U>::T W;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS];
   const uint32_t tile = blockIdx.x;
   const uint32_t b = fdiv(tile, a.tiles_per_b);
   const uint32_t rem = tile - b * a.tiles_per_b.d;
-  const uint32_t rt = fdiv(rem, a.n_st);
-  const uint32_t st = rem - rt * a.n_st.d;
+  uint32_t rt, st;
+  if (a.diagonal) {
+    // Diagonal tile order (Ruetsch and Micikevicius, "Optimizing matrix
+    // transpose in CUDA", 2009): blocks running together take tiles from all
+    // tile rows and columns, so that with power-of-two pitches their reads and
+    // writes do not all land on the same few memory channels.
+    const uint32_t k = fdiv(rem, a.n_rt);
+    rt = rem - k * a.n_rt.d;
+    const uint32_t d = k + rt;
+    st = d - fdiv(d, a.n_st) * a.n_st.d;
+  } else {
+    rt = fdiv(rem, a.n_st);
+    st = rem - rt * a.n_st.d;
+  }
   const uint32_t r0 = rt * G::T, s0 = st * G::T;
   const int nr = (int)min((uint32_t)G::T, a.R - r0);
   const int ns = (int)min((uint32_t)G::T, a.S - s0);
@@ -98,16 +113,39 @@ __global__ __launch_bounds__(256) void tr_tile(const uint8_t* __restrict__ in,
   const int tid = threadIdx.x;
   if constexpr (VEC) {
     // Row pitches and tile edges are whole 16-byte vectors on both sides.
+    constexpr int P = G::T / G::RPP;  // passes
     const int lr = tid / G::VPR, lv = tid % G::VPR;
+    if (nr == G::T && ns == G::T) {
+      // Interior tile: every load is issued before the first LDS store, so
+      // each wave keeps P loads in flight.
+      u32x4 v[P];
 #pragma unroll
-    for (int p = 0; p < G::T / G::RPP; ++p) {
+      for (int p = 0; p < P; ++p) v[p] = load_raw(src + (p * G::RPP + lr) * in_pitch + lv * 16);
+#pragma unroll
+      for (int p = 0; p < P; ++p) lds_put16<U>(lds + (p * G::RPP + lr) * G::PITCH + lv * 16, v[p]);
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        W e[G::IPV];
+#pragma unroll
+        for (int k = 0; k < G::IPV; ++k)
+          e[k] = *reinterpret_cast<const W*>(lds + (lv * G::IPV + k) * G::PITCH +
+                                             (p * G::RPP + lr) * U);
+        __builtin_memcpy(&v[p], e, 16);
+      }
+#pragma unroll
+      for (int p = 0; p < P; ++p) store_raw_nt(dst + (p * G::RPP + lr) * out_pitch + lv * 16, v[p]);
+      return;
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
       const int i = p * G::RPP + lr;
       if (i < nr && lv * G::IPV < ns)
         lds_put16<U>(lds + i * G::PITCH + lv * 16, load_raw(src + i * in_pitch + lv * 16));
     }
     __syncthreads();
 #pragma unroll
-    for (int p = 0; p < G::T / G::RPP; ++p) {
+    for (int p = 0; p < P; ++p) {
       const int j = p * G::RPP + lr;  // output row s - s0
       if (j < ns && lv * G::IPV < nr) {
         W e[G::IPV];
@@ -120,14 +158,14 @@ __global__ __launch_bounds__(256) void tr_tile(const uint8_t* __restrict__ in,
       }
     }
   } else {
-    for (int idx = tid; idx < G::T * G::T; idx += 256) {
+    for (int idx = tid; idx < G::T * G::T; idx += G::NT) {
       const int i = idx / G::T, c = idx % G::T;
       if (i < nr && c < ns)
         *reinterpret_cast<W*>(lds + i * G::PITCH + c * U) =
             *reinterpret_cast<const W*>(src + i * in_pitch + c * U);
     }
     __syncthreads();
-    for (int idx = tid; idx < G::T * G::T; idx += 256) {
+    for (int idx = tid; idx < G::T * G::T; idx += G::NT) {
       const int j = idx / G::T, c = idx % G::T;
       if (j < ns && c < nr)
         *reinterpret_cast<W*>(dst + j * out_pitch + c * U) =
@@ -142,6 +180,8 @@ template <int W, bool VEC>
 __global__ __launch_bounds__(256) void tr_small(const uint8_t* __restrict__ in,
                                                 uint8_t* __restrict__ out, SmallArgs a) {
   typedef typename Item<W>::T It;
+  constexpr uint32_t IPV = 16 / W;
+  constexpr uint32_t MAXV = kSmallChunkBytes / 16 / 256;  // vectors per thread, at most
   __shared__ __attribute__((aligned(16))) uint8_t lds[kSmallChunkBytes];
   const uint32_t m0 = blockIdx.x * a.per_chunk;
   const uint32_t mats = min(a.per_chunk, a.B - m0);
@@ -151,44 +191,60 @@ __global__ __launch_bounds__(256) void tr_small(const uint8_t* __restrict__ in,
   const uint8_t* src = in + base;
   uint8_t* dst = out + base;
   const uint32_t tid = threadIdx.x;
-  constexpr uint32_t IPV = 16 / W;
-  // load: contiguous
+  // load: the chunk is contiguous; all of a thread's loads are issued first
   uint32_t n_vec = 0;
   if constexpr (VEC) {
-    n_vec = n_items / IPV;
-    for (uint32_t v = tid; v < n_vec; v += 256)
-      *reinterpret_cast<u32x4*>(lds + v * 16) = load_raw(src + (uint64_t)v * 16);
+    n_vec = n_items / IPV;  // the same for every thread of the block
+    if (n_vec > 0) {
+      u32x4 x[MAXV];
+      // indexes past the end re-load the last vector (in bounds, discarded),
+      // so no branch separates the loads and all of them are in flight together
+#pragma unroll
+      for (uint32_t p = 0; p < MAXV; ++p)
+        x[p] = load_raw(src + (uint64_t)min(tid + p * 256, n_vec - 1) * 16);
+#pragma unroll
+      for (uint32_t p = 0; p < MAXV; ++p)
+        if (tid + p * 256 < n_vec) *reinterpret_cast<u32x4*>(lds + (tid + p * 256) * 16) = x[p];
+    }
   }
   for (uint32_t i = n_vec * IPV + tid; i < n_items; i += 256)
     *reinterpret_cast<It*>(lds + i * W) = *reinterpret_cast<const It*>(src + (uint64_t)i * W);
   __syncthreads();
-  // store: output item j of the chunk is (m, s, r, e) in output order
-  auto input_item = [&](uint32_t j, uint32_t& m, uint32_t& s, uint32_t& r, uint32_t& e) {
-    m = fdiv(j, a.mat_items);
-    uint32_t t = j - m * a.mat_items.d;
+  // store: output item j of the chunk is (m, s, r, e) in output order; its
+  // input item is ((m R + r) S + s) E + e
+  const uint32_t SE = S * E, RSE = a.mat_items.d;
+  auto input_item = [&](uint32_t j, uint32_t& s, uint32_t& r, uint32_t& e) {
+    const uint32_t m = fdiv(j, a.mat_items);
+    uint32_t t = j - m * RSE;
     s = fdiv(t, a.re);
     t -= s * a.re.d;
     r = fdiv(t, a.e);
     e = t - r * E;
+    return ((m * R + r) * S + s) * E + e;
   };
   if constexpr (VEC) {
     for (uint32_t v = tid; v < n_vec; v += 256) {
-      uint32_t m, s, r, e;
-      input_item(v * IPV, m, s, r, e);
+      uint32_t s, r, e;
+      uint32_t off = input_item(v * IPV, s, r, e);
       It x[IPV];
 #pragma unroll
       for (uint32_t k = 0; k < IPV; ++k) {
-        x[k] = *reinterpret_cast<const It*>(lds + (((m * R + r) * S + s) * E + e) * W);
-        if (++e == E) {
-          e = 0;
-          if (++r == R) {
-            r = 0;
-            if (++s == S) {
-              s = 0;
-              ++m;
-            }
-          }
-        }
+        x[k] = *reinterpret_cast<const It*>(lds + off * W);
+        // step to the next output item with selects, not branches: e, then r,
+        // then s carry over; the input offset moves by the matching stride
+        ++e;
+        ++off;
+        const bool ce = e == E;
+        e = ce ? 0u : e;
+        r += ce;
+        off += ce ? SE - E : 0u;
+        const bool cr = r == R;
+        r = cr ? 0u : r;
+        s += cr;
+        off += cr ? E - RSE : 0u;
+        const bool cs = s == S;
+        s = cs ? 0u : s;
+        off += cs ? RSE - SE : 0u;
       }
       u32x4 o;
       __builtin_memcpy(&o, x, 16);
@@ -196,10 +252,9 @@ __global__ __launch_bounds__(256) void tr_small(const uint8_t* __restrict__ in,
     }
   }
   for (uint32_t j = n_vec * IPV + tid; j < n_items; j += 256) {
-    uint32_t m, s, r, e;
-    input_item(j, m, s, r, e);
-    *reinterpret_cast<It*>(dst + (uint64_t)j * W) =
-        *reinterpret_cast<const It*>(lds + (((m * R + r) * S + s) * E + e) * W);
+    uint32_t s, r, e;
+    const uint32_t off = input_item(j, s, r, e);
+    *reinterpret_cast<It*>(dst + (uint64_t)j * W) = *reinterpret_cast<const It*>(lds + off * W);
   }
 }
 
@@ -224,10 +279,11 @@ __global__ __launch_bounds__(256) void tr_items(const uint8_t* __restrict__ in,
 template <int U>
 hipError_t launch_tile_u(const uint8_t* in, uint8_t* out, const TileArgs& a, uint32_t n_tiles,
                          bool vec, hipStream_t s) {
+  const dim3 block(TileGeom<U>::NT);
   if (vec)
-    hipLaunchKernelGGL((tr_tile<U, true>), dim3(n_tiles), dim3(256), 0, s, in, out, a);
+    hipLaunchKernelGGL((tr_tile<U, true>), dim3(n_tiles), block, 0, s, in, out, a);
   else
-    hipLaunchKernelGGL((tr_tile<U, false>), dim3(n_tiles), dim3(256), 0, s, in, out, a);
+    hipLaunchKernelGGL((tr_tile<U, false>), dim3(n_tiles), block, 0, s, in, out, a);
   return hipGetLastError();
 }
 

@@ -65,9 +65,10 @@ def _oracle_tr(orc, x_bytes, shape, es):
     return orc.transpose021(x_bytes.view(_vdt(es)).reshape(shape)).view(np.uint8).reshape(-1)
 
 
-TILE = lambda item, vec: {"kernel": "tile", "item": item, "vec": vec}  # noqa: E731
-SMALL = lambda item, vec: {"kernel": "small", "item": item, "vec": vec}  # noqa: E731
-ITEMS = lambda item: {"kernel": "items", "item": item, "vec": False}  # noqa: E731
+TILE = lambda item, vec, diag=False: {"kernel": "tile", "item": item, "vec": vec,  # noqa: E731
+                                      "diag": diag}
+SMALL = lambda item, vec: {"kernel": "small", "item": item, "vec": vec, "diag": False}  # noqa: E731
+ITEMS = lambda item: {"kernel": "items", "item": item, "vec": False, "diag": False}  # noqa: E731
 
 # (shape [B, R, S, E], elem_bytes, pointer offsets, expected plan of the fused call)
 CASES = [
@@ -82,6 +83,10 @@ CASES = [
     ((1, 40, 33, 1), 16, (0, 0), TILE(16, True)),
     ((2, 100, 96, 2), 2, (0, 0), TILE(4, True)),        # unit of two fp16 elements
     ((1, 128, 160, 1), 4, (4, 0), TILE(4, False)),      # input off 16-byte alignment
+    ((2, 1024, 300, 1), 4, (0, 0), TILE(4, True, True)),  # 4 KiB output pitch: diagonal order
+    ((1, 2048, 200, 1), 2, (0, 0), TILE(2, True, True)),
+    ((1, 520, 1024, 1), 4, (0, 0), TILE(4, True, True)),  # 4 KiB input pitch, ragged R
+    ((1, 1000, 2048, 1), 1, (0, 4), TILE(1, False, False)),  # 2 KiB pitch: row order
     ((105, 2, 116, 1), 2, (0, 0), SMALL(2, True)),      # NHWC shuffle of 116 channels
     ((37, 3, 2, 1), 4, (0, 0), SMALL(4, True)),         # 24-byte matrices
     ((1000, 5, 3, 1), 1, (0, 0), SMALL(1, True)),       # 15-byte matrices
@@ -148,7 +153,7 @@ def test_transpose_2d_fp32_8192(npa, orc):
         assert np.array_equal(out.cpu().numpy().reshape(-1).view(np.uint32),
                               orc.transpose021(x).reshape(-1).view(np.uint32)), fn
     assert npa.np_transpose_plan(xt.data_ptr(), out.data_ptr(), synth.TRANSPOSE_2D, 4) == \
-        TILE(4, True)
+        TILE(4, True, True)
 
 
 @pytest.mark.parametrize("layout", [0, 1], ids=["nchw", "nhwc"])
