@@ -69,11 +69,13 @@ def lib():
         L.oracle_qkv_rope.argtypes = [P, P, P, P, i64, C.c_int, C.c_int, P, C.c_float,
                                       C.c_float, C.c_int, C.c_int, P, P, P, P]
         L.oracle_rope_inv_freq.argtypes = [C.c_float, C.c_int, P]
+        L.oracle_rmsnorm_linear.argtypes = [P, P, P, P, P, i64, i64, i64, C.c_float, C.c_float,
+                                             C.c_int, C.c_int, P, P]
         L.oracle_channel_shuffle.argtypes = [P, P, i64, i64, i64, i64, i64, C.c_int, C.c_int]
         L.oracle_transpose021.argtypes = [P, P, i64, i64, i64, i64, C.c_int]
         for f in ("oracle_chain", "oracle_det_decode", "oracle_add_rmsnorm", "oracle_qkv_rope",
                   "oracle_rope_inv_freq", "oracle_add_layernorm", "oracle_channel_shuffle",
-                  "oracle_transpose021"):
+                  "oracle_transpose021", "oracle_rmsnorm_linear"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -234,6 +236,27 @@ def qkv_rope(qkv, n_heads: int, head_dim: int, base: float, q_scale: float, dt: 
                                base, q_scale, dt, int(eager), *[_p(e) for e in extra])
     _check(rc, "oracle_qkv_rope")
     return (q, k, v, *extra) if want_bound else (q, k, v)
+
+
+def rmsnorm_linear(x, w_norm, Wt, bias, eps: float, scale: float, dt: int, eager: bool = False,
+                   want_exact: bool = False):
+    """RMSNorm + linear + scale (see oracle.h). x [M, K], Wt [N, K]; returns out
+    [M, N] (and, with want_exact, the unrounded values and the per-output
+    magnitude |scale| rstd sum|a W| of the dot product's terms)."""
+    x = _raw(x)
+    Wt = _raw(Wt)
+    M, K = x.shape
+    N = Wt.shape[0]
+    if Wt.shape[1] != K:
+        raise ValueError("Wt must be [N, K]")
+    wn = None if w_norm is None else _raw(w_norm)
+    b = None if bias is None else _raw(bias)
+    out = np.empty((M, N), _NP[dt])
+    ex = np.empty((M, N), np.float64) if want_exact else None
+    cd = np.empty((M, N), np.float64) if want_exact else None
+    _check(lib().oracle_rmsnorm_linear(_p(x), _p(wn), _p(Wt), _p(b), _p(out), M, N, K, eps,
+                                       scale, dt, int(eager), _p(ex), _p(cd)), "rmsnorm_linear")
+    return (out, ex, cd) if want_exact else out
 
 
 # --------------------------------------------------------------------------

@@ -455,6 +455,52 @@ int oracle_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n
 
 }  // extern "C"
 
+int oracle_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, const void* bias,
+                          void* out, int64_t M, int64_t N, int64_t K, float eps, float scale,
+                          int dt, int eager, double* exact, double* cond) {
+  if (!x || !Wt || !out || M < 0 || N < 0 || K <= 0 || !valid_dt(dt)) return -1;
+  if (!(eps > 0.0f) || !std::isfinite(eps) || !std::isfinite(scale)) return -1;
+  const Fmt& f = fmt_of(dt);
+  const long double sc = (long double)scale;
+  std::vector<double> a((size_t)K);
+  for (int64_t m = 0; m < M; ++m) {
+    long double ss = 0.0L;
+    for (int64_t k = 0; k < K; ++k) {
+      const long double v = load(x, dt, m * K + k);
+      ss += v * v;
+    }
+    const long double rstd = 1.0L / std::sqrt(ss / (long double)K + (long double)eps);
+    for (int64_t k = 0; k < K; ++k) {
+      const double xv = load(x, dt, m * K + k);
+      const double wv = w_norm ? load(w_norm, dt, k) : 1.0;
+      // fused: the operand is x * w in dt; eager: the stored RMSNorm output
+      a[k] = eager ? round_to((double)((long double)xv * rstd * (long double)wv), f)
+                   : round_to(xv * wv, f);
+    }
+    for (int64_t n = 0; n < N; ++n) {
+      long double acc = 0.0L, mag = 0.0L;
+      for (int64_t k = 0; k < K; ++k) {
+        const long double t = (long double)a[k] * (long double)load(Wt, dt, n * K + k);
+        acc += t;
+        mag += t < 0 ? -t : t;
+      }
+      const long double b = bias ? (long double)load(bias, dt, n) : 0.0L;
+      double e;
+      if (!eager) {
+        e = (double)(sc * (rstd * acc + b));
+        if (cond) cond[m * N + n] = (double)(std::fabs(sc) * rstd * mag);
+      } else {
+        const double z = round_to((double)(acc + b), f);
+        e = (double)(sc * (long double)z);
+        if (cond) cond[m * N + n] = (double)(std::fabs(sc) * mag);
+      }
+      if (exact) exact[m * N + n] = e;
+      store(out, dt, m * N + n, round_to(e, f));
+    }
+  }
+  return 0;
+}
+
 int oracle_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64_t H,
                            int64_t W, int64_t groups, int layout, int elem_bytes) {
   if (!in || !out || N < 0 || C < 0 || H < 0 || W < 0 || groups <= 0 || elem_bytes < 1 ||

@@ -126,6 +126,26 @@ int oracle_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n
 int oracle_rope_inv_freq(float base, int head_dim, float* inv);
 
 /*
+ * RMSNorm + linear + scale (TeleTron write-up, 2kiu.com/news/5927820, section
+ * 4.2: the row's RMS scale factor is computed inside the kernel and used
+ * directly in the linear layer's accumulation, so no normalised tensor is
+ * stored; section 3.1: a norm followed by a projection). x [M, K], w_norm [K]
+ * (NULL: weight 1), Wt [N, K] (the linear weight with K contiguous: out = y
+ * Wt^T), bias [N] (NULL: 0), out [M, N], all of dt:
+ *   rstd_m = 1 / sqrt(mean_k x_mk^2 + eps)
+ *   a_mk   = round_dt(x_mk * w_k)       (the linear layer's operand, in dt)
+ *   out_mn = round_dt(scale * (rstd_m * sum_k a_mk * Wt_nk + bias_n))
+ * eager = 1: the unfused form, three stored steps: y = round_dt(x rstd w);
+ * z = round_dt(sum_k y_mk Wt_nk + bias_n); out = round_dt(scale * z).
+ * exact: optional [M, N] unrounded values. cond: optional [M, N]
+ * |scale| * rstd_m * sum_k |a_mk Wt_nk| (the size of the dot product's terms,
+ * which bounds what a different summation order can change).
+ */
+int oracle_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, const void* bias,
+                          void* out, int64_t M, int64_t N, int64_t K, float eps, float scale,
+                          int dt, int eager, double* exact, double* cond);
+
+/*
  * ChannelShuffle (runtime page "CUDA算子与AI运行时", gtnt.cn/news/145880,
  * section 2: the channels of an [N, C, H, W] tensor viewed as [groups,
  * C/groups], the two axes swapped, viewed back as C channels). Output channel
