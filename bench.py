@@ -79,6 +79,7 @@ def rope_bytes(T, H, D, es=2):
 # kernel (static count of its gfx950 code, one side of tanh's branch): the
 # fallback when no rocprofv3 SQ_INSTS_VALU count for the current sources exists.
 VALU_SLOTS = {0: 1, 1: 2, 2: 2, 3: 1, 4: 1, 5: 1, 6: 1, 7: 8, 8: 7, 9: 10, 10: 2, 11: 2}
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 VALU_PEAK = 256 * 64 * 2.4e9  # lane-instr/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
 
 
@@ -108,6 +109,7 @@ KERNEL_SOURCES = {
     "tr": ["norm_pass_amd/csrc/layout.hip", "norm_pass_amd/csrc/device.h"],
     "shuffle_nchw": ["norm_pass_amd/csrc/layout.hip", "norm_pass_amd/csrc/device.h"],
     "shuffle_nhwc": ["norm_pass_amd/csrc/layout.hip", "norm_pass_amd/csrc/device.h"],
+    "rl": ["norm_pass_amd/csrc/rmsnorm_linear.hip", "norm_pass_amd/csrc/device.h"],
 }
 
 
@@ -361,6 +363,27 @@ def build_workloads(torch, npa, synth, quick: bool):
                    "(not in the step; baseline: naive strided copy)",
                xs, "f16", shp, "fuse_channel_shuffle", "naive_channel_shuffle", (g, lay), tf,
                "tr_items<16>" if lay == 0 else "tr_small<2, true>")
+    # RMSNorm + linear + scale on the matrix cores (not in the step): fused
+    # kernel vs RMSNorm -> GEMM + bias -> scale, and torch's bf16 linear
+    # (the vendor GEMM) on the stored RMSNorm output, for context
+    M_, K_, N_ = synth.RMS_LINEAR_SHAPE
+    if quick:
+        M_ = 2048
+    xr, wr, Wr, br = (tdev(a_, "bf16") for a_ in synth.rmsnorm_linear_inputs((M_, K_, N_)))
+    orl = torch.empty((M_, N_), dtype=torch.bfloat16, device=dev)
+    wsr = torch.empty(npa.rmsnorm_linear_workspace_bytes(M_, K_), dtype=torch.uint8, device=dev)
+    yr = torch.empty((M_, K_), dtype=torch.bfloat16, device=dev)
+    npa.fuse_add_rmsnorm(xr, None, wr, None, yr, 1e-6)
+    sc = synth.RMS_LINEAR_SCALE
+    W["rl"] = dict(
+        desc=f"bf16 RMSNorm + linear + scale, x [{M_}, {K_}] x Wt [{N_}, {K_}]^T (not in the step)",
+        fused=npa.bind("fuse_rmsnorm_linear", xr, wr, Wr, br, orl, 1e-6, sc),
+        unfused=npa.bind("unfused_rmsnorm_linear", xr, wr, Wr, br, orl, wsr, 1e-6, sc),
+        unfused_spec=("unfused_rmsnorm_linear", (xr, wr, Wr, br, orl, wsr, 1e-6, sc)),
+        torch=lambda: torch.nn.functional.linear(yr, Wr, br).mul_(sc),
+        plan=None, bytes=2 * (M_ * K_ + N_ * K_ + M_ * N_ + K_ + N_),
+        unfused_bytes=2 * (3 * M_ * K_ + N_ * K_ + 3 * M_ * N_ + K_ + N_),
+        flops=2 * M_ * N_ * K_, launches=3, kernel="rms_linear_mfma")
     W["_compile_ms"] = compile_ms
     return W
 
@@ -529,7 +552,15 @@ def main(argv=None):
         if "torch" in w:
             t_med, _, _ = time_calls(torch, w["torch"], reps, max(5, args.trials // 2))
             per[k]["torch_us_med"] = round(t_med * 1e6, 3)
-            per[k]["plan"] = w["plan"]
+            if w.get("plan") is not None:
+                per[k]["plan"] = w["plan"]
+        if "flops" in w:
+            tf = w["flops"] / f_med / 1e12
+            per[k]["TFLOPs"] = round(tf, 1)
+            per[k]["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+            per[k]["unfused"]["TFLOPs"] = round(w["flops"] / u_med / 1e12, 1)
+            if "torch_us_med" in per[k]:
+                per[k]["torch_TFLOPs"] = round(w["flops"] / (per[k]["torch_us_med"] * 1e-6) / 1e12, 1)
         log(f"[bench] {k}: fused {f_med * 1e6:.2f} us ({gbps:.0f} GB/s), "
             f"unfused {u_med * 1e6:.2f} us x{w['launches']} launches "
             f"(graph {g_med * 1e6:.2f} us)"

@@ -264,6 +264,39 @@ int unfused_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int 
  * the per-launch cost, the NaiveRT write-up's "29 empty calls"). */
 int np_empty_launches(int count, hipStream_t stream);
 
+/*
+ * fuse_rmsnorm_linear: RMSNorm + linear + scale in one matrix-core kernel
+ * (TeleTron write-up, section 4.2: the row's RMS factor is computed in the
+ * kernel and used directly in the linear layer's accumulation, bias and an
+ * elementwise scale follow, and no normalised tensor is stored). Row-major,
+ * dt = NP_BF16 or NP_F16:
+ *   x [M, K], w_norm [K] (NULL: weight 1), Wt [N, K] (the linear weight with K
+ *   contiguous, i.e. out = y Wt^T as a torch Linear stores it), bias [N]
+ *   (NULL: 0), out [M, N]:
+ *   rstd_m = 1 / sqrt(mean_k x_mk^2 + eps)
+ *   out_mn = scale * (rstd_m * sum_k round_dt(x_mk w_k) Wt_nk + bias_n)
+ *   (the product x w is rounded to dt once, as the matrix cores take dt
+ *   operands; the sums are fp32).
+ * Limits: K a multiple of 8; M, N, K < 2^31; x, Wt, w_norm 16-byte aligned.
+ * M = 0 is a no-op that touches no buffer.
+ * Errors: NP_EINVAL for another dtype, bad sizes or alignment, NULL x / Wt /
+ * out, eps not finite and > 0, scale not finite, out overlapping an input.
+ */
+int fuse_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, const void* bias,
+                        void* out, int64_t M, int64_t N, int64_t K, float eps, float scale,
+                        np_dtype dt, hipStream_t stream);
+
+/*
+ * unfused_rmsnorm_linear: the same three steps as separate launches: RMSNorm
+ * (y = x rstd w rounded to dt, stored in the workspace, >= M * K * 2 bytes,
+ * 16-byte aligned); the linear layer with its bias (same matrix-core GEMM,
+ * result rounded to dt into out); the scale (out = scale * out in dt).
+ */
+int unfused_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, const void* bias,
+                           void* out, int64_t M, int64_t N, int64_t K, float eps, float scale,
+                           np_dtype dt, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* ---- layout: strided transpose and ChannelShuffle --------------------------
  *
  * The runtime page "CUDA算子与AI运行时" (gtnt.cn/news/145880), sections 2 and

@@ -63,6 +63,8 @@ def _load():
         "unfused_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I, P, S, P],
         "unfused_qkv_rope": [P, P, P, P, I64, I, I, P, F, F, I, P],
         "np_empty_launches": [I, P],
+        "fuse_rmsnorm_linear": [P, P, P, P, P, I64, I64, I64, F, F, I, P],
+        "unfused_rmsnorm_linear": [P, P, P, P, P, I64, I64, I64, F, F, I, P, S, P],
         "fuse_transpose021": [P, P, I64, I64, I64, I64, I, P],
         "naive_transpose021": [P, P, I64, I64, I64, I64, I, P],
         "fuse_channel_shuffle": [P, P, I64, I64, I64, I64, I64, I, I, P],
@@ -227,6 +229,20 @@ _a_unfused_chain = _a_fuse_chain
 _a_unfused_qkv_rope = _a_fuse_qkv_rope
 
 
+def _a_fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps: float = 1e-6, scale: float = 1.0,
+                           stream=None):
+    _keep(stream, x, w_norm, Wt, bias, out)
+    return (_ptr(x), _ptr(w_norm), _ptr(Wt), _ptr(bias), _ptr(out), x.shape[0], Wt.shape[0],
+            x.shape[-1], eps, scale, dtype_code(x), _stream(stream))
+
+
+def _a_unfused_rmsnorm_linear(x, w_norm, Wt, bias, out, workspace, eps: float = 1e-6,
+                              scale: float = 1.0, stream=None):
+    a = _a_fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps, scale, stream)
+    _keep(stream, workspace)
+    return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
+
+
 def _dense(*ts):
     for t in ts:
         if not t.is_contiguous():
@@ -345,6 +361,27 @@ def fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps: float = 1e-5, stream=
     _check(_lib.fuse_add_layernorm(*_a_fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps,
                                                           stream)), "fuse_add_layernorm")
     return h_out, out
+
+
+def fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps: float = 1e-6, scale: float = 1.0,
+                        stream=None):
+    """out = scale * (Linear(RMSNorm(x)) + bias) with the RMS factor applied to the
+    accumulator: x [M, K], w_norm [K] or None, Wt [N, K], bias [N] or None, out [M, N]."""
+    _check(_lib.fuse_rmsnorm_linear(*_a_fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps, scale,
+                                                            stream)), "fuse_rmsnorm_linear")
+    return out
+
+
+def rmsnorm_linear_workspace_bytes(M: int, K: int) -> int:
+    return M * K * 2
+
+
+def unfused_rmsnorm_linear(x, w_norm, Wt, bias, out, workspace, eps: float = 1e-6,
+                           scale: float = 1.0, stream=None):
+    _check(_lib.unfused_rmsnorm_linear(*_a_unfused_rmsnorm_linear(x, w_norm, Wt, bias, out,
+                                                                  workspace, eps, scale, stream)),
+           "unfused_rmsnorm_linear")
+    return out
 
 
 def fuse_transpose021(x, out, shape=None, stream=None):

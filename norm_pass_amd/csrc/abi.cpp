@@ -360,6 +360,32 @@ int run_transpose(const void* in, void* out, int64_t B, int64_t R, int64_t S, in
   return ok();
 }
 
+int validate_rms_linear(const void* x, const void* w, const void* Wt, const void* b,
+                        const void* out, int64_t M, int64_t N, int64_t K, float eps, float scale,
+                        int dt) {
+  if (dt != NP_BF16 && dt != NP_F16)
+    return fail(NP_EINVAL, "rmsnorm_linear takes fp16 or bf16 (the matrix-core operand types)");
+  if (M < 0 || M >= ((int64_t)1 << 31)) return fail(NP_EINVAL, "M = %lld out of range", (long long)M);
+  if (N < 1 || N >= ((int64_t)1 << 31)) return fail(NP_EINVAL, "N = %lld out of range", (long long)N);
+  if (K < 8 || K >= ((int64_t)1 << 31) || K % 8 != 0)
+    return fail(NP_EINVAL, "K = %lld must be a multiple of 8, >= 8", (long long)K);
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(NP_EINVAL, "eps must be finite and > 0");
+  if (!std::isfinite(scale)) return fail(NP_EINVAL, "scale must be finite");
+  if (M == 0) return NP_OK;  // nothing to compute: no buffer is touched
+  if (!x || !Wt || !out) return fail(NP_EINVAL, "NULL x, Wt or out");
+  if (!aligned16(x) || !aligned16(Wt) || (w && !aligned16(w)))
+    return fail(NP_EINVAL, "x, Wt and w_norm must be 16-byte aligned");
+  const uint64_t es = 2, o = (uint64_t)(uintptr_t)out, ob = (uint64_t)M * N * es;
+  auto overlaps = [&](const void* p, uint64_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    return p && a < o + ob && o < a + bytes;
+  };
+  if ((overlaps(x, (uint64_t)M * K * es) || overlaps(Wt, (uint64_t)N * K * es) ||
+                overlaps(w, (uint64_t)K * es) || overlaps(b, (uint64_t)N * es)))
+    return fail(NP_EINVAL, "out overlaps an input");
+  return NP_OK;
+}
+
 int shuffle_shape(int64_t N, int64_t C, int64_t H, int64_t W, int64_t groups, int layout,
                   int64_t* B, int64_t* R, int64_t* S, int64_t* E) {
   if (N < 0 || C < 0 || H < 0 || W < 0)
@@ -700,6 +726,42 @@ int naive_channel_shuffle(const void* in, void* out, int64_t N, int64_t C, int64
   int rc = shuffle_shape(N, C, H, W, groups, layout, &B, &R, &S, &E);
   if (rc) return rc;
   return run_transpose(in, out, B, R, S, E, elem_bytes, true, stream, "naive_channel_shuffle");
+}
+
+int fuse_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, const void* bias,
+                        void* out, int64_t M, int64_t N, int64_t K, float eps, float scale,
+                        np_dtype dt, hipStream_t stream) {
+  int rc = validate_rms_linear(x, w_norm, Wt, bias, out, M, N, K, eps, scale, dt);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  if ((rc = check_device())) return rc;
+  hipError_t e = np::launch_rmsnorm_linear(x, w_norm, Wt, bias, out, (int)M, (int)N, (int)K, eps,
+                                           scale, dt, true, stream);
+  if (e != hipSuccess) return hip_fail(e, "fuse_rmsnorm_linear");
+  return ok();
+}
+
+int unfused_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, const void* bias,
+                           void* out, int64_t M, int64_t N, int64_t K, float eps, float scale,
+                           np_dtype dt, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  int rc = validate_rms_linear(x, w_norm, Wt, bias, out, M, N, K, eps, scale, dt);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  const uint64_t need = (uint64_t)M * K * 2;
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(NP_EINVAL, "workspace needs %llu bytes, 16-byte aligned",
+                (unsigned long long)need);
+  if ((rc = check_device())) return rc;
+  // RMSNorm -> y (stored); GEMM + bias -> out; scale -> out
+  hipError_t e = np::launch_add_rmsnorm(x, nullptr, w_norm, nullptr, workspace, M, K, eps, dt,
+                                        true, stream);
+  if (e == hipSuccess)
+    e = np::launch_rmsnorm_linear(workspace, nullptr, Wt, bias, out, (int)M, (int)N, (int)K, eps,
+                                  1.0f, dt, false, stream);
+  if (e == hipSuccess) e = np::launch_unary(NP_MUL_C, scale, out, out, M * N, dt, stream);
+  if (e != hipSuccess) return hip_fail(e, "unfused_rmsnorm_linear");
+  return ok();
 }
 
 int np_transpose_plan(const void* in, const void* out, int64_t B, int64_t R, int64_t S,

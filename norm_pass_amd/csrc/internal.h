@@ -51,6 +51,11 @@ hipError_t launch_add_layernorm(const void* x, const void* r, const void* g, con
                                 void* h, void* out, int64_t rows, int64_t cols, float eps, int dt,
                                 bool vec, hipStream_t s);
 
+// RMSNorm + linear + scale (matrix cores); norm = false: plain GEMM + bias
+hipError_t launch_rmsnorm_linear(const void* x, const void* w, const void* Wt, const void* b,
+                                 void* out, int M, int N, int K, float eps, float scale, int dt,
+                                 bool norm, hipStream_t s);
+
 // QKV split + RoPE + scale
 struct RopeArgs {
   const void* qkv;

@@ -259,3 +259,24 @@ def shuffle_inputs(shape=SHUFFLE_NCHW, seed: int = 1007, dtype: str = "f16", lay
     NHWC (layout 1)."""
     n, c, h, w = shape
     return normal((n, c, h, w) if layout == 0 else (n, h, w, c), seed, dtype)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm + linear + scale (the TeleTron write-up, section 4.2): the norm of
+# the residual-add workload (16384 tokens x hidden 4096) followed by a square
+# 4096 -> 4096 projection, bf16 storage.
+# --------------------------------------------------------------------------
+
+RMS_LINEAR_SHAPE = (16384, 4096, 4096)  # M tokens, K hidden in, N out
+RMS_LINEAR_SCALE = 0.5
+
+
+def rmsnorm_linear_inputs(shape=RMS_LINEAR_SHAPE, seed: int = 1008, dtype: str = "bf16"):
+    """x [M, K] ~ N(0, 1); w_norm [K] ~ N(1, 0.1^2); Wt [N, K] ~ N(0, 1/K)
+    (unit-variance outputs); bias [N] ~ N(0, 0.1^2)."""
+    M, K, N = shape
+    x = normal((M, K), seed, dtype)
+    w = normal((K,), seed + 1, dtype, mean=1.0, std=0.1)
+    Wt = normal((N, K), seed + 2, dtype, std=K ** -0.5)
+    b = normal((N,), seed + 3, dtype, std=0.1)
+    return x, w, Wt, b

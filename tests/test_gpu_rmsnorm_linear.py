@@ -1,0 +1,138 @@
+"""GPU parity of fuse_rmsnorm_linear / unfused_rmsnorm_linear against the
+oracle (TeleTron write-up, section 4.2: RMSNorm + linear + scale in one
+kernel, the RMS factor applied to the linear layer's accumulation).
+
+Tolerance, from the arithmetic: the kernel forms the dt operand x*w exactly as
+the oracle does (an exact product rounded once), accumulates the K products in
+fp32 on the matrix cores in its own order, and applies rstd, bias and scale
+in fp32. Its fp32 value can differ from the exact one by at most
+2^-24 (K + 16) times the magnitude |scale| rstd sum|a W| of the terms, and the
+final rounding adds at most one ulp of the output type; every element must
+lie within that, and at least 99.5 % of the elements must equal the oracle's
+rounded value bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import ORACLE_DT, empty, need_gpu, to_dev, to_host
+from tolerance import bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def npa():
+    need_gpu()
+    import norm_pass_amd
+    norm_pass_amd.np_init(0)
+    return norm_pass_amd
+
+
+def _vals(bits, dt):
+    return bf16_bits_to_f32(bits).astype(np.float64) if dt == "bf16" else \
+        bits.view(np.float16).astype(np.float64)
+
+
+def _ulp(v, dt):
+    mant = 7 if dt == "bf16" else 10
+    emin = -126 if dt == "bf16" else -14
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
+    return 2.0 ** (e - mant)
+
+
+def _inputs(M, K, N, seed, dt):
+    x = synth.normal((M, K), seed, dt)
+    w = synth.normal((K,), seed + 1, dt, mean=1.0, std=0.1)
+    Wt = synth.normal((N, K), seed + 2, dt, std=K ** -0.5)
+    b = synth.normal((N,), seed + 3, dt, std=0.1)
+    return x, w, Wt, b
+
+
+def _check(got, exact, cond, K, dt, min_equal=0.995, want_bits=None):
+    g = _vals(got, dt)
+    err = np.abs(g - exact)
+    lim = _ulp(exact, dt) + 2.0 ** -24 * (K + 16) * cond
+    bad = err > lim
+    assert not bad.any(), (int(bad.sum()), float((err - lim).max()))
+    if want_bits is not None:
+        assert (got == want_bits).mean() >= min_equal, float((got == want_bits).mean())
+
+
+CASES = [  # M, N, K
+    (256, 256, 512), (300, 260, 520), (1, 1, 8), (129, 130, 72), (64, 384, 1024), (517, 33, 136),
+]
+
+
+@pytest.mark.parametrize("M,N,K", CASES)
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("with_w,with_b,scale", [(True, True, 0.5), (False, False, 1.0),
+                                                 (True, False, -2.0)])
+def test_fused_matches_oracle(npa, orc, M, N, K, dt, with_w, with_b, scale):
+    x, w, Wt, b = _inputs(M, K, N, 4000 + M + N + K, dt)
+    w = w if with_w else None
+    b = b if with_b else None
+    want, exact, cond = orc.rmsnorm_linear(x, w, Wt, b, 1e-6, scale, ORACLE_DT[dt],
+                                           want_exact=True)
+    out = empty((M, N), dt)
+    npa.fuse_rmsnorm_linear(to_dev(x, dt), None if w is None else to_dev(w, dt), to_dev(Wt, dt),
+                            None if b is None else to_dev(b, dt), out, 1e-6, scale)
+    torch.cuda.synchronize()
+    _check(to_host(out), exact, cond, K, dt, want_bits=want)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 260, 520)])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_unfused_matches_oracle_eager(npa, orc, M, N, K, dt):
+    x, w, Wt, b = _inputs(M, K, N, 5000 + M, dt)
+    want, exact, cond = orc.rmsnorm_linear(x, w, Wt, b, 1e-6, 0.5, ORACLE_DT[dt], eager=True,
+                                           want_exact=True)
+    out = empty((M, N), dt)
+    ws = torch.empty(npa.rmsnorm_linear_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+    npa.unfused_rmsnorm_linear(to_dev(x, dt), to_dev(w, dt), to_dev(Wt, dt), to_dev(b, dt), out,
+                               ws, 1e-6, 0.5)
+    torch.cuda.synchronize()
+    # the unfused GEMM's operand y = round(x rstd w) is computed with the fp32
+    # rstd of the RMSNorm kernel: a y element may round the other way than the
+    # oracle's (one ulp of y), which moves the sum by up to 2^-8 of one term
+    g = _vals(to_host(out), dt)
+    lim = 2 * _ulp(exact, dt) + 2.0 ** -24 * (K + 16) * cond + 2.0 ** -8 * cond / np.sqrt(K)
+    assert (np.abs(g - exact) <= lim).all()
+    assert (to_host(out) == want).mean() > 0.98
+
+
+def test_full_size_sampled_rows(npa, orc):
+    """The bench's workload (bf16, M 16384, K 4096, N 4096) in the bench's
+    launch, sampled rows (all their 4096 outputs) against the oracle."""
+    M, K, N = 16384, 4096, 4096
+    x, w, Wt, b = synth.rmsnorm_linear_inputs()
+    out = empty((M, N), "bf16")
+    npa.fuse_rmsnorm_linear(to_dev(x, "bf16"), to_dev(w, "bf16"), to_dev(Wt, "bf16"),
+                            to_dev(b, "bf16"), out, 1e-6, synth.RMS_LINEAR_SCALE)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(17)
+    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.integers(0, M, 12)]))
+    want, exact, cond = orc.rmsnorm_linear(x[rows], w, Wt, b, 1e-6, synth.RMS_LINEAR_SCALE,
+                                           ORACLE_DT["bf16"], want_exact=True)
+    got = to_host(out[torch.from_numpy(rows).cuda()])
+    _check(got, exact, cond, K, "bf16", want_bits=want)
+
+
+def test_empty_and_rejects(npa):
+    x = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    Wt = torch.zeros(32, 64, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(0, 32, dtype=torch.bfloat16, device="cuda")
+    npa.fuse_rmsnorm_linear(x, None, Wt, None, out)  # M = 0: nothing to do
+    x = torch.zeros(4, 64, dtype=torch.float32, device="cuda")
+    with pytest.raises(npa.NPError):
+        npa.fuse_rmsnorm_linear(x, None, Wt.float(), None, torch.zeros(4, 32, device="cuda"))
+    xb = torch.zeros(4, 60, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(npa.NPError):  # K % 8 != 0
+        npa.fuse_rmsnorm_linear(xb, None, torch.zeros(32, 60, dtype=torch.bfloat16,
+                                                      device="cuda"),
+                                None, torch.zeros(4, 32, dtype=torch.bfloat16, device="cuda"))
+    buf = torch.zeros(4 * 64 + 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(npa.NPError):  # misaligned x
+        npa.fuse_rmsnorm_linear(buf[1:1 + 256].view(4, 64), None, Wt, None,
+                                torch.zeros(4, 32, dtype=torch.bfloat16, device="cuda"))
