@@ -11,14 +11,16 @@
 // squares; the epilogue scales the accumulator by rstd. x is read exactly as
 // a plain GEMM reads its A operand; there is no separate norm pass.
 //
-// Tiles: 128 x 128 outputs per 256-thread workgroup, K in steps of 64 (a
-// partial last step reads zeros); each wave owns 64 x 64 outputs as 2 x 2
-// blocks of v_mfma_f32_32x32x16 (bf16 or f16 inputs, fp32 accumulation).
+// Tiles: 256 x 256 outputs per 256-thread workgroup (one per CU: the two LDS
+// stages take 144 KiB of gfx950's 160 KiB), K in steps of 64 (a partial last
+// step reads zeros); each wave owns 128 x 128 outputs as 4 x 4 blocks of
+// v_mfma_f32_32x32x16 (bf16 or f16 inputs, fp32 accumulation).
 // Operand layout of that instruction: lane l supplies A[l % 32][8 (l / 32) ..
 // + 8] and B[8 (l / 32) .. + 8][l % 32] (16 contiguous bytes of a K-contiguous
 // row each); accumulator register j of lane l is C[8 (j / 4) + 4 (l / 32) +
-// j % 4][l % 32]. The next K step's global loads are issued before the current
-// step's MFMAs, so they are in flight while the matrix cores run.
+// j % 4][l % 32]. The loads of K step s + 2 are issued right after step s + 1
+// is staged, so they are in flight while the matrix cores run step s + 1; the
+// epilogue rounds the tile into LDS and writes 16-byte rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,64 +50,89 @@ struct Mfma<_Float16> {
   }
 };
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int PITCH = BK + 8;  // elements; 144-byte LDS rows keep 8 lanes' 16-byte reads in distinct banks
-constexpr int NTHR = 256;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int PITCH = BK + 8;  // elements: 144-byte LDS rows keep 8 lanes' 16-byte reads in distinct banks
+constexpr int NTHR = 256;      // 4 waves, each 128 x 128 outputs = 4 x 4 MFMA blocks
+constexpr int STAGE = (BM + BN) * PITCH;  // elements per LDS stage (A then B)
+constexpr int CPITCH = BN + 8;            // elements per row of the epilogue's output tile
+constexpr int SMEM = 2 * STAGE * 2;       // bytes: two stages (147,456); the output tile reuses them
+static_assert(BM * CPITCH * 2 <= SMEM, "epilogue tile must fit in the stage buffers");
+constexpr int GROUP_M = 4;  // tiles of 4 row blocks x all column blocks are taken together
+
+// Workgroups are dispatched round robin to the 8 XCDs (each with its own L2):
+// give XCD x a contiguous run of tiles so that the workgroups sharing an L2 also
+// share A and B panels.
+__device__ __forceinline__ int xcd_tile(int bid, int nb) {
+  const int x = bid & 7, j = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return x * per + min(x, rem) + j;
+}
 
 // NORM: accumulate sum of squares and scale by rstd (fused form); otherwise a
 // plain GEMM with bias (the unfused form's linear layer). HAS_W: multiply the
 // A operand by the norm weight on its way to LDS.
 template <typename T, bool NORM, bool HAS_W, bool HAS_B>
-__global__ __launch_bounds__(NTHR) void rms_linear_mfma(const T* __restrict__ x,
-                                                        const T* __restrict__ w,
-                                                        const T* __restrict__ Wt,
-                                                        const T* __restrict__ bias,
-                                                        T* __restrict__ out, int M, int N, int K,
-                                                        float eps, float scale) {
+__global__ __launch_bounds__(NTHR, 1) void rms_linear_mfma(const T* __restrict__ x,
+                                                           const T* __restrict__ w,
+                                                           const T* __restrict__ Wt,
+                                                           const T* __restrict__ bias,
+                                                           T* __restrict__ out, int M, int N,
+                                                           int K, float eps, float scale,
+                                                           int tiles_m, int tiles_n, int vec_out) {
   typedef typename Mfma<T>::v8 v8;
-  __shared__ __attribute__((aligned(16))) T As[BM * PITCH];
-  __shared__ __attribute__((aligned(16))) T Bs[BN * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ float rstd_s[BM];
+  T* const lds = reinterpret_cast<T*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  // staging map: vector i of this thread is row tid / 8 + 32 i, k chunk tid % 8
+  // output tile of this workgroup
+  const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  const int per_group = GROUP_M * tiles_n;
+  const int g = t / per_group, within = t - g * per_group;
+  const int gsz = min(GROUP_M, tiles_m - g * GROUP_M);
+  const int m0 = (g * GROUP_M + within % gsz) * BM, n0 = (within / gsz) * BN;
+  // staging map: vector i of this thread is row srow + 32 i, k chunk kc
   const int srow = tid >> 3, kc = (tid & 7) * 8;
-  const T* xrow[4];
-  const T* brow[4];
-  bool mval[4], nval[4];
+  unsigned mval = 0, nval = 0;  // bit i: row srow + 32 i is inside M / N
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + srow + 32 * i, gn = n0 + srow + 32 * i;
-    mval[i] = gm < M;
-    nval[i] = gn < N;
-    xrow[i] = x + (int64_t)(mval[i] ? gm : M - 1) * K;  // clamped: always a valid row
-    brow[i] = Wt + (int64_t)(nval[i] ? gn : N - 1) * K;
+  for (int i = 0; i < 8; ++i) {
+    mval |= (unsigned)(m0 + srow + 32 * i < M) << i;
+    nval |= (unsigned)(n0 + srow + 32 * i < N) << i;
   }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 xa[4], xb[4], wa = zero;
+  u32x4 xa[8], xb[8], wa = {0u, 0u, 0u, 0u};
   auto load_step = [&](int k0) {
     const int gk = k0 + kc;
     const bool kval = gk < K;  // K % 8 == 0: a vector is wholly inside or outside
     const int lk = kval ? gk : 0;
+    // every load is issued unconditionally from a clamped (in-bounds) address
+    // and masked afterwards: a branch around a load would serialise them
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 va = load_raw(xrow[i] + lk);
-      const u32x4 vb = load_raw(brow[i] + lk);
-      xa[i] = (kval && mval[i]) ? va : zero;
-      xb[i] = (kval && nval[i]) ? vb : zero;
+    for (int i = 0; i < 8; ++i) {
+      const int gm = min(m0 + srow + 32 * i, M - 1), gn = min(n0 + srow + 32 * i, N - 1);
+      xa[i] = load_raw(x + (int64_t)gm * K + lk);
+      xb[i] = load_raw(Wt + (int64_t)gn * K + lk);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xa[i] &= (uint32_t)(-(int32_t)(kval && ((mval >> i) & 1)));
+      xb[i] &= (uint32_t)(-(int32_t)(kval && ((nval >> i) & 1)));
     }
     if (HAS_W) wa = load_raw(w + lk);
   };
-  float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto store_step = [&]() {
+  float ss[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) ss[i] = 0.0f;
+  auto store_step = [&](int buf) {
+    T* As = lds + buf * STAGE;
+    T* Bs = As + BM * PITCH;
+    T wv[8];
+    if (HAS_W) __builtin_memcpy(wv, &wa, 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
       u32x4 av = xa[i];
       if (NORM || HAS_W) {
-        T e[8], wv[8];
+        T e[8];
         __builtin_memcpy(e, &xa[i], 16);
-        if (HAS_W) __builtin_memcpy(wv, &wa, 16);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float f = to_f(e[j]);
@@ -118,66 +145,93 @@ __global__ __launch_bounds__(NTHR) void rms_linear_mfma(const T* __restrict__ x,
       *reinterpret_cast<u32x4*>(&Bs[(srow + 32 * i) * PITCH + kc]) = xb[i];
     }
   };
-  f32x16 acc[2][2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int ksteps = (K + BK - 1) / BK;
-  load_step(0);
-  const int arow = wm * 64 + (lane & 31), brw = wn * 64 + (lane & 31), kl = (lane >> 5) * 8;
-  for (int t = 0; t < ksteps; ++t) {
-    __syncthreads();  // the previous step's MFMA operands have been read
-    store_step();
-    __syncthreads();
-    if (t + 1 < ksteps) load_step((t + 1) * BK);  // in flight during the MFMAs below
+  const int arow = wm * 128 + (lane & 31), brw = wn * 128 + (lane & 31), kl = (lane >> 5) * 8;
+  auto compute = [&](int buf) {
+    const T* As = lds + buf * STAGE;
+    const T* Bs = As + BM * PITCH;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      v8 a[2], b[2];
+      v8 a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const u32x4 ra = *reinterpret_cast<const u32x4*>(&As[(arow + 32 * i) * PITCH + ks * 16 + kl]);
         const u32x4 rb = *reinterpret_cast<const u32x4*>(&Bs[(brw + 32 * i) * PITCH + ks * 16 + kl]);
         __builtin_memcpy(&a[i], &ra, 16);
         __builtin_memcpy(&b[i], &rb, 16);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = Mfma<T>::run(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::run(a[i], b[j], acc[i][j]);
     }
+  };
+
+  // two LDS stages: step s computes from stage s & 1 while the loads of step
+  // s + 1 (issued a step earlier) land in registers and then in the other stage
+  // The loop body has no branch, so the compiler can interleave the staging
+  // (VALU, LDS stores, global loads) with the asynchronous MFMAs; loads past
+  // the end of K read clamped addresses and are masked to zero.
+  const int ksteps = (K + BK - 1) / BK;
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  load_step(BK);
+  for (int s = 0; s + 1 < ksteps; ++s) {
+    compute(s & 1);
+    store_step((s + 1) & 1);
+    load_step((s + 2) * BK);
+    __syncthreads();
   }
+  compute((ksteps - 1) & 1);
+  __syncthreads();
   // rstd per row: the 8 lanes that staged a row hold its partial sums
   if (NORM) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       float v = ss[i];
       v += __shfl_xor(v, 1);
       v += __shfl_xor(v, 2);
       v += __shfl_xor(v, 4);
       if ((tid & 7) == 0) rstd_s[srow + 32 * i] = 1.0f / sqrtf(v / (float)K + eps);
     }
+    __syncthreads();
   }
-  __syncthreads();
+  // epilogue: rstd, bias, scale in fp32, rounded to T into an LDS tile, then
+  // written out as 16-byte rows
+  T* const cs = lds;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int gn = n0 + wn * 64 + j * 32 + (lane & 31);
-    if (gn >= N) continue;
-    const float bv = HAS_B ? to_f(bias[gn]) : 0.0f;
+  for (int j = 0; j < 4; ++j) {
+    const int col = wn * 128 + j * 32 + (lane & 31);
+    const float bv = (HAS_B && n0 + col < N) ? to_f(bias[n0 + col]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int gm = m0 + row;
-        if (gm < M) {
-          const float rs = NORM ? rstd_s[row] : 1.0f;
-          out[(int64_t)gm * N + gn] = from_f<T>(scale * __builtin_fmaf(rs, acc[i][j][r], bv));
-        }
+        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const float rs = NORM ? rstd_s[row] : 1.0f;
+        cs[row * CPITCH + col] = from_f<T>(scale * __builtin_fmaf(rs, acc[i][j][r], bv));
       }
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < BM * BN / 8 / NTHR; ++i) {
+    const int v = tid + NTHR * i;
+    const int row = v >> 5, cv = (v & 31) * 8;
+    const int gm = m0 + row, gn = n0 + cv;
+    if (gm >= M) continue;
+    T* dst = out + (int64_t)gm * N + gn;
+    if (vec_out && gn + 8 <= N) {
+      store_raw_nt(dst, *reinterpret_cast<const u32x4*>(&cs[row * CPITCH + cv]));
+    } else {
+      for (int e = 0; e < 8 && gn + e < N; ++e) dst[e] = cs[row * CPITCH + cv + e];
     }
   }
 }
@@ -185,7 +239,9 @@ __global__ __launch_bounds__(NTHR) void rms_linear_mfma(const T* __restrict__ x,
 template <typename T, bool NORM>
 hipError_t launch_t(const void* x, const void* w, const void* Wt, const void* b, void* out,
                     int M, int N, int K, float eps, float scale, hipStream_t s) {
-  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const dim3 grid(tm * tn);
+  const int vec_out = (N % 8 == 0 && ((uintptr_t)out & 15) == 0) ? 1 : 0;
   const T* xp = static_cast<const T*>(x);
   const T* wp = static_cast<const T*>(w);
   const T* Wp = static_cast<const T*>(Wt);
@@ -193,7 +249,7 @@ hipError_t launch_t(const void* x, const void* w, const void* Wt, const void* b,
   T* op = static_cast<T*>(out);
 #define NP_RL(HW, HB)                                                                          \
   hipLaunchKernelGGL((rms_linear_mfma<T, NORM, HW, HB>), grid, dim3(NTHR), 0, s, xp, wp, Wp, bp, \
-                     op, M, N, K, eps, scale)
+                     op, M, N, K, eps, scale, tm, tn, vec_out)
   if (w && b) NP_RL(true, true);
   else if (w) NP_RL(true, false);
   else if (b) NP_RL(false, true);
