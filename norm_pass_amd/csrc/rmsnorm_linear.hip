@@ -11,16 +11,17 @@
 // squares; the epilogue scales the accumulator by rstd. x is read exactly as
 // a plain GEMM reads its A operand; there is no separate norm pass.
 //
-// Tiles: 256 x 256 outputs per 256-thread workgroup (one per CU: the two LDS
-// stages take 144 KiB of gfx950's 160 KiB), K in steps of 64 (a partial last
-// step reads zeros); each wave owns 128 x 128 outputs as 4 x 4 blocks of
-// v_mfma_f32_32x32x16 (bf16 or f16 inputs, fp32 accumulation).
+// Tiles: 256 x 256 outputs per 512-thread workgroup (one per CU: the two LDS
+// stages take 144 KiB of gfx950's 160 KiB; two waves per SIMD, so one wave's
+// MFMAs run while the other waits on LDS or stages data), K in steps of 64 (a
+// partial last step reads zeros); each wave owns 128 x 64 outputs as 4 x 2
+// blocks of v_mfma_f32_32x32x16 (bf16 or f16 inputs, fp32 accumulation).
 // Operand layout of that instruction: lane l supplies A[l % 32][8 (l / 32) ..
 // + 8] and B[8 (l / 32) .. + 8][l % 32] (16 contiguous bytes of a K-contiguous
 // row each); accumulator register j of lane l is C[8 (j / 4) + 4 (l / 32) +
-// j % 4][l % 32]. The loads of K step s + 2 are issued right after step s + 1
-// is staged, so they are in flight while the matrix cores run step s + 1; the
-// epilogue rounds the tile into LDS and writes 16-byte rows.
+// j % 4][l % 32]. The loads of K step s + 2 are issued before the MFMAs of
+// step s, so they are in flight while the matrix cores run; the epilogue
+// rounds the tile into LDS and writes 16-byte rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,11 +53,16 @@ struct Mfma<_Float16> {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int PITCH = BK + 8;  // elements: 144-byte LDS rows keep 8 lanes' 16-byte reads in distinct banks
-constexpr int NTHR = 256;      // 4 waves, each 128 x 128 outputs = 4 x 4 MFMA blocks
+constexpr int NTHR = 512;      // 8 waves (2 per SIMD), each 128 x 64 outputs = 4 x 2 MFMA blocks
+constexpr int WN = 4;          // waves along N (2 along M)
+constexpr int FM = 4, FN = 2;  // 32 x 32 MFMA blocks per wave along M and N
+constexpr int SV = BM * BK / 8 / NTHR;  // 16-byte staging vectors per thread and operand
+constexpr int SROWS = NTHR / 8;         // rows staged per pass
 constexpr int STAGE = (BM + BN) * PITCH;  // elements per LDS stage (A then B)
 constexpr int CPITCH = BN + 8;            // elements per row of the epilogue's output tile
 constexpr int SMEM = 2 * STAGE * 2;       // bytes: two stages (147,456); the output tile reuses them
 static_assert(BM * CPITCH * 2 <= SMEM, "epilogue tile must fit in the stage buffers");
+static_assert(2 * 32 * FM == BM && WN * 32 * FN == BN && SV * SROWS == BM, "tile / wave layout");
 constexpr int GROUP_M = 4;  // tiles of 4 row blocks x all column blocks are taken together
 
 // Workgroups are dispatched round robin to the 8 XCDs (each with its own L2):
@@ -72,7 +78,7 @@ __device__ __forceinline__ int xcd_tile(int bid, int nb) {
 // plain GEMM with bias (the unfused form's linear layer). HAS_W: multiply the
 // A operand by the norm weight on its way to LDS.
 template <typename T, bool NORM, bool HAS_W, bool HAS_B>
-__global__ __launch_bounds__(NTHR, 1) void rms_linear_mfma(const T* __restrict__ x,
+__global__ __launch_bounds__(NTHR) void rms_linear_mfma(const T* __restrict__ x,
                                                            const T* __restrict__ w,
                                                            const T* __restrict__ Wt,
                                                            const T* __restrict__ bias,
@@ -84,22 +90,22 @@ __global__ __launch_bounds__(NTHR, 1) void rms_linear_mfma(const T* __restrict__
   __shared__ float rstd_s[BM];
   T* const lds = reinterpret_cast<T*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   // output tile of this workgroup
   const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
   const int per_group = GROUP_M * tiles_n;
   const int g = t / per_group, within = t - g * per_group;
   const int gsz = min(GROUP_M, tiles_m - g * GROUP_M);
   const int m0 = (g * GROUP_M + within % gsz) * BM, n0 = (within / gsz) * BN;
-  // staging map: vector i of this thread is row srow + 32 i, k chunk kc
+  // staging map: vector i of this thread is row srow + SROWS i, k chunk kc
   const int srow = tid >> 3, kc = (tid & 7) * 8;
-  unsigned mval = 0, nval = 0;  // bit i: row srow + 32 i is inside M / N
+  unsigned mval = 0, nval = 0;  // bit i: row srow + SROWS i is inside M / N
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    mval |= (unsigned)(m0 + srow + 32 * i < M) << i;
-    nval |= (unsigned)(n0 + srow + 32 * i < N) << i;
+  for (int i = 0; i < SV; ++i) {
+    mval |= (unsigned)(m0 + srow + SROWS * i < M) << i;
+    nval |= (unsigned)(n0 + srow + SROWS * i < N) << i;
   }
-  u32x4 xa[8], xb[8], wa = {0u, 0u, 0u, 0u};
+  u32x4 xa[SV], xb[SV], wa = {0u, 0u, 0u, 0u};
   auto load_step = [&](int k0) {
     const int gk = k0 + kc;
     const bool kval = gk < K;  // K % 8 == 0: a vector is wholly inside or outside
@@ -107,28 +113,28 @@ __global__ __launch_bounds__(NTHR, 1) void rms_linear_mfma(const T* __restrict__
     // every load is issued unconditionally from a clamped (in-bounds) address
     // and masked afterwards: a branch around a load would serialise them
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int gm = min(m0 + srow + 32 * i, M - 1), gn = min(n0 + srow + 32 * i, N - 1);
+    for (int i = 0; i < SV; ++i) {
+      const int gm = min(m0 + srow + SROWS * i, M - 1), gn = min(n0 + srow + SROWS * i, N - 1);
       xa[i] = load_raw(x + (int64_t)gm * K + lk);
       xb[i] = load_raw(Wt + (int64_t)gn * K + lk);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < SV; ++i) {
       xa[i] &= (uint32_t)(-(int32_t)(kval && ((mval >> i) & 1)));
       xb[i] &= (uint32_t)(-(int32_t)(kval && ((nval >> i) & 1)));
     }
     if (HAS_W) wa = load_raw(w + lk);
   };
-  float ss[8];
+  float ss[SV];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ss[i] = 0.0f;
+  for (int i = 0; i < SV; ++i) ss[i] = 0.0f;
   auto store_step = [&](int buf) {
     T* As = lds + buf * STAGE;
     T* Bs = As + BM * PITCH;
     T wv[8];
     if (HAS_W) __builtin_memcpy(wv, &wa, 16);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < SV; ++i) {
       u32x4 av = xa[i];
       if (NORM || HAS_W) {
         T e[8];
@@ -141,52 +147,59 @@ __global__ __launch_bounds__(NTHR, 1) void rms_linear_mfma(const T* __restrict__
         }
         if (HAS_W) __builtin_memcpy(&av, e, 16);
       }
-      *reinterpret_cast<u32x4*>(&As[(srow + 32 * i) * PITCH + kc]) = av;
-      *reinterpret_cast<u32x4*>(&Bs[(srow + 32 * i) * PITCH + kc]) = xb[i];
+      *reinterpret_cast<u32x4*>(&As[(srow + SROWS * i) * PITCH + kc]) = av;
+      *reinterpret_cast<u32x4*>(&Bs[(srow + SROWS * i) * PITCH + kc]) = xb[i];
     }
   };
-  f32x16 acc[4][4];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  const int arow = wm * 128 + (lane & 31), brw = wn * 128 + (lane & 31), kl = (lane >> 5) * 8;
+  const int arow = wm * 32 * FM + (lane & 31), brw = wn * 32 * FN + (lane & 31);
+  const int kl = (lane >> 5) * 8;
   auto compute = [&](int buf) {
     const T* As = lds + buf * STAGE;
     const T* Bs = As + BM * PITCH;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      v8 a[4], b[4];
+      v8 a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < FM; ++i) {
         const u32x4 ra = *reinterpret_cast<const u32x4*>(&As[(arow + 32 * i) * PITCH + ks * 16 + kl]);
-        const u32x4 rb = *reinterpret_cast<const u32x4*>(&Bs[(brw + 32 * i) * PITCH + ks * 16 + kl]);
         __builtin_memcpy(&a[i], &ra, 16);
-        __builtin_memcpy(&b[i], &rb, 16);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < FN; ++j) {
+        const u32x4 rb = *reinterpret_cast<const u32x4*>(&Bs[(brw + 32 * j) * PITCH + ks * 16 + kl]);
+        __builtin_memcpy(&b[j], &rb, 16);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::run(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<T>::run(a[i], b[j], acc[i][j]);
     }
   };
 
   // two LDS stages: step s computes from stage s & 1 while the loads of step
   // s + 1 (issued a step earlier) land in registers and then in the other stage
-  // The loop body has no branch, so the compiler can interleave the staging
-  // (VALU, LDS stores, global loads) with the asynchronous MFMAs; loads past
-  // the end of K read clamped addresses and are masked to zero.
+  // Step s: stage the registers of step s + 1 into the free LDS stage, issue
+  // the global loads of step s + 2 into the same registers, then run step s's
+  // MFMAs, so the loads have a whole step of MFMAs to land. The loop body has
+  // no branch, so the compiler can interleave the staging with the
+  // asynchronous MFMAs; loads past the end of K read clamped addresses and
+  // are masked to zero.
   const int ksteps = (K + BK - 1) / BK;
   load_step(0);
   store_step(0);
-  __syncthreads();
   load_step(BK);
+  __syncthreads();
   for (int s = 0; s + 1 < ksteps; ++s) {
-    compute(s & 1);
     store_step((s + 1) & 1);
     load_step((s + 2) * BK);
+    compute(s & 1);
     __syncthreads();
   }
   compute((ksteps - 1) & 1);
@@ -194,12 +207,12 @@ __global__ __launch_bounds__(NTHR, 1) void rms_linear_mfma(const T* __restrict__
   // rstd per row: the 8 lanes that staged a row hold its partial sums
   if (NORM) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < SV; ++i) {
       float v = ss[i];
       v += __shfl_xor(v, 1);
       v += __shfl_xor(v, 2);
       v += __shfl_xor(v, 4);
-      if ((tid & 7) == 0) rstd_s[srow + 32 * i] = 1.0f / sqrtf(v / (float)K + eps);
+      if ((tid & 7) == 0) rstd_s[srow + SROWS * i] = 1.0f / sqrtf(v / (float)K + eps);
     }
     __syncthreads();
   }
@@ -207,14 +220,14 @@ __global__ __launch_bounds__(NTHR, 1) void rms_linear_mfma(const T* __restrict__
   // written out as 16-byte rows
   T* const cs = lds;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = wn * 128 + j * 32 + (lane & 31);
+  for (int j = 0; j < FN; ++j) {
+    const int col = wn * 32 * FN + j * 32 + (lane & 31);
     const float bv = (HAS_B && n0 + col < N) ? to_f(bias[n0 + col]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int row = wm * 32 * FM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const float rs = NORM ? rstd_s[row] : 1.0f;
         cs[row * CPITCH + col] = from_f<T>(scale * __builtin_fmaf(rs, acc[i][j][r], bv));
       }
