@@ -355,10 +355,12 @@ def build_workloads(torch, npa, synth, quick: bool):
         xs = synth.shuffle_inputs((N_, C_, H_, Wd), layout=lay)
         if lay == 0:
             shp = (N_, g, C_ // g, H_ * Wd)
-            tf = (lambda t: t.view(N_, g, C_ // g, H_, Wd).transpose(1, 2).contiguous())
+            tf = (lambda t, n=N_, c=C_, h=H_, wd=Wd:
+                  t.view(n, g, c // g, h, wd).transpose(1, 2).contiguous())
         else:
             shp = (N_ * H_ * Wd, g, C_ // g, 1)
-            tf = (lambda t: t.view(N_, H_, Wd, g, C_ // g).transpose(3, 4).contiguous())
+            tf = (lambda t, n=N_, c=C_, h=H_, wd=Wd:
+                  t.view(n, h, wd, g, c // g).transpose(3, 4).contiguous())
         layout(nm, f"fp16 ChannelShuffle {nm[8:].upper()} [{N_}, {C_}, {H_}, {Wd}], groups {g} "
                    "(not in the step; baseline: naive strided copy)",
                xs, "f16", shp, "fuse_channel_shuffle", "naive_channel_shuffle", (g, lay), tf,
@@ -366,24 +368,24 @@ def build_workloads(torch, npa, synth, quick: bool):
     # RMSNorm + linear + scale on the matrix cores (not in the step): fused
     # kernel vs RMSNorm -> GEMM + bias -> scale, and torch's bf16 linear
     # (the vendor GEMM) on the stored RMSNorm output, for context
-    M_, K_, N_ = synth.RMS_LINEAR_SHAPE
+    Mr, Kr, Nr = synth.RMS_LINEAR_SHAPE
     if quick:
-        M_ = 2048
-    xr, wr, Wr, br = (tdev(a_, "bf16") for a_ in synth.rmsnorm_linear_inputs((M_, K_, N_)))
-    orl = torch.empty((M_, N_), dtype=torch.bfloat16, device=dev)
-    wsr = torch.empty(npa.rmsnorm_linear_workspace_bytes(M_, K_), dtype=torch.uint8, device=dev)
-    yr = torch.empty((M_, K_), dtype=torch.bfloat16, device=dev)
+        Mr = 2048
+    xr, wr, Wr, br = (tdev(a_, "bf16") for a_ in synth.rmsnorm_linear_inputs((Mr, Kr, Nr)))
+    orl = torch.empty((Mr, Nr), dtype=torch.bfloat16, device=dev)
+    wsr = torch.empty(npa.rmsnorm_linear_workspace_bytes(Mr, Kr), dtype=torch.uint8, device=dev)
+    yr = torch.empty((Mr, Kr), dtype=torch.bfloat16, device=dev)
     npa.fuse_add_rmsnorm(xr, None, wr, None, yr, 1e-6)
     sc = synth.RMS_LINEAR_SCALE
     W["rl"] = dict(
-        desc=f"bf16 RMSNorm + linear + scale, x [{M_}, {K_}] x Wt [{N_}, {K_}]^T (not in the step)",
+        desc=f"bf16 RMSNorm + linear + scale, x [{Mr}, {Kr}] x Wt [{Nr}, {Kr}]^T (not in the step)",
         fused=npa.bind("fuse_rmsnorm_linear", xr, wr, Wr, br, orl, 1e-6, sc),
         unfused=npa.bind("unfused_rmsnorm_linear", xr, wr, Wr, br, orl, wsr, 1e-6, sc),
         unfused_spec=("unfused_rmsnorm_linear", (xr, wr, Wr, br, orl, wsr, 1e-6, sc)),
         torch=lambda: torch.nn.functional.linear(yr, Wr, br).mul_(sc),
-        plan=None, bytes=2 * (M_ * K_ + N_ * K_ + M_ * N_ + K_ + N_),
-        unfused_bytes=2 * (3 * M_ * K_ + N_ * K_ + 3 * M_ * N_ + K_ + N_),
-        flops=2 * M_ * N_ * K_, launches=3, kernel="rms_linear_mfma")
+        plan=None, bytes=2 * (Mr * Kr + Nr * Kr + Mr * Nr + Kr + Nr),
+        unfused_bytes=2 * (3 * Mr * Kr + Nr * Kr + 3 * Mr * Nr + Kr + Nr),
+        flops=2 * Mr * Nr * Kr, launches=3, kernel="rms_linear_mfma")
     W["_compile_ms"] = compile_ms
     return W
 
