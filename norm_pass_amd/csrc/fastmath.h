@@ -31,6 +31,18 @@ NP_FM_INLINE float np_fast_exp(float x) {
   return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(err, kLn2, 1.0f);
 }
 
+// e * exp(x c) for a constant c given as c_hi + c_lo (the binary32 value of
+// c log2(e) and its rounding error), the same argument splitting as
+// np_fast_exp: an affine map before an exp and a constant factor after it
+// fold into the exp's own constants. lim = 300 / |c_hi| keeps 2^t finite.
+NP_FM_INLINE float np_fast_exp_affine(float x, float c_hi, float c_lo, float e, float lim) {
+  const float kLn2 = 0.693147180559945309f;
+  const float xc = __builtin_amdgcn_fmed3f(x, -lim, lim);
+  const float t = xc * c_hi;
+  const float err = __builtin_fmaf(xc, c_lo, __builtin_fmaf(xc, c_hi, -t));
+  return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(err, kLn2 * e, e);
+}
+
 NP_FM_INLINE float np_fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + np_fast_exp(-x));
 }

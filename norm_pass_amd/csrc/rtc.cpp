@@ -14,6 +14,7 @@
 #include <hip/hiprtc.h>
 
 #include <chrono>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <functional>
@@ -57,6 +58,88 @@ std::string op_line(int kind, int arg, float c, bool fast) {
     case NP_CAST_BF16: return "v = (float)(__bf16)v;";
   }
   return "";
+}
+
+// fp16-output chains (the fast transcendental policy) are also folded at
+// generation time; the rewritten chain equals the original in exact
+// arithmetic and rounds no more often:
+//  - runs of constant multiplies (mul_c, scale) become one multiply by their
+//    product, runs of add_c one add of their sum (constants combined in
+//    double, rounded once);
+//  - a multiply followed by an add becomes one fused multiply-add;
+//  - an affine map in front of an exp (x a + b, or (x + b) a = x a + a b)
+//    folds into the exp's constants, exp(x a + b) = e^b 2^(x a log2 e), and a
+//    multiply after it into its factor: e^b c 2^(x a log2 e)
+//    (np_fast_exp_affine);
+//  - a cast that repeats the cast before it is dropped.
+bool is_mul(int k) { return k == NP_MUL_C || k == NP_SCALE; }
+
+std::string exp_affine(double a, double b, double factor) {
+  const double c = a * 1.4426950408889634074;  // a log2(e)
+  const float c_hi = (float)c;
+  const float c_lo = (float)(c - (double)c_hi);
+  const float e = (float)(std::exp(b) * factor);
+  const float lim = c_hi != 0.0f ? (float)(300.0 / std::fabs((double)c_hi)) : 3.0e38f;
+  return "v = np_fast_exp_affine(v, " + hexf(c_hi) + ", " + hexf(c_lo) + ", " + hexf(e) + ", " +
+         hexf(lim) + ");";
+}
+
+std::vector<std::string> fold_fast(const ChainArgs& a) {
+  std::vector<std::string> out;
+  const int n = a.n_ops;
+  int i = 0;
+  auto run = [&](int j, bool mul, double* acc) {  // consume a run of mul (or add) constants
+    *acc = mul ? 1.0 : 0.0;
+    while (j < n && (mul ? is_mul(a.kind[j]) : a.kind[j] == NP_ADD_C)) {
+      *acc = mul ? *acc * (double)a.c[j] : *acc + (double)a.c[j];
+      ++j;
+    }
+    return j;
+  };
+  while (i < n) {
+    const int k = a.kind[i];
+    if (is_mul(k) || k == NP_ADD_C || k == NP_EXP) {
+      double m = 1.0, b = 0.0;
+      int j = i;
+      if (is_mul(k)) j = run(j, true, &m);
+      if (j < n && a.kind[j] == NP_ADD_C) j = run(j, false, &b);
+      if (!is_mul(k) && k == NP_ADD_C && j < n && is_mul(a.kind[j])) {
+        // (x + b) m in front of an exp is x m + b m
+        double m2 = 1.0;
+        const int j2 = run(j, true, &m2);
+        if (j2 < n && a.kind[j2] == NP_EXP) {
+          double after = 1.0;
+          const int j3 = run(j2 + 1, true, &after);
+          out.push_back(exp_affine(m2, b * m2, after));
+          i = j3;
+          continue;
+        }
+      }
+      if (j < n && a.kind[j] == NP_EXP) {
+        double after = 1.0;
+        const int j2 = run(j + 1, true, &after);
+        out.push_back(exp_affine(m, b, after));
+        i = j2;
+        continue;
+      }
+      const bool has_mul = is_mul(k), has_add = a.kind[j - 1] == NP_ADD_C;
+      if (has_mul && has_add)
+        out.push_back("v = __builtin_fmaf(v, " + hexf((float)m) + ", " + hexf((float)b) + ");");
+      else if (has_mul)
+        out.push_back("v = v * " + hexf((float)m) + ";");
+      else
+        out.push_back("v = v + " + hexf((float)b) + ";");
+      i = j;
+      continue;
+    }
+    if ((k == NP_CAST_F16 || k == NP_CAST_BF16) && i > 0 && a.kind[i - 1] == k) {
+      ++i;  // casting again to the same type changes nothing
+      continue;
+    }
+    out.push_back(op_line(k, a.arg[i], a.c[i], true));
+    ++i;
+  }
+  return out;
 }
 
 struct Entry {
@@ -133,8 +216,12 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
     << "__device__ __forceinline__ float chain(";
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "const float* x" << j;
   s << ", int e) {\n  float v = 0.0f;\n";
-  for (int i = 0; i < a.n_ops; ++i)
-    s << "  " << op_line(a.kind[i], a.arg[i], a.c[i], fast) << "\n";
+  if (fast) {
+    for (const std::string& l : fold_fast(a)) s << "  " << l << "\n";
+  } else {
+    for (int i = 0; i < a.n_ops; ++i)
+      s << "  " << op_line(a.kind[i], a.arg[i], a.c[i], fast) << "\n";
+  }
   s << "  return v;\n}\n";
   // vector kernel: one group of NPS_G elements per thread, dwordx4 accesses,
   // non-temporal stores; the < NPS_G leftover elements go to the first threads

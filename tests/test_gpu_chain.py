@@ -188,6 +188,47 @@ def test_c5_specialised(npa, orc):
         npa.np_shutdown()
 
 
+@pytest.mark.parametrize("seed", range(1, 9))
+def test_specialised_folds(npa, orc, seed):
+    """fp16-output specialisation folds constant runs, multiply-add pairs and
+    affine maps around exp into fewer instructions; every folded chain must
+    still match the oracle (the unfolded definition) to the fp16 bar."""
+    ops = synth.c5_chain(n_ops=12, seed=seed)
+    src = npa.np_chain_source(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    body = src[src.index("float chain("):src.index("return v;")]
+    assert body.count("\n  v = ") < len(ops)  # something was folded
+    npa.fuse_chain_prepare(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    try:
+        _c5(npa, orc, synth.c5_inputs(65536, seed=seed), ops)
+        _c5(npa, orc, synth.c5_inputs((1 << 20) + 3, seed=seed + 50), ops)
+    finally:
+        torch.cuda.synchronize()
+        npa.np_shutdown()
+
+
+def test_c5_large_sampled_specialised(npa, orc):
+    """The bench's launch: the prepared (folded) kernel on 2^28 elements,
+    sampled outputs against the oracle."""
+    n = 1 << 28
+    ops = synth.c5_chain()
+    x = synth.c5_inputs(n)
+    tx = to_dev(x, "f16")
+    out = empty((n,), "f16")
+    npa.fuse_chain_prepare(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    try:
+        npa.fuse_chain(ops, [tx], out)
+        torch.cuda.synchronize()
+    finally:
+        npa.np_shutdown()
+    rng = np.random.default_rng(1)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 1 << 20), np.arange(n - 4096, n),
+                                    np.arange(4096)]))
+    got = to_host(out[torch.from_numpy(idx).cuda()])
+    ref, exact, bound = orc.chain(ops, [x[idx]], F16, want_bound=True)
+    check_half(got, ref, "f16", half_values(got, "f16"), exact, bound,
+               what="c5 2^28 sampled, specialised")
+
+
 def test_empty_launches(npa):
     npa.np_empty_launches(29)
     torch.cuda.synchronize()
