@@ -369,6 +369,8 @@ int validate_rms_linear(const void* x, const void* w, const void* Wt, const void
   if (N < 1 || N >= ((int64_t)1 << 31)) return fail(NP_EINVAL, "N = %lld out of range", (long long)N);
   if (K < 8 || K >= ((int64_t)1 << 31) || K % 8 != 0)
     return fail(NP_EINVAL, "K = %lld must be a multiple of 8, >= 8", (long long)K);
+  if (((M + 255) / 256) * ((N + 255) / 256) >= ((int64_t)1 << 31))
+    return fail(NP_EINVAL, "M x N needs more than 2^31 output tiles of 256 x 256");
   if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(NP_EINVAL, "eps must be finite and > 0");
   if (!std::isfinite(scale)) return fail(NP_EINVAL, "scale must be finite");
   if (M == 0) return NP_OK;  // nothing to compute: no buffer is touched

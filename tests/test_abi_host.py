@@ -232,3 +232,35 @@ def test_transpose_plans(npa):
         naive = npa.np_transpose_plan(_LAY[0] + off[0], _LAY[1] + off[1], shape, es, True)
         assert naive["kernel"] == "items"
     assert npa.np_transpose_plan(_LAY[0], _LAY[1], (0, 3, 3, 1), 4) is None
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((4, 32, 60, 1e-6, 1.0, 2), "multiple of 8"),
+    ((4, 32, 64, 1e-6, 1.0, 0), "fp16 or bf16"),
+    ((4, 0, 64, 1e-6, 1.0, 2), "N ="),
+    ((-1, 32, 64, 1e-6, 1.0, 2), "M ="),
+    ((4, 32, 64, 0.0, 1.0, 2), "eps"),
+    ((4, 32, 64, 1e-6, float("inf"), 2), "scale"),
+    (((1 << 31) - 1, (1 << 31) - 1, 64, 1e-6, 1.0, 2), "2^31 output tiles"),
+])
+def test_rmsnorm_linear_rejects(npa, args, msg):
+    M, N, K, eps, scale, dt = args
+    p = [C.c_void_p(1 << 40), None, C.c_void_p(1 << 42), None, C.c_void_p(1 << 44)]
+    for fn in (npa.lib().fuse_rmsnorm_linear,):
+        assert fn(*p, M, N, K, eps, scale, dt, NULL) == -1
+        assert msg in _err(npa)
+    assert npa.lib().unfused_rmsnorm_linear(*p, 4, 32, 64, 1e-6, 1.0, 2, NULL, 0, NULL) == -1
+    assert "workspace" in _err(npa)
+
+
+def test_rmsnorm_linear_rejects_overlap_and_alignment(npa):
+    base = 1 << 40
+    # out overlaps x
+    assert npa.lib().fuse_rmsnorm_linear(C.c_void_p(base), None, C.c_void_p(1 << 42), None,
+                                         C.c_void_p(base + 64), 4, 32, 64, 1e-6, 1.0, 2,
+                                         NULL) == -1
+    assert "overlaps" in _err(npa)
+    assert npa.lib().fuse_rmsnorm_linear(C.c_void_p(base + 2), None, C.c_void_p(1 << 42), None,
+                                         C.c_void_p(1 << 44), 4, 32, 64, 1e-6, 1.0, 2,
+                                         NULL) == -1
+    assert "aligned" in _err(npa)
