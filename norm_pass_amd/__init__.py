@@ -65,6 +65,7 @@ def _load():
         "np_empty_launches": [I, P],
         "fuse_rmsnorm_linear": [P, P, P, P, P, I64, I64, I64, F, F, I, P],
         "unfused_rmsnorm_linear": [P, P, P, P, P, I64, I64, I64, F, F, I, P, S, P],
+        "np_fold_norm_weight": [P, P, P, I64, I64, I, P],
         "fuse_transpose021": [P, P, I64, I64, I64, I64, I, P],
         "naive_transpose021": [P, P, I64, I64, I64, I64, I, P],
         "fuse_channel_shuffle": [P, P, I64, I64, I64, I64, I64, I, I, P],
@@ -370,6 +371,16 @@ def fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps: float = 1e-6, scale: floa
     _check(_lib.fuse_rmsnorm_linear(*_a_fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps, scale,
                                                             stream)), "fuse_rmsnorm_linear")
     return out
+
+
+def np_fold_norm_weight(w_norm, Wt, Wt_folded, stream=None):
+    """Wt_folded = round(w_norm * Wt) per element (the norm weight moved into the
+    linear weight, once); Wt [N, K]."""
+    _keep(stream, w_norm, Wt, Wt_folded)
+    _check(_lib.np_fold_norm_weight(_ptr(w_norm), _ptr(Wt), _ptr(Wt_folded), Wt.shape[0],
+                                    Wt.shape[1], dtype_code(Wt), _stream(stream)),
+           "np_fold_norm_weight")
+    return Wt_folded
 
 
 def rmsnorm_linear_workspace_bytes(M: int, K: int) -> int:

@@ -766,6 +766,27 @@ int unfused_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, co
   return ok();
 }
 
+int np_fold_norm_weight(const void* w_norm, const void* Wt, void* Wt_folded, int64_t N, int64_t K,
+                        np_dtype dt, hipStream_t stream) {
+  if (dt != NP_BF16 && dt != NP_F16) return fail(NP_EINVAL, "fold takes fp16 or bf16");
+  if (N < 1 || N >= ((int64_t)1 << 31) || K < 8 || K >= ((int64_t)1 << 31) || K % 8 != 0)
+    return fail(NP_EINVAL, "bad sizes N = %lld, K = %lld (K a multiple of 8)", (long long)N,
+                (long long)K);
+  if (!w_norm || !Wt || !Wt_folded) return fail(NP_EINVAL, "NULL argument");
+  if (!aligned16(w_norm) || !aligned16(Wt) || !aligned16(Wt_folded))
+    return fail(NP_EINVAL, "w_norm, Wt and Wt_folded must be 16-byte aligned");
+  const uint64_t bytes = (uint64_t)N * K * 2, a = (uint64_t)(uintptr_t)Wt,
+                 o = (uint64_t)(uintptr_t)Wt_folded, wa = (uint64_t)(uintptr_t)w_norm;
+  if (a != o && a < o + bytes && o < a + bytes)
+    return fail(NP_EINVAL, "Wt_folded partially overlaps Wt");
+  if (wa < o + bytes && o < wa + (uint64_t)K * 2) return fail(NP_EINVAL, "Wt_folded overlaps w_norm");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = np::launch_fold_norm_weight(w_norm, Wt, Wt_folded, N, K, dt, stream);
+  if (e != hipSuccess) return hip_fail(e, "np_fold_norm_weight");
+  return ok();
+}
+
 int np_transpose_plan(const void* in, const void* out, int64_t B, int64_t R, int64_t S,
                       int64_t E, int elem_bytes, int naive) {
   int64_t total = 0;

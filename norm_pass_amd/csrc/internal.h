@@ -56,6 +56,9 @@ hipError_t launch_rmsnorm_linear(const void* x, const void* w, const void* Wt, c
                                  void* out, int M, int N, int K, float eps, float scale, int dt,
                                  bool norm, hipStream_t s);
 
+hipError_t launch_fold_norm_weight(const void* w, const void* Wt, void* Wf, int64_t N, int64_t K,
+                                   int dt, hipStream_t s);
+
 // QKV split + RoPE + scale
 struct RopeArgs {
   const void* qkv;

@@ -36,18 +36,38 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <typename T>
 struct Mfma;
+// run: one 32x32x16 MFMA. sumsq: acc + the sum of squares of the 8 elements,
+// as four packed dot products (v_dot2_f32_bf16 / v_dot2_f32_f16, fp32 sums).
 template <>
 struct Mfma<__bf16> {
   typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 run(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float sumsq(v8 a, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v2 p = {a[2 * i], a[2 * i + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+    }
+    return acc;
   }
 };
 template <>
 struct Mfma<_Float16> {
   typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 run(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float sumsq(v8 a, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v2 p = {a[2 * i], a[2 * i + 1]};
+      acc = __builtin_amdgcn_fdot2(p, p, acc, false);
+    }
+    return acc;
   }
 };
 
@@ -249,6 +269,203 @@ __global__ __launch_bounds__(NTHR) void rms_linear_mfma(const T* __restrict__ x,
   }
 }
 
+
+// ---- direct-to-LDS pipeline (A operand used as stored: no norm weight) ------
+//
+// With no per-element work on A, both operands go from global memory straight
+// into LDS (global_load_lds_dwordx4: lane l of a wave writes the 16 bytes at
+// the wave's LDS base + 16 l), through a ring of four 32-wide K stages, so the
+// loads of step s + 3 are in flight while step s runs on the matrix cores and
+// no registers hold staged data. LDS rows are 64 bytes (four 16-byte chunks);
+// chunk c of row r is stored at position c ^ ((r >> 1) & 3), so the 8 rows read
+// together by an MFMA fragment load hit distinct banks. The row sums of x^2
+// come from the A fragments the MFMAs already read (packed dot products, in
+// the two waves with wn == wm: one per 128-row half, on different SIMDs).
+// Rows past M or N are loaded from the last valid row (outputs discarded); K
+// must be a multiple of 32. Waits and barriers are explicit: vmcnt counts this
+// wave's LDS DMAs in issue order, and a plain s_barrier (no fence, which would
+// drain every DMA in flight) then makes the step's stage complete for all
+// waves.
+constexpr int DBK = 32, DNS = 4;
+constexpr int D_ABYTES = BM * DBK * 2, D_STAGE = 2 * D_ABYTES;  // A then B, 16 KiB each
+constexpr int D_SMEM = DNS * D_STAGE > BM * CPITCH * 2 ? DNS * D_STAGE : BM * CPITCH * 2;
+constexpr int D_NJ = 16 / (NTHR / 64);  // DMA instructions per wave, operand and stage
+static_assert(BM == BN && D_NJ * (NTHR / 64) * 64 * 16 == D_ABYTES, "DMA map");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory (wave-uniform base + per-lane 32-bit
+// offset) into LDS at the wave-uniform address lds + 16 lane. Written out so
+// that the offset register stays the instruction's operand: the compiler's
+// own form recomputed 64-bit addresses into registers it then reused for LDS
+// reads, and waited for every DMA in flight first. Completion is tracked by
+// the explicit vmcnt waits of the caller.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, void* lds) {
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(off),
+               "s"(base)
+               : "memory", "m0");
+}
+
+template <typename T, bool NORM, bool HAS_B>
+__global__ __launch_bounds__(NTHR) void rms_linear_dma(const T* __restrict__ x,
+                                                       const T* __restrict__ Wt,
+                                                       const T* __restrict__ bias,
+                                                       T* __restrict__ out, int M, int N, int K,
+                                                       float eps, float scale, int tiles_m,
+                                                       int tiles_n, int vec_out) {
+  typedef typename Mfma<T>::v8 v8;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[D_SMEM];
+  __shared__ float rstd_s[BM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  const int per_group = GROUP_M * tiles_n;
+  const int g = t / per_group, within = t - g * per_group;
+  const int gsz = min(GROUP_M, tiles_m - g * GROUP_M);
+  const int m0 = (g * GROUP_M + within % gsz) * BM, n0 = (within / gsz) * BN;
+  // DMA map: instruction j of this wave fills LDS chunks (wave D_NJ + j) 64 + lane.
+  // Addresses are a wave-uniform base (tile corner + k0) plus loop-invariant
+  // per-lane byte offsets (< 2^31: K < 2^22 on this path), so no fresh address
+  // registers are written each step (a register the compiler reuses right after
+  // an LDS DMA forces a wait for every DMA in flight).
+  const uint8_t* const xa0 = reinterpret_cast<const uint8_t*>(x + (int64_t)m0 * K);
+  const uint8_t* const wb0 = reinterpret_cast<const uint8_t*>(Wt + (int64_t)n0 * K);
+  uint32_t oa[D_NJ], ob[D_NJ];
+#pragma unroll
+  for (int j = 0; j < D_NJ; ++j) {
+    const int p = (wave * D_NJ + j) * 64 + lane;
+    const int r = p >> 2, c = (p & 3) ^ ((r >> 1) & 3);
+    oa[j] = (uint32_t)(((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2);
+    ob[j] = (uint32_t)(((min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
+  }
+  const int ksteps = K / DBK;
+  auto issue = [&](int step) {
+    const int k0b = min(step, ksteps - 1) * DBK * 2;  // steps past the end refill a free stage
+    uint8_t* st = smem + (step % DNS) * D_STAGE;
+#pragma unroll
+    for (int j = 0; j < D_NJ; ++j) {
+      lds_dma16(xa0 + k0b, oa[j], st + (wave * D_NJ + j) * 1024);
+      lds_dma16(wb0 + k0b, ob[j], st + D_ABYTES + (wave * D_NJ + j) * 1024);
+    }
+  };
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // row sums of x^2 from the A fragments (lane l: rows wm 128 + 32 i + l % 32,
+  // one k half), in waves wn == wm (one per 128-row half), which write rstd
+  float ss[FM] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bool sumsq = NORM && wn == wm;  // wave-uniform
+  const int l32 = lane & 31, hi = lane >> 5;
+  auto compute = [&](int stage) {
+    const uint8_t* As = smem + stage * D_STAGE;
+    const uint8_t* Bs = As + D_ABYTES;
+    v8 a[2][FM], b[2][FN];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 2 * ks + hi;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * 32 * FM + 32 * i + l32;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 64 + ((c ^ ((r >> 1) & 3)) << 4));
+        __builtin_memcpy(&a[ks][i], &v, 16);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * 32 * FN + 32 * j + l32;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 64 + ((c ^ ((r >> 1) & 3)) << 4));
+        __builtin_memcpy(&b[ks][j], &v, 16);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<T>::run(a[ks][i], b[ks][j], acc[i][j]);
+    if (sumsq) {  // wave-uniform: the two waves with wn == wm, one per 128-row half
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) ss[i] = Mfma<T>::sumsq(a[ks][i], ss[i]);
+    }
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  for (int s = 0; s < ksteps; ++s) {
+    // this wave's DMAs of step s have landed (those of s + 1 and s + 2 may not)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * 2 * D_NJ) : "memory");
+    asm volatile("s_barrier" ::: "memory");  // every wave's have; step s - 1 is done
+    issue(s + 3);                            // into the stage of step s - 1
+    compute(s % DNS);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still write LDS
+  __syncthreads();
+  if (NORM) {
+    if (sumsq) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const float v = ss[i] + __shfl_xor(ss[i], 32);  // the two k halves of the row
+        if (hi == 0) rstd_s[wm * 32 * FM + 32 * i + l32] = 1.0f / sqrtf(v / (float)K + eps);
+      }
+    }
+    __syncthreads();
+  }
+  T* const cs = reinterpret_cast<T*>(smem);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = wn * 32 * FN + j * 32 + l32;
+    const float bv = (HAS_B && n0 + col < N) ? to_f(bias[n0 + col]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 * FM + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float rs = NORM ? rstd_s[row] : 1.0f;
+        cs[row * CPITCH + col] = from_f<T>(scale * __builtin_fmaf(rs, acc[i][j][r], bv));
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < BM * BN / 8 / NTHR; ++i) {
+    const int v = tid + NTHR * i;
+    const int row = v >> 5, cv = (v & 31) * 8;
+    const int gm = m0 + row, gn = n0 + cv;
+    if (gm >= M) continue;
+    T* dst = out + (int64_t)gm * N + gn;
+    if (vec_out && gn + 8 <= N) {
+      store_raw_nt(dst, *reinterpret_cast<const u32x4*>(&cs[row * CPITCH + cv]));
+    } else {
+      for (int e = 0; e < 8 && gn + e < N; ++e) dst[e] = cs[row * CPITCH + cv + e];
+    }
+  }
+}
+
+// Fold the norm weight into the linear weight: Wf[n][k] = round_T(w[k] Wt[n][k]).
+template <typename T>
+__global__ __launch_bounds__(256) void fold_weight(const T* __restrict__ w, const T* __restrict__ Wt,
+                                                   T* __restrict__ Wf, int64_t n_vec, int kvec) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= n_vec) return;
+  const int kv = (int)(v % kvec);
+  T a[8], b[8];
+  const u32x4 ra = load_raw(Wt + v * 8), rb = load_raw(w + kv * 8);
+  __builtin_memcpy(a, &ra, 16);
+  __builtin_memcpy(b, &rb, 16);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = from_f<T>(to_f(a[i]) * to_f(b[i]));  // exact product, one rounding
+  u32x4 o;
+  __builtin_memcpy(&o, a, 16);
+  store_raw(Wf + v * 8, o);
+}
+
 template <typename T, bool NORM>
 hipError_t launch_t(const void* x, const void* w, const void* Wt, const void* b, void* out,
                     int M, int N, int K, float eps, float scale, hipStream_t s) {
@@ -260,6 +477,15 @@ hipError_t launch_t(const void* x, const void* w, const void* Wt, const void* b,
   const T* Wp = static_cast<const T*>(Wt);
   const T* bp = static_cast<const T*>(b);
   T* op = static_cast<T*>(out);
+  if (!w && K % DBK == 0 && K < (1 << 22)) {
+    if (b)
+      hipLaunchKernelGGL((rms_linear_dma<T, NORM, true>), grid, dim3(NTHR), 0, s, xp, Wp, bp, op,
+                         M, N, K, eps, scale, tm, tn, vec_out);
+    else
+      hipLaunchKernelGGL((rms_linear_dma<T, NORM, false>), grid, dim3(NTHR), 0, s, xp, Wp, bp, op,
+                         M, N, K, eps, scale, tm, tn, vec_out);
+    return hipGetLastError();
+  }
 #define NP_RL(HW, HB)                                                                          \
   hipLaunchKernelGGL((rms_linear_mfma<T, NORM, HW, HB>), grid, dim3(NTHR), 0, s, xp, wp, Wp, bp, \
                      op, M, N, K, eps, scale, tm, tn, vec_out)
@@ -272,6 +498,21 @@ hipError_t launch_t(const void* x, const void* w, const void* Wt, const void* b,
 }
 
 }  // namespace
+
+hipError_t launch_fold_norm_weight(const void* w, const void* Wt, void* Wf, int64_t N, int64_t K,
+                                   int dt, hipStream_t s) {
+  const int64_t n_vec = N * K / 8;
+  const dim3 grid((unsigned)((n_vec + 255) / 256));
+  if (dt == NP_BF16)
+    hipLaunchKernelGGL(fold_weight<__bf16>, grid, dim3(256), 0, s, (const __bf16*)w,
+                       (const __bf16*)Wt, (__bf16*)Wf, n_vec, (int)(K / 8));
+  else if (dt == NP_F16)
+    hipLaunchKernelGGL(fold_weight<_Float16>, grid, dim3(256), 0, s, (const _Float16*)w,
+                       (const _Float16*)Wt, (_Float16*)Wf, n_vec, (int)(K / 8));
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm_linear(const void* x, const void* w, const void* Wt, const void* b,
                                  void* out, int M, int N, int K, float eps, float scale, int dt,

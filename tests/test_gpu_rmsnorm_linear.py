@@ -119,6 +119,64 @@ def test_full_size_sampled_rows(npa, orc):
     _check(got, exact, cond, K, "bf16", want_bits=want)
 
 
+def _oracle_fold(orc, w, Wt, dt):
+    """round_dt(w_k Wt_nk): the product of two dt values is exact in float64."""
+    wv = _vals(w, dt)
+    Wv = _vals(Wt.reshape(-1), dt).reshape(Wt.shape)
+    return orc.round_array(Wv * wv[None, :], ORACLE_DT[dt])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_fold_norm_weight_bit_exact(npa, orc, dt):
+    N, K = 96, 200
+    _, w, Wt, _ = _inputs(1, K, N, 6100, dt)
+    out = empty((N, K), dt)
+    npa.np_fold_norm_weight(to_dev(w, dt), to_dev(Wt, dt), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out), _oracle_fold(orc, w, Wt, dt))
+
+
+# the direct-to-LDS kernel: no norm weight, K a multiple of 32; ragged M and N
+DMA_CASES = [(300, 260, 512), (33, 1000, 96), (517, 40, 64), (256, 512, 4096), (1, 8, 32)]
+
+
+@pytest.mark.parametrize("M,N,K", DMA_CASES)
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("with_b", [True, False])
+def test_direct_lds_path_matches_oracle(npa, orc, M, N, K, dt, with_b):
+    x, w, Wt, b = _inputs(M, K, N, 6200 + M + N + K, dt)
+    b = b if with_b else None
+    want, exact, cond = orc.rmsnorm_linear(x, None, Wt, b, 1e-6, 0.75, ORACLE_DT[dt],
+                                           want_exact=True)
+    out = empty((M, N), dt)
+    npa.fuse_rmsnorm_linear(to_dev(x, dt), None, to_dev(Wt, dt),
+                            None if b is None else to_dev(b, dt), out, 1e-6, 0.75)
+    torch.cuda.synchronize()
+    _check(to_host(out), exact, cond, K, dt, want_bits=want)
+
+
+def test_folded_full_size_sampled_rows(npa, orc):
+    """The bench's folded launch: the norm weight folded into Wt once, then the
+    direct-to-LDS kernel on the 16384 x 4096 x 4096 workload; sampled rows
+    against the oracle with the oracle's own folded weight."""
+    M, K, N = synth.RMS_LINEAR_SHAPE
+    x, w, Wt, b = synth.rmsnorm_linear_inputs()
+    Wf = empty((N, K), "bf16")
+    npa.np_fold_norm_weight(to_dev(w, "bf16"), to_dev(Wt, "bf16"), Wf)
+    out = empty((M, N), "bf16")
+    npa.fuse_rmsnorm_linear(to_dev(x, "bf16"), None, Wf, to_dev(b, "bf16"), out, 1e-6,
+                            synth.RMS_LINEAR_SCALE)
+    torch.cuda.synchronize()
+    Wf_o = _oracle_fold(orc, w, Wt, "bf16")
+    assert np.array_equal(to_host(Wf), Wf_o)
+    rng = np.random.default_rng(23)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
+    want, exact, cond = orc.rmsnorm_linear(x[rows], None, Wf_o, b, 1e-6, synth.RMS_LINEAR_SCALE,
+                                           ORACLE_DT["bf16"], want_exact=True)
+    got = to_host(out[torch.from_numpy(rows).cuda()])
+    _check(got, exact, cond, K, "bf16", want_bits=want)
+
+
 def test_empty_and_rejects(npa):
     x = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
     Wt = torch.zeros(32, 64, dtype=torch.bfloat16, device="cuda")
