@@ -31,16 +31,15 @@ NP_FM_INLINE float np_fast_exp(float x) {
   return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(err, kLn2, 1.0f);
 }
 
-// e * exp(x c) for a constant c given as c_hi + c_lo (the binary32 value of
-// c log2(e) and its rounding error), the same argument splitting as
-// np_fast_exp: an affine map before an exp and a constant factor after it
-// fold into the exp's own constants. lim = 300 / |c_hi| keeps 2^t finite.
-NP_FM_INLINE float np_fast_exp_affine(float x, float c_hi, float c_lo, float e, float lim) {
-  const float kLn2 = 0.693147180559945309f;
-  const float xc = __builtin_amdgcn_fmed3f(x, -lim, lim);
-  const float t = xc * c_hi;
-  const float err = __builtin_fmaf(xc, c_lo, __builtin_fmaf(xc, c_hi, -t));
-  return __builtin_amdgcn_exp2f(t) * __builtin_fmaf(err, kLn2 * e, e);
+// e * exp(x a) for constants c = a log2(e) and e (an affine map before an exp
+// and a factor after it, folded into the exp by the runtime specialiser):
+// 2^(x c) by v_exp_f32, times e. Without the argument splitting of
+// np_fast_exp the rounding of x c adds |x c| / 2 ulp of relative error (the
+// specialiser's fp16-output chains keep |x c| small; at |x c| = 16 this is 2^-20,
+// 1/512 of an fp16 ulp). Infinite or NaN arguments give inf, 0 or NaN as exp
+// does; 2^(x c) below 2^-126 is flushed to zero.
+NP_FM_INLINE float np_fast_exp_affine(float x, float c, float e) {
+  return __builtin_amdgcn_exp2f(x * c) * e;
 }
 
 NP_FM_INLINE float np_fast_sigmoid(float x) {

@@ -62,7 +62,7 @@ std::string op_line(int kind, int arg, float c, bool fast) {
 
 // fp16-output chains (the fast transcendental policy) are also folded at
 // generation time; the rewritten chain equals the original in exact
-// arithmetic and rounds no more often:
+// arithmetic:
 //  - runs of constant multiplies (mul_c, scale) become one multiply by their
 //    product, runs of add_c one add of their sum (constants combined in
 //    double, rounded once);
@@ -70,18 +70,14 @@ std::string op_line(int kind, int arg, float c, bool fast) {
 //  - an affine map in front of an exp (x a + b, or (x + b) a = x a + a b)
 //    folds into the exp's constants, exp(x a + b) = e^b 2^(x a log2 e), and a
 //    multiply after it into its factor: e^b c 2^(x a log2 e)
-//    (np_fast_exp_affine);
+//    (np_fast_exp_affine: v_exp_f32 of x·a·log2 e, times the factor);
 //  - a cast that repeats the cast before it is dropped.
 bool is_mul(int k) { return k == NP_MUL_C || k == NP_SCALE; }
 
 std::string exp_affine(double a, double b, double factor) {
-  const double c = a * 1.4426950408889634074;  // a log2(e)
-  const float c_hi = (float)c;
-  const float c_lo = (float)(c - (double)c_hi);
+  const float c = (float)(a * 1.4426950408889634074);  // a log2(e)
   const float e = (float)(std::exp(b) * factor);
-  const float lim = c_hi != 0.0f ? (float)(300.0 / std::fabs((double)c_hi)) : 3.0e38f;
-  return "v = np_fast_exp_affine(v, " + hexf(c_hi) + ", " + hexf(c_lo) + ", " + hexf(e) + ", " +
-         hexf(lim) + ");";
+  return "v = np_fast_exp_affine(v, " + hexf(c) + ", " + hexf(e) + ");";
 }
 
 std::vector<std::string> fold_fast(const ChainArgs& a) {
