@@ -22,7 +22,12 @@ constexpr int kBlock = 256;
 
 // One formula for every channel, so that the lanes of a wave (which hold
 // different channels) do not diverge: channels 2 and 3 need exp(t), all others
-// sigmoid(t) = 1 / (1 + exp(-t)); one exp of +-t serves both.
+// sigmoid(t) = 1 / (1 + exp(-t)); one exp of +-t serves both. The exp is
+// np_fast_exp (<= 2 fp32 ulp) and the reciprocal v_rcp_f32 (1 ulp) applied to
+// (1 + e) 2^-32 and scaled back by 2^-32: the scaled input stays below 2^96,
+// so the reciprocal never has to produce a subnormal (which it would flush),
+// and the final exact multiply by 2^-32 rounds correctly into the subnormal
+// range. Sigmoid error <= 4 ulp (5e-7 relative).
 //   k = 0: (sigmoid + x) * stride   k = 1: (sigmoid + y) * stride
 //   k = 2: exp * anchor_w           k = 3: exp * anchor_h      k >= 4: sigmoid
 // Per-tile constants (stride, anchor, 1/W) are read once per workgroup.
@@ -33,7 +38,7 @@ struct TileConst {
 
 __device__ __forceinline__ float decode_one(const TileConst& tc, int k, int cell, float t) {
   const bool is_exp = k == 2 || k == 3;
-  const float e = expf(is_exp ? t : -t);
+  const float e = np_fast_exp(is_exp ? t : -t);
   // cell / W and cell % W: (cell + 0.5) / W is >= 0.5 / W from an integer, far
   // above the float rounding for cell < 2^22, so truncation gives the row
   const int y = (int)(((float)cell + 0.5f) * tc.inv_w);
@@ -41,7 +46,8 @@ __device__ __forceinline__ float decode_one(const TileConst& tc, int k, int cell
   const float grid = k == 0 ? (float)x : k == 1 ? (float)y : 0.0f;
   const float mul = k < 2 ? tc.stride : 1.0f;
   const float anc = k == 3 ? tc.ah : tc.aw;
-  return is_exp ? e * anc : (1.0f / (1.0f + e) + grid) * mul;
+  const float sig = __builtin_amdgcn_rcpf(__builtin_fmaf(e, 0x1p-32f, 0x1p-32f)) * 0x1p-32f;
+  return is_exp ? e * anc : (sig + grid) * mul;
 }
 
 #ifndef NP_DET_XCD_REMAP
