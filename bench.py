@@ -75,17 +75,8 @@ def rope_bytes(T, H, D, es=2):
     return 6 * q, 6 * q + 2 * q + 2 * q + 2 * q
 
 
-# VALU instructions per element of one chain op in the fp16-output specialised
-# kernel (static count of its gfx950 code, one side of tanh's branch): the
-# fallback when no rocprofv3 SQ_INSTS_VALU count for the current sources exists.
-VALU_SLOTS = {0: 1, 1: 2, 2: 2, 3: 1, 4: 1, 5: 1, 6: 1, 7: 8, 8: 7, 9: 10, 10: 2, 11: 2}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 VALU_PEAK = 256 * 64 * 2.4e9  # lane-instr/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
-
-
-def chain_slots(ops) -> int:
-    """VALU slots per element: every op, plus the final rounding store."""
-    return sum(VALU_SLOTS[k] for k, _, _ in ops) + 1
 
 
 def file_hash(*paths) -> str:
@@ -612,16 +603,18 @@ def main(argv=None):
     hbm_frac = d["bytes"] / t_dom / 1e9 / HBM_PEAK_GBPS
     if dom.startswith("c5"):
         n_el = d["bytes"] // 4
+        # executed VALU instructions per element from the committed rocprofv3
+        # SQ_INSTS_VALU count; none (and no achieved figure) once the kernel
+        # sources have changed since it was taken
         per_el = measured_valu_per_element(dom)
-        src = "rocprofv3 SQ_INSTS_VALU"
-        if per_el is None:
-            per_el, src = float(chain_slots(synth.c5_chain())), "static slot table"
-        achieved = per_el * n_el / t_dom / 1e12
+        achieved = per_el * n_el / t_dom / 1e12 if per_el is not None else None
         roof = {"kernel": dom, "launch_us": round(t_dom * 1e6, 2), "bound": "alu",
-                "achieved": round(achieved, 2),
+                "achieved": round(achieved, 2) if achieved is not None else None,
                 "peak": round(VALU_PEAK / 1e12, 2), "unit": "T VALU lane-instr/s",
-                "frac": round(achieved * 1e12 / VALU_PEAK, 4),
-                "valu_per_element": round(per_el, 2), "valu_count_source": src,
+                "frac": round(achieved * 1e12 / VALU_PEAK, 4) if achieved is not None else None,
+                "valu_per_element": round(per_el, 2) if per_el is not None else None,
+                "valu_count_source": "rocprofv3 SQ_INSTS_VALU" if per_el is not None
+                else "none for the current kernel sources",
                 "hbm_frac": round(hbm_frac, 4), "traffic": measured_traffic(dom)}
     else:
         achieved = d["bytes"] / t_dom / 1e9
@@ -635,8 +628,9 @@ def main(argv=None):
                                    / HBM_PEAK_GBPS, 4)
     for k in ("c5_small", "c5_large"):
         n_el = per[k]["bytes"] // 4
-        per[k]["valu_frac"] = round(chain_slots(synth.c5_chain()) * n_el
-                                    / (per[k]["us_med"] * 1e-6) / VALU_PEAK, 4)
+        v = measured_valu_per_element(k)
+        per[k]["valu_frac"] = (round(v * n_el / (per[k]["us_med"] * 1e-6) / VALU_PEAK, 4)
+                               if v is not None else None)
 
     cpu = None
     if not args.no_cpu:

@@ -33,7 +33,8 @@ NP_FM_INLINE float np_fast_exp(float x) {
 
 // e * exp(x a) for constants c = a log2(e) and e (an affine map before an exp
 // and a factor after it, folded into the exp by the runtime specialiser):
-// 2^(x c) by v_exp_f32, times e. Without the argument splitting of
+// 2^(x c) by v_exp_f32, times e (the specialiser uses it for e = 0 only; the
+// shifted form below serves every other factor). Without the argument splitting of
 // np_fast_exp the rounding of x c adds |x c| / 2 ulp of relative error (the
 // specialiser's fp16-output chains keep |x c| small; at |x c| = 16 this is 2^-20,
 // 1/512 of an fp16 ulp). Infinite or NaN arguments give inf, 0 or NaN as exp
@@ -42,24 +43,80 @@ NP_FM_INLINE float np_fast_exp_affine(float x, float c, float e) {
   return __builtin_amdgcn_exp2f(x * c) * e;
 }
 
+// |e| exp(x a) for a factor e != 0, as 2^(x c + d) with d = log2 |e| (the
+// caller negates the result when e < 0): one FMA forms the exponent, so the
+// factor costs no multiply. The FMA's rounding adds |x c + d| / 2 ulp of
+// relative error, as the product x c does above; a result the factor brings
+// back into range is not lost to an overflow or flush of 2^(x c) first.
+NP_FM_INLINE float np_fast_exp_shifted(float x, float c, float d) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, d));
+}
+
 NP_FM_INLINE float np_fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + np_fast_exp(-x));
+}
+
+// sigmoid(x a + b) = 1 / (1 + e^-b 2^(x c)) for constants c = -a log2(e) and
+// e = e^-b (an affine map folded into the sigmoid by the runtime specialiser).
+// The rounding of x c adds |x c| / 2 ulp to the exponential's relative error,
+// and the sigmoid's relative error is at most that of the exponential. An
+// overflowing 2^(x c) gives 1 / inf = 0; an underflowing one gives 1.
+NP_FM_INLINE float np_fast_sigmoid_affine(float x, float c, float e) {
+  return __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(x * c), e, 1.0f));
+}
+
+// tanh for |x| < 0.625: the odd polynomial evaluated on x itself. Every step is
+// symmetric under a sign change, so this equals the |x| form with the sign put
+// back, except that -0 gives +0.
+NP_FM_INLINE float np_fast_tanh_poly(float x) {
+  const float z = x * x;
+  float p = -0.005704987328499556f;
+  p = __builtin_fmaf(p, z, 0.0206390880048275f);
+  p = __builtin_fmaf(p, z, -0.05373971536755562f);
+  p = __builtin_fmaf(p, z, 0.13331441581249237f);
+  p = __builtin_fmaf(p, z, -0.3333328068256378f);
+  return __builtin_fmaf(x * z, p, x);
+}
+
+// tanh for x >= 0.625 (and +inf): 1 - 2 / (1 + e^(2x)), e^(2x) = 2^(2x log2 e).
+NP_FM_INLINE float np_fast_tanh_exp_pos(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * 2.88539008177792681f);
+  return __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+}
+
+// tanh for x <= -0.625 (and -inf): 2 / (1 + e^(-2x)) - 1, the negation of the
+// form above at -x (the same bits with the sign flipped).
+NP_FM_INLINE float np_fast_tanh_exp_neg(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * -2.88539008177792681f);
+  return __builtin_fmaf(2.0f, __builtin_amdgcn_rcpf(1.0f + e), -1.0f);
 }
 
 NP_FM_INLINE float np_fast_tanh(float x) {
   const float a = __builtin_fabsf(x);
   float r;
-  if (a < 0.625f) {  // a branch, not a select: a wave whose lanes agree runs one side
-    const float z = a * a;
-    float p = -0.005704987328499556f;
-    p = __builtin_fmaf(p, z, 0.0206390880048275f);
-    p = __builtin_fmaf(p, z, -0.05373971536755562f);
-    p = __builtin_fmaf(p, z, 0.13331441581249237f);
-    p = __builtin_fmaf(p, z, -0.3333328068256378f);
-    r = __builtin_fmaf(a * z, p, a);
-  } else {
-    const float e = __builtin_amdgcn_exp2f(a * 2.88539008177792681f);  // e^(2a) = 2^(2a log2 e)
-    r = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
-  }
+  if (a < 0.625f)  // a branch, not a select: a wave whose lanes agree runs one side
+    r = np_fast_tanh_poly(a);
+  else
+    r = np_fast_tanh_exp_pos(a);
   return __builtin_copysignf(r, x);
+}
+
+// tanh when the sign of x is known (x >= 0, x <= 0): one branch, no sign
+// handling. NaN takes the exponential side and stays NaN.
+NP_FM_INLINE float np_fast_tanh_pos(float x) {
+  float r;
+  if (x < 0.625f)
+    r = np_fast_tanh_poly(x);
+  else
+    r = np_fast_tanh_exp_pos(x);
+  return r;
+}
+
+NP_FM_INLINE float np_fast_tanh_neg(float x) {
+  float r;
+  if (x > -0.625f)
+    r = np_fast_tanh_poly(x);
+  else
+    r = np_fast_tanh_exp_neg(x);
+  return r;
 }

@@ -14,6 +14,7 @@
 #include <hip/hiprtc.h>
 
 #include <chrono>
+#include <cfloat>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -69,19 +70,149 @@ std::string op_line(int kind, int arg, float c, bool fast) {
 //  - a multiply followed by an add becomes one fused multiply-add;
 //  - an affine map in front of an exp (x a + b, or (x + b) a = x a + a b)
 //    folds into the exp's constants, exp(x a + b) = e^b 2^(x a log2 e), and a
-//    multiply after it into its factor: e^b c 2^(x a log2 e)
-//    (np_fast_exp_affine: v_exp_f32 of x·a·log2 e, times the factor);
+//    multiply after it into its factor: e^b c 2^(x a log2 e), and the factor
+//    into the exponent, 2^(x a log2 e + log2 |e^b c|) (np_fast_exp_shifted:
+//    one FMA and v_exp_f32);
+//  - likewise in front of a sigmoid: 1 / (1 + e^-b 2^(-x a log2 e))
+//    (np_fast_sigmoid_affine);
+//  - the factor of a folded exp moves into the constant of an exp or sigmoid
+//    that follows it directly (2^(x c1) e1 c2 = 2^(x c1) (e1 c2));
 //  - a cast that repeats the cast before it is dropped.
+// Each tanh is then emitted in the cheapest form that holds on the range of
+// its argument (value ranges below).
 bool is_mul(int k) { return k == NP_MUL_C || k == NP_SCALE; }
 
-std::string exp_affine(double a, double b, double factor) {
-  const float c = (float)(a * 1.4426950408889634074);  // a log2(e)
-  const float e = (float)(std::exp(b) * factor);
-  return "v = np_fast_exp_affine(v, " + hexf(c) + ", " + hexf(e) + ");";
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr double kInf = HUGE_VAL;
+
+// ---- value ranges ----------------------------------------------------------
+// Before every op the specialiser tracks an interval that holds every binary32
+// value the generated code can compute there (NaN aside: NaN passes through
+// every emitted form). A loaded input may be any value of its type,
+// infinities included. Each op maps the interval through its monotone real
+// function; the result is widened by 2^-16 of the largest finite magnitude
+// among operand, constant and result, plus 2^-126 -- more than the rounding
+// and approximation error of any form emitted for it (<= 4 ulp of the result,
+// 2^-24 of the operands of a folded sum, or |t| / 2 ulp for the exponent t,
+// |t| < 152, of a folded exp or sigmoid) -- and a bound beyond the binary32 range becomes
+// infinite (the computed value overflows there). Ops whose computed result
+// always has the sign of the exact one (multiply, exp, sigmoid, tanh, casts)
+// do not widen across zero. Casts widen by their own half ulp.
+struct Range {
+  double lo, hi;
+};
+
+constexpr double kRangeRel = 0x1p-16;
+
+double finite_mag(const Range& r) {
+  return std::fmax(std::isfinite(r.lo) ? std::fabs(r.lo) : 0.0,
+                   std::isfinite(r.hi) ? std::fabs(r.hi) : 0.0);
 }
 
-std::vector<std::string> fold_fast(const ChainArgs& a) {
-  std::vector<std::string> out;
+Range widen(const Range& r, double d, bool keeps_sign, double max_finite) {
+  Range w{r.lo - d, r.hi + d};
+  if (keeps_sign && r.lo >= 0.0) w.lo = std::fmax(w.lo, 0.0);
+  if (keeps_sign && r.hi <= 0.0) w.hi = std::fmin(w.hi, 0.0);
+  if (w.lo < -max_finite) w.lo = -kInf;
+  if (w.hi > max_finite) w.hi = kInf;
+  return w;
+}
+
+// an op's exact image r of the operand interval -> the computed values
+Range computed(const Range& r, double operand_mag, bool keeps_sign) {
+  const double d = std::fmax(operand_mag, finite_mag(r)) * kRangeRel + 0x1p-126;
+  return widen(r, d, keeps_sign, FLT_MAX);
+}
+
+Range cast_to(const Range& r, double half_ulp_rel, double half_ulp_min, double max_finite) {
+  return widen(r, finite_mag(r) * half_ulp_rel + half_ulp_min, true, max_finite);
+}
+
+double sigmoid_d(double t) { return 1.0 / (1.0 + std::exp(-t)); }
+
+std::vector<Range> op_ranges(const ChainArgs& a) {
+  std::vector<Range> before(a.n_ops);
+  Range r{-kInf, kInf};
+  for (int i = 0; i < a.n_ops; ++i) {
+    before[i] = r;
+    const double c = a.c[i];
+    switch (a.kind[i]) {
+      case NP_ADD_C:
+        r = computed({r.lo + c, r.hi + c}, std::fmax(finite_mag(r), std::fabs(c)), false);
+        break;
+      case NP_MUL_C:
+      case NP_SCALE:
+        // 0 * inf is NaN, which the interval does not hold
+        r = computed(c > 0 ? Range{r.lo * c, r.hi * c}
+                           : c < 0 ? Range{r.hi * c, r.lo * c} : Range{0.0, 0.0},
+                     0.0, true);
+        break;
+      case NP_RELU: r = {0.0, std::fmax(r.hi, 0.0)}; break;  // a NaN input gives 0
+      case NP_EXP: r = computed({std::exp(r.lo), std::exp(r.hi)}, 0.0, true); break;
+      case NP_SIGMOID: r = computed({sigmoid_d(r.lo), sigmoid_d(r.hi)}, 0.0, true); break;
+      case NP_TANH: r = computed({std::tanh(r.lo), std::tanh(r.hi)}, 0.0, true); break;
+      case NP_CAST_F16: r = cast_to(r, 0x1p-11, 0x1p-25, 65504.0); break;
+      case NP_CAST_BF16: r = cast_to(r, 0x1p-8, 0x1p-134, 0x1.fep127); break;
+      default: r = {-kInf, kInf}; break;  // a loaded input: any value
+    }
+  }
+  return before;
+}
+
+// ---- tanh on a known range -------------------------------------------------
+// Odd Taylor series tanh x = x + sum_k T_k x^(2k+1) (coefficients from the
+// Bernoulli numbers: -1/3, 2/15, -17/315, 62/2835, -1382/155925). For
+// |x| <= 1/2 its terms alternate in sign and shrink by a factor below 0.41 x^2,
+// so cutting it after T_k x^(2k+1) leaves a relative error below
+// |T_(k+1)| x^(2k+2) / (1 - x^2/3). A cut is taken when that is at most 2^-26
+// (a quarter of a binary32 ulp); Horner's rounding adds < 1/4 ulp (the
+// correction term is under 0.09 x), the final FMA 1/2 ulp.
+constexpr double kTanhT[6] = {1.0,           -1.0 / 3.0,       2.0 / 15.0,
+                              -17.0 / 315.0, 62.0 / 2835.0,   -1382.0 / 155925.0};
+constexpr double kTanhTau = 0x1p-26;
+
+std::string tanh_on(const Range& r) {
+  const double m = std::fmax(std::fabs(r.lo), std::fabs(r.hi));
+  const double shrink = 1.0 / (1.0 - m * m / 3.0);
+  if (m <= 0.5) {
+    if (m * m / 3.0 * shrink <= kTanhTau) return "";  // tanh x = x to 2^-26
+    for (int k = 1; k <= 4; ++k) {
+      if (std::fabs(kTanhT[k + 1]) * std::pow(m, 2 * k + 2) * shrink > kTanhTau) continue;
+      std::string l = "{ const float z = v * v; ";
+      if (k == 1) return l + "v = __builtin_fmaf(v * z, " + hexf((float)kTanhT[1]) + ", v); }";
+      l += "float p = " + hexf((float)kTanhT[k]) + "; ";
+      for (int j = k - 1; j >= 1; --j) l += "p = __builtin_fmaf(p, z, " + hexf((float)kTanhT[j]) + "); ";
+      return l + "v = __builtin_fmaf(v * z, p, v); }";
+    }
+  }
+  if (m < 0.625) return "v = np_fast_tanh_poly(v);";
+  if (r.lo >= 0.625) return "v = np_fast_tanh_exp_pos(v);";
+  if (r.hi <= -0.625) return "v = np_fast_tanh_exp_neg(v);";
+  if (r.lo >= 0.0) return "v = np_fast_tanh_pos(v);";
+  if (r.hi <= 0.0) return "v = np_fast_tanh_neg(v);";
+  return "v = np_fast_tanh(v);";
+}
+
+// ---- folded op list --------------------------------------------------------
+enum : int { K_FMA = 100, K_EXPA, K_SIGA };
+
+struct Node {
+  int kind;                 // an NP_ op kind, or K_FMA / K_EXPA / K_SIGA
+  int arg = 0;              // input index (LOAD, ADD_IN, MUL_IN)
+  double m = 1.0, b = 0.0;  // MUL_C: m; ADD_C: b; FMA: v m + b; EXPA / SIGA: constant m, factor b
+  Range in{-kInf, kInf};    // range of v in front of a tanh
+};
+
+// A folded constant must stay a normal binary32 number (or zero): e^b of a
+// large |b| would overflow where the unfolded add would not.
+bool foldable(double x) {
+  const double a = std::fabs(x);
+  return a == 0.0 || (a >= 0x1p-100 && a <= 0x1p100);
+}
+
+std::vector<Node> fold_fast(const ChainArgs& a) {
+  const std::vector<Range> before = op_ranges(a);
+  std::vector<Node> out;
   const int n = a.n_ops;
   int i = 0;
   auto run = [&](int j, bool mul, double* acc) {  // consume a run of mul (or add) constants
@@ -92,39 +223,60 @@ std::vector<std::string> fold_fast(const ChainArgs& a) {
     }
     return j;
   };
+  auto transcendental = [&](int j) {
+    return j < n && (a.kind[j] == NP_EXP || a.kind[j] == NP_SIGMOID);
+  };
+  // the exp or sigmoid at j after the affine map x m + b, folded into one node
+  // when its constants stay foldable; *next = the op after it
+  auto fold_at = [&](int j, double m, double b, Node* t, int* next) {
+    if (a.kind[j] == NP_EXP) {
+      double after = 1.0;
+      *next = run(j + 1, true, &after);
+      *t = {K_EXPA, 0, m * kLog2e, std::exp(b) * after};
+    } else {
+      *next = j + 1;
+      *t = {K_SIGA, 0, -m * kLog2e, std::exp(-b)};
+    }
+    return foldable(t->m) && foldable(t->b);
+  };
   while (i < n) {
     const int k = a.kind[i];
-    if (is_mul(k) || k == NP_ADD_C || k == NP_EXP) {
+    if (is_mul(k) || k == NP_ADD_C || k == NP_EXP || k == NP_SIGMOID) {
       double m = 1.0, b = 0.0;
-      int j = i;
+      int j = i, next = 0;
+      Node t{0};
       if (is_mul(k)) j = run(j, true, &m);
       if (j < n && a.kind[j] == NP_ADD_C) j = run(j, false, &b);
-      if (!is_mul(k) && k == NP_ADD_C && j < n && is_mul(a.kind[j])) {
-        // (x + b) m in front of an exp is x m + b m
+      if (k == NP_ADD_C && j < n && is_mul(a.kind[j])) {
+        // (x + b) m in front of an exp or sigmoid is x m + b m
         double m2 = 1.0;
         const int j2 = run(j, true, &m2);
-        if (j2 < n && a.kind[j2] == NP_EXP) {
-          double after = 1.0;
-          const int j3 = run(j2 + 1, true, &after);
-          out.push_back(exp_affine(m2, b * m2, after));
-          i = j3;
+        if (transcendental(j2) && fold_at(j2, m2, b * m2, &t, &next)) {
+          out.push_back(t);
+          i = next;
           continue;
         }
       }
-      if (j < n && a.kind[j] == NP_EXP) {
-        double after = 1.0;
-        const int j2 = run(j + 1, true, &after);
-        out.push_back(exp_affine(m, b, after));
-        i = j2;
-        continue;
+      if (transcendental(j)) {
+        if (fold_at(j, m, b, &t, &next)) {
+          out.push_back(t);
+          i = next;
+          continue;
+        }
+        if (j == i) {  // a bare exp or sigmoid whose following factor cannot fold
+          out.push_back({t.kind, 0, t.kind == K_EXPA ? kLog2e : -kLog2e, 1.0});
+          i = j + 1;
+          continue;
+        }
+        // otherwise the affine map stays a separate statement
       }
       const bool has_mul = is_mul(k), has_add = a.kind[j - 1] == NP_ADD_C;
       if (has_mul && has_add)
-        out.push_back("v = __builtin_fmaf(v, " + hexf((float)m) + ", " + hexf((float)b) + ");");
+        out.push_back({K_FMA, 0, m, b});
       else if (has_mul)
-        out.push_back("v = v * " + hexf((float)m) + ";");
+        out.push_back({NP_MUL_C, 0, m, 0.0});
       else
-        out.push_back("v = v + " + hexf((float)b) + ";");
+        out.push_back({NP_ADD_C, 0, 1.0, b});
       i = j;
       continue;
     }
@@ -132,10 +284,47 @@ std::vector<std::string> fold_fast(const ChainArgs& a) {
       ++i;  // casting again to the same type changes nothing
       continue;
     }
-    out.push_back(op_line(k, a.arg[i], a.c[i], true));
+    Node op{k, a.arg[i], (double)a.c[i], (double)a.c[i]};
+    op.in = before[i];
+    out.push_back(op);
     ++i;
   }
+  // an exp's factor moves into the constant of the exp or sigmoid after it
+  for (size_t q = 0; q + 1 < out.size(); ++q) {
+    if (out[q].kind != K_EXPA || (out[q + 1].kind != K_EXPA && out[q + 1].kind != K_SIGA))
+      continue;
+    const double c = out[q + 1].m * out[q].b;
+    if (!foldable(c)) continue;
+    out[q + 1].m = c;
+    out[q].b = 1.0;
+  }
   return out;
+}
+
+std::string emit(const Node& n) {
+  switch (n.kind) {
+    case K_FMA:
+      return "v = __builtin_fmaf(v, " + hexf((float)n.m) + ", " + hexf((float)n.b) + ");";
+    case K_EXPA: {
+      if (n.b == 1.0) return "v = __builtin_amdgcn_exp2f(v * " + hexf((float)n.m) + ");";
+      if (n.b == 0.0)
+        return "v = np_fast_exp_affine(v, " + hexf((float)n.m) + ", " + hexf(0.0f) + ");";
+      const std::string call = "np_fast_exp_shifted(v, " + hexf((float)n.m) + ", " +
+                               hexf((float)std::log2(std::fabs(n.b))) + ")";
+      return n.b < 0.0 ? "v = -" + call + ";" : "v = " + call + ";";
+    }
+    case K_SIGA:
+      return "v = np_fast_sigmoid_affine(v, " + hexf((float)n.m) + ", " + hexf((float)n.b) + ");";
+    case NP_MUL_C: return "v = v * " + hexf((float)n.m) + ";";
+    case NP_ADD_C: return "v = v + " + hexf((float)n.b) + ";";
+    case NP_TANH: {
+      char buf[96];
+      std::snprintf(buf, sizeof buf, "// tanh argument in [%a, %a]", n.in.lo, n.in.hi);
+      const std::string f = tanh_on(n.in);
+      return std::string(buf) + (f.empty() ? " (tanh x = x there)" : "\n  " + f);
+    }
+    default: return op_line(n.kind, n.arg, (float)n.m, true);
+  }
 }
 
 struct Entry {
@@ -213,7 +402,7 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "const float* x" << j;
   s << ", int e) {\n  float v = 0.0f;\n";
   if (fast) {
-    for (const std::string& l : fold_fast(a)) s << "  " << l << "\n";
+    for (const Node& nd : fold_fast(a)) s << "  " << emit(nd) << "\n";
   } else {
     for (int i = 0; i < a.n_ops; ++i)
       s << "  " << op_line(a.kind[i], a.arg[i], a.c[i], fast) << "\n";

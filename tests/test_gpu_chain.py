@@ -206,6 +206,23 @@ def test_specialised_folds(npa, orc, seed):
         npa.np_shutdown()
 
 
+@pytest.mark.parametrize("seed", [29, 200, 201, 202, 203, 204, 205])
+def test_specialised_every_fp16_input(npa, orc, seed):
+    """Every fp16 input that is not NaN (both zeros, subnormals, the largest
+    finite values, both infinities) through a specialised 29-op chain: the
+    tanh forms chosen from the argument ranges and the folded exps must hold
+    over the whole input domain, not only over the workload's N(0, 1) draws."""
+    ops = synth.c5_chain(n_ops=29, seed=seed)
+    x = np.arange(1 << 16, dtype=np.uint16).view(np.float16)
+    x = x[~np.isnan(x)]
+    npa.fuse_chain_prepare(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    try:
+        _c5(npa, orc, x, ops)
+    finally:
+        torch.cuda.synchronize()
+        npa.np_shutdown()
+
+
 def test_c5_large_sampled_specialised(npa, orc):
     """The bench's launch: the prepared (folded) kernel on 2^28 elements,
     sampled outputs against the oracle."""
