@@ -383,7 +383,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         torch=lambda: torch.nn.functional.linear(yr, Wr, br).mul_(sc),
         plan=None, bytes=2 * (Mr * Kr + Nr * Kr + Mr * Nr + Kr + Nr),
         unfused_bytes=2 * (3 * Mr * Kr + Nr * Kr + 3 * Mr * Nr + Kr + Nr),
-        flops=2 * Mr * Nr * Kr, launches=3, kernel="rms_linear_dma")
+        flops=2 * Mr * Nr * Kr, launches=3, kernel="rms_linear_dma4")
     W["_compile_ms"] = compile_ms
     return W
 

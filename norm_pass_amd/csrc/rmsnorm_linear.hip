@@ -448,6 +448,185 @@ __global__ __launch_bounds__(NTHR) void rms_linear_dma(const T* __restrict__ x,
   }
 }
 
+// ---- four-wave direct-to-LDS pipeline (K a multiple of 64) -----------------
+//
+// The same direct-to-LDS scheme with one wave per SIMD, each owning 128 x 128
+// outputs (4 x 4 MFMA blocks, 256 fp32 accumulators per lane, held in the
+// accumulation registers): a fragment read from LDS now feeds four MFMAs
+// instead of two or four, which halves the LDS read traffic per MFMA (the
+// eight-wave kernel's reads and DMA writes together kept LDS about as busy as
+// the matrix cores). With a single wave per SIMD no other wave hides LDS
+// latency, so the fragments of the next 16-wide k slice are read while this
+// slice's MFMAs run (two register sets, reads spread between the MFMAs). Each
+// K step is 64 wide, so every row's 128 bytes -- one cache line -- arrive in
+// one step; two 64 KiB stages form the ring. LDS rows are 128 bytes and chunk
+// c of row r sits at position c ^ (r & 7), conflict free for the 8 rows an
+// MFMA fragment load reads together. The row sums of x^2 come from the A
+// fragments the MFMAs read: each of the two waves sharing a 128-row half takes
+// two of its four 32-row blocks, so every wave runs the same code (a branch
+// around the sums would split the MFMA / LDS-read interleave of the waves that
+// take it, and with one wave per SIMD nothing else fills the gap).
+constexpr int Q_BK = 64, Q_NTHR = 256;
+constexpr int Q_ABYTES = BM * Q_BK * 2, Q_STAGE = 2 * Q_ABYTES;  // A then B, 32 KiB each
+constexpr int Q_SMEM = 2 * Q_STAGE > BM * CPITCH * 2 ? 2 * Q_STAGE : BM * CPITCH * 2;
+constexpr int Q_NJ = Q_ABYTES / 1024 / (Q_NTHR / 64);  // DMA instructions per wave and operand
+static_assert(BM == BN && Q_NJ == 8, "DMA map");
+
+template <typename T, bool NORM, bool HAS_B>
+__global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ x,
+                                                          const T* __restrict__ Wt,
+                                                          const T* __restrict__ bias,
+                                                          T* __restrict__ out, int M, int N, int K,
+                                                          float eps, float scale, int tiles_m,
+                                                          int tiles_n, int vec_out) {
+  typedef typename Mfma<T>::v8 v8;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Q_SMEM];
+  __shared__ float rstd_s[BM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  const int per_group = GROUP_M * tiles_n;
+  const int g = t / per_group, within = t - g * per_group;
+  const int gsz = min(GROUP_M, tiles_m - g * GROUP_M);
+  const int m0 = (g * GROUP_M + within % gsz) * BM, n0 = (within / gsz) * BN;
+  // DMA map: instruction j of this wave fills LDS chunks (wave Q_NJ + j) 64 + lane:
+  // row p / 8, stored chunk p % 8, which holds k chunk (p % 8) ^ (row % 8)
+  const uint8_t* const xa0 = reinterpret_cast<const uint8_t*>(x + (int64_t)m0 * K);
+  const uint8_t* const wb0 = reinterpret_cast<const uint8_t*>(Wt + (int64_t)n0 * K);
+  uint32_t oa[Q_NJ], ob[Q_NJ];
+#pragma unroll
+  for (int j = 0; j < Q_NJ; ++j) {
+    const int p = (wave * Q_NJ + j) * 64 + lane;
+    const int r = p >> 3, c = (p & 7) ^ (r & 7);
+    oa[j] = (uint32_t)(((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2);
+    ob[j] = (uint32_t)(((min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
+  }
+  const int ksteps = K / Q_BK;
+  auto issue = [&](int step) {
+    const int k0b = min(step, ksteps - 1) * Q_BK * 2;  // steps past the end refill a free stage
+    uint8_t* st = smem + (step & 1) * Q_STAGE;
+#pragma unroll
+    for (int j = 0; j < Q_NJ; ++j) {
+      lds_dma16(xa0 + k0b, oa[j], st + (wave * Q_NJ + j) * 1024);
+      lds_dma16(wb0 + k0b, ob[j], st + Q_ABYTES + (wave * Q_NJ + j) * 1024);
+    }
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // register slot i holds row block i ^ (2 wn) of the wave's 128 rows, so that
+  // slots 0 and 1 are the two blocks whose sums of squares this wave forms
+  // (the two waves of a row half split its four blocks; no branch)
+  float ss[2] = {0.0f, 0.0f};
+  const int l32 = lane & 31, hi = lane >> 5;
+  auto rb = [&](int i) { return i ^ (2 * wn); };
+  v8 fa[2][4], fb[2][4];
+  // fragments of 16-wide k slice ks (0..3) of a stage into register set buf
+  auto rd = [&](int buf, int stage, int ks) {
+    const uint8_t* As = smem + stage * Q_STAGE;
+    const uint8_t* Bs = As + Q_ABYTES;
+    const int c = 2 * ks + hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + 32 * rb(i) + l32;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 128 + ((c ^ (r & 7)) << 4));
+      __builtin_memcpy(&fa[buf][i], &v, 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 128 + 32 * j + l32;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 128 + ((c ^ (r & 7)) << 4));
+      __builtin_memcpy(&fb[buf][j], &v, 16);
+    }
+  };
+  auto mm = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::run(fa[buf][i], fb[buf][j], acc[i][j]);
+    if (NORM) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ss[i] = Mfma<T>::sumsq(fa[buf][i], ss[i]);
+    }
+    // one MFMA, then one LDS read (the next slice's fragments), eight times
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+  issue(0);
+  issue(1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Q_NJ) : "memory");  // this wave's step 0
+  asm volatile("s_barrier" ::: "memory");                         // everyone's
+  rd(0, 0, 0);
+  for (int s = 0; s < ksteps; ++s) {
+    const int st = s & 1;
+    rd(1, st, 1);
+    mm(0);
+    rd(0, st, 2);
+    mm(1);
+    rd(1, st, 3);
+    mm(0);
+    // step s + 1 has landed everywhere, and every wave has read all of step s
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    issue(s + 2);  // into the stage of step s
+    rd(0, st ^ 1, 0);
+    mm(1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still write LDS
+  __syncthreads();
+  if (NORM) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float v = ss[i] + __shfl_xor(ss[i], 32);  // the two k halves of the row
+      if (hi == 0) rstd_s[wm * 128 + 32 * rb(i) + l32] = 1.0f / sqrtf(v / (float)K + eps);
+    }
+    __syncthreads();
+  }
+  T* const cs = reinterpret_cast<T*>(smem);
+  float bv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = wn * 128 + j * 32 + l32;
+    bv[j] = (HAS_B && n0 + col < N) ? to_f(bias[n0 + col]) : 0.0f;
+  }
+  // row by row: one rstd read per row, the row's four column blocks
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 128 + rb(i) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const float rs = NORM ? rstd_s[row] : 1.0f;
+      T* const crow = cs + row * CPITCH + wn * 128 + l32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        crow[j * 32] = from_f<T>(scale * __builtin_fmaf(rs, acc[i][j][r], bv[j]));
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < BM * BN / 8 / Q_NTHR; ++i) {
+    const int v = tid + Q_NTHR * i;
+    const int row = v >> 5, cv = (v & 31) * 8;
+    const int gm = m0 + row, gn = n0 + cv;
+    if (gm >= M) continue;
+    T* dst = out + (int64_t)gm * N + gn;
+    if (vec_out && gn + 8 <= N) {
+      store_raw_nt(dst, *reinterpret_cast<const u32x4*>(&cs[row * CPITCH + cv]));
+    } else {
+      for (int e = 0; e < 8 && gn + e < N; ++e) dst[e] = cs[row * CPITCH + cv + e];
+    }
+  }
+}
+
 // Fold the norm weight into the linear weight: Wf[n][k] = round_T(w[k] Wt[n][k]).
 template <typename T>
 __global__ __launch_bounds__(256) void fold_weight(const T* __restrict__ w, const T* __restrict__ Wt,
@@ -477,6 +656,15 @@ hipError_t launch_t(const void* x, const void* w, const void* Wt, const void* b,
   const T* Wp = static_cast<const T*>(Wt);
   const T* bp = static_cast<const T*>(b);
   T* op = static_cast<T*>(out);
+  if (!w && K % Q_BK == 0 && K < (1 << 22)) {
+    if (b)
+      hipLaunchKernelGGL((rms_linear_dma4<T, NORM, true>), grid, dim3(Q_NTHR), 0, s, xp, Wp, bp,
+                         op, M, N, K, eps, scale, tm, tn, vec_out);
+    else
+      hipLaunchKernelGGL((rms_linear_dma4<T, NORM, false>), grid, dim3(Q_NTHR), 0, s, xp, Wp, bp,
+                         op, M, N, K, eps, scale, tm, tn, vec_out);
+    return hipGetLastError();
+  }
   if (!w && K % DBK == 0 && K < (1 << 22)) {
     if (b)
       hipLaunchKernelGGL((rms_linear_dma<T, NORM, true>), grid, dim3(NTHR), 0, s, xp, Wp, bp, op,

@@ -136,8 +136,11 @@ def test_fold_norm_weight_bit_exact(npa, orc, dt):
     assert np.array_equal(to_host(out), _oracle_fold(orc, w, Wt, dt))
 
 
-# the direct-to-LDS kernel: no norm weight, K a multiple of 32; ragged M and N
-DMA_CASES = [(300, 260, 512), (33, 1000, 96), (517, 40, 64), (256, 512, 4096), (1, 8, 32)]
+# the direct-to-LDS kernels: no norm weight and K a multiple of 32 (the
+# four-wave kernel when K is a multiple of 64, the eight-wave one otherwise);
+# ragged M and N, and N not a multiple of 8 (element-wise output stores)
+DMA_CASES = [(300, 260, 512), (33, 1000, 96), (517, 40, 64), (256, 512, 4096), (1, 8, 32),
+             (1, 8, 64), (513, 257, 192), (300, 250, 128), (70, 30, 96)]
 
 
 @pytest.mark.parametrize("M,N,K", DMA_CASES)
