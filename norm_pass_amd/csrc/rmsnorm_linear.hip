@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -627,6 +629,204 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ 
   }
 }
 
+// ---- four-wave kernel with the norm weight applied on the way to LDS --------
+//
+// The four-wave layout of rms_linear_dma4 for the case where a norm weight is
+// passed: B still streams into LDS by DMA, but A = round(x w) must be formed
+// first, so x passes through registers. Each thread stages eight 16-byte
+// vectors of the 256 x 64 A block per step (rows q 32 + tid / 8, k chunk
+// tid % 8, so its eight norm-weight values are one vector), sums the squares of
+// its x values with packed dot products, multiplies by w (exact product, one
+// rounding to T) and writes the chunk to its swizzled LDS position. Step s + 1
+// is staged in the middle of step s (its global loads were issued right after
+// the previous barrier, beside the B DMAs), into the stage every wave finished
+// reading at that barrier. The last step stages nothing, so no row sum counts a
+// step twice.
+template <typename T, bool HAS_B>
+__global__ __launch_bounds__(Q_NTHR) void rms_linear_reg4(const T* __restrict__ x,
+                                                          const T* __restrict__ w,
+                                                          const T* __restrict__ Wt,
+                                                          const T* __restrict__ bias,
+                                                          T* __restrict__ out, int M, int N, int K,
+                                                          float eps, float scale, int tiles_m,
+                                                          int tiles_n, int vec_out) {
+  typedef typename Mfma<T>::v8 v8;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Q_SMEM];
+  __shared__ float rstd_s[BM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  const int per_group = GROUP_M * tiles_n;
+  const int g = t / per_group, within = t - g * per_group;
+  const int gsz = min(GROUP_M, tiles_m - g * GROUP_M);
+  const int m0 = (g * GROUP_M + within % gsz) * BM, n0 = (within / gsz) * BN;
+  const uint8_t* const wb0 = reinterpret_cast<const uint8_t*>(Wt + (int64_t)n0 * K);
+  uint32_t ob[Q_NJ];
+#pragma unroll
+  for (int j = 0; j < Q_NJ; ++j) {
+    const int p = (wave * Q_NJ + j) * 64 + lane;
+    const int r = p >> 3, c = (p & 7) ^ (r & 7);
+    ob[j] = (uint32_t)(((min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
+  }
+  // A staging map: vector q of this thread is row arow0 + 32 q, k chunk ac
+  const int arow0 = tid >> 3, ac = tid & 7;
+  const T* xrow[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) xrow[q] = x + (int64_t)min(m0 + arow0 + 32 * q, M - 1) * K + 8 * ac;
+  const int ksteps = K / Q_BK;
+  u32x4 xa[8], wa;
+  auto gload = [&](int step) {
+    const int k0 = min(step, ksteps - 1) * Q_BK;  // steps past the end reload the last one
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xa[q] = load_raw(xrow[q] + k0);
+    wa = load_raw(w + k0 + 8 * ac);
+  };
+  auto dma_b = [&](int step) {
+    const int k0b = min(step, ksteps - 1) * Q_BK * 2;
+    uint8_t* st = smem + (step & 1) * Q_STAGE + Q_ABYTES;
+#pragma unroll
+    for (int j = 0; j < Q_NJ; ++j) lds_dma16(wb0 + k0b, ob[j], st + (wave * Q_NJ + j) * 1024);
+  };
+  float ss[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) ss[q] = 0.0f;
+  auto stage_a = [&](int step) {  // squares of x, a = round(x w), swizzled into LDS
+    uint8_t* As = smem + (step & 1) * Q_STAGE;
+    T wv[8];
+    __builtin_memcpy(wv, &wa, 16);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      v8 xv;
+      __builtin_memcpy(&xv, &xa[q], 16);
+      ss[q] = Mfma<T>::sumsq(xv, ss[q]);
+      T e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = from_f<T>(to_f(xv[j]) * to_f(wv[j]));
+      const int r = arow0 + 32 * q;
+      *reinterpret_cast<u32x4*>(As + r * 128 + ((ac ^ (r & 7)) << 4)) = *reinterpret_cast<const u32x4*>(e);
+    }
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const int l32 = lane & 31, hi = lane >> 5;
+  v8 fa[2][4], fb[2][4];
+  auto rd = [&](int buf, int stage, int ks) {
+    const uint8_t* As = smem + stage * Q_STAGE;
+    const uint8_t* Bs = As + Q_ABYTES;
+    const int c = 2 * ks + hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + 32 * i + l32;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 128 + ((c ^ (r & 7)) << 4));
+      __builtin_memcpy(&fa[buf][i], &v, 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 128 + 32 * j + l32;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 128 + ((c ^ (r & 7)) << 4));
+      __builtin_memcpy(&fb[buf][j], &v, 16);
+    }
+  };
+  auto mm = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::run(fa[buf][i], fb[buf][j], acc[i][j]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+  gload(0);
+  dma_b(0);
+  dma_b(1);
+  stage_a(0);
+  gload(1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Q_NJ + 9) : "memory");  // B of step 0 (A(1) may run)
+  __syncthreads();  // A of step 0 written by every thread, B of step 0 landed everywhere
+  rd(0, 0, 0);
+  // one K step; MORE: there is a step after it to stage and refill
+  auto body = [&](int s, auto more) {
+    const int st = s & 1;
+    rd(1, st, 1);
+    mm(0);
+    if constexpr (decltype(more)::value) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage_a(s + 1);  // into the stage every wave finished reading at the last barrier
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    rd(0, st, 2);
+    mm(1);
+    rd(1, st, 3);
+    mm(0);
+    if constexpr (decltype(more)::value) {
+      // B of step s + 1 landed (this wave's DMAs; A(s + 2) is not issued yet),
+      // this wave's A writes done; then everyone's
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
+      dma_b(s + 2);  // into the stage of step s, which every wave has finished reading
+      gload(s + 2);
+      rd(0, st ^ 1, 0);
+    }
+    mm(1);
+  };
+  for (int s = 0; s + 1 < ksteps; ++s) body(s, std::true_type());
+  body(ksteps - 1, std::false_type());
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still write LDS
+  __syncthreads();
+  // rstd per row: the 8 lanes that staged a row hold its partial sums
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float v = ss[q];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    if (ac == 0) rstd_s[arow0 + 32 * q] = 1.0f / sqrtf(v / (float)K + eps);
+  }
+  __syncthreads();
+  T* const cs = reinterpret_cast<T*>(smem);
+  float bv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = wn * 128 + j * 32 + l32;
+    bv[j] = (HAS_B && n0 + col < N) ? to_f(bias[n0 + col]) : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const float rs = rstd_s[row];
+      T* const crow = cs + row * CPITCH + wn * 128 + l32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        crow[j * 32] = from_f<T>(scale * __builtin_fmaf(rs, acc[i][j][r], bv[j]));
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < BM * BN / 8 / Q_NTHR; ++i) {
+    const int v = tid + Q_NTHR * i;
+    const int row = v >> 5, cv = (v & 31) * 8;
+    const int gm = m0 + row, gn = n0 + cv;
+    if (gm >= M) continue;
+    T* dst = out + (int64_t)gm * N + gn;
+    if (vec_out && gn + 8 <= N) {
+      store_raw_nt(dst, *reinterpret_cast<const u32x4*>(&cs[row * CPITCH + cv]));
+    } else {
+      for (int e = 0; e < 8 && gn + e < N; ++e) dst[e] = cs[row * CPITCH + cv + e];
+    }
+  }
+}
+
 // Fold the norm weight into the linear weight: Wf[n][k] = round_T(w[k] Wt[n][k]).
 template <typename T>
 __global__ __launch_bounds__(256) void fold_weight(const T* __restrict__ w, const T* __restrict__ Wt,
@@ -671,6 +871,15 @@ hipError_t launch_t(const void* x, const void* w, const void* Wt, const void* b,
                          M, N, K, eps, scale, tm, tn, vec_out);
     else
       hipLaunchKernelGGL((rms_linear_dma<T, NORM, false>), grid, dim3(NTHR), 0, s, xp, Wp, bp, op,
+                         M, N, K, eps, scale, tm, tn, vec_out);
+    return hipGetLastError();
+  }
+  if (NORM && w && K % Q_BK == 0 && K < (1 << 22)) {
+    if (b)
+      hipLaunchKernelGGL((rms_linear_reg4<T, true>), grid, dim3(Q_NTHR), 0, s, xp, wp, Wp, bp, op,
+                         M, N, K, eps, scale, tm, tn, vec_out);
+    else
+      hipLaunchKernelGGL((rms_linear_reg4<T, false>), grid, dim3(Q_NTHR), 0, s, xp, wp, Wp, bp, op,
                          M, N, K, eps, scale, tm, tn, vec_out);
     return hipGetLastError();
   }

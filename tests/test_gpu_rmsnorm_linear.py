@@ -60,8 +60,9 @@ def _check(got, exact, cond, K, dt, min_equal=0.995, want_bits=None):
         assert (got == want_bits).mean() >= min_equal, float((got == want_bits).mean())
 
 
-CASES = [  # M, N, K
+CASES = [  # M, N, K (K a multiple of 64: the four-wave kernels; otherwise the eight-wave ones)
     (256, 256, 512), (300, 260, 520), (1, 1, 8), (129, 130, 72), (64, 384, 1024), (517, 33, 136),
+    (513, 257, 192), (1, 8, 64), (300, 250, 128),
 ]
 
 
