@@ -120,3 +120,42 @@ NP_FM_INLINE float np_fast_tanh_neg(float x) {
     r = np_fast_tanh_exp_neg(x);
   return r;
 }
+
+// Casts to fp16 merged with the affine ops around them (fp16-output chains, by
+// the runtime specialiser), on gfx950's mixed-precision FMAs:
+// round_f16(v m + b) in one v_fma_mixlo_f16 (a single rounding of the fused
+// product-sum, where a separate fp32 op and cast round twice: both are within
+// half an fp16 ulp plus half an fp32 ulp of v m + b), and (float)h m + b in
+// one v_fma_mix_f32 with the f16 operand taken as is (exact widening, then one
+// fp32 rounding, as a multiply or FMA after the cast). A zero result may come
+// out +0 where the separate ops give -0; the value is the same. The constants
+// travel in scalar registers.
+NP_FM_INLINE _Float16 np_fma_to_f16(float v, float m, float b) {
+  _Float16 r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(m), "v"(b));
+  return r;
+}
+
+NP_FM_INLINE _Float16 np_mul_to_f16(float v, float m) {
+  _Float16 r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(r) : "v"(v), "s"(m));
+  return r;
+}
+
+NP_FM_INLINE _Float16 np_add_to_f16(float v, float b) {
+  _Float16 r;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, %2" : "=v"(r) : "v"(v), "s"(b));
+  return r;
+}
+
+NP_FM_INLINE float np_fma_from_f16(_Float16 h, float m, float b) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "s"(m), "v"(b));
+  return r;
+}
+
+NP_FM_INLINE float np_mul_from_f16(_Float16 h, float m) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "s"(m));
+  return r;
+}

@@ -327,6 +327,58 @@ std::string emit(const Node& n) {
   }
 }
 
+// Emits the folded ops; a cast to fp16 is merged with a constant multiply, add
+// or FMA right before it (np_{mul,add,fma}_to_f16: one rounding to fp16) and
+// with a constant multiply, FMA or pure 2^(v c) right after it
+// (np_{mul,fma}_from_f16 take the fp16 value as is), which saves the
+// conversions between them.
+bool affine_node(const Node& n) {
+  return n.kind == NP_MUL_C || n.kind == NP_ADD_C || n.kind == K_FMA;
+}
+
+std::vector<std::string> emit_all(const std::vector<Node>& nodes) {
+  std::vector<std::string> out;
+  const size_t n = nodes.size();
+  size_t i = 0;
+  while (i < n) {
+    const bool before = affine_node(nodes[i]) && i + 1 < n && nodes[i + 1].kind == NP_CAST_F16;
+    if (!before && nodes[i].kind != NP_CAST_F16) {
+      out.push_back(emit(nodes[i]));
+      ++i;
+      continue;
+    }
+    std::string l = "{ const _Float16 h = ";
+    if (before) {
+      const Node& f = nodes[i];
+      if (f.kind == NP_MUL_C)
+        l += "np_mul_to_f16(v, " + hexf((float)f.m) + "); ";
+      else if (f.kind == NP_ADD_C)
+        l += "np_add_to_f16(v, " + hexf((float)f.b) + "); ";
+      else
+        l += "np_fma_to_f16(v, " + hexf((float)f.m) + ", " + hexf((float)f.b) + "); ";
+      i += 2;  // the op and the cast
+    } else {
+      l += "(_Float16)v; ";
+      i += 1;
+    }
+    const Node* g = i < n ? &nodes[i] : nullptr;
+    if (g && g->kind == K_FMA) {
+      l += "v = np_fma_from_f16(h, " + hexf((float)g->m) + ", " + hexf((float)g->b) + "); }";
+      ++i;
+    } else if (g && g->kind == NP_MUL_C) {
+      l += "v = np_mul_from_f16(h, " + hexf((float)g->m) + "); }";
+      ++i;
+    } else if (g && g->kind == K_EXPA && g->b == 1.0) {
+      l += "v = __builtin_amdgcn_exp2f(np_mul_from_f16(h, " + hexf((float)g->m) + ")); }";
+      ++i;
+    } else {
+      l += "v = (float)h; }";
+    }
+    out.push_back(l);
+  }
+  return out;
+}
+
 struct Entry {
   hipModule_t mod = nullptr;
   hipFunction_t fn = nullptr;         // vector kernel
@@ -402,7 +454,7 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "const float* x" << j;
   s << ", int e) {\n  float v = 0.0f;\n";
   if (fast) {
-    for (const Node& nd : fold_fast(a)) s << "  " << emit(nd) << "\n";
+    for (const std::string& l : emit_all(fold_fast(a))) s << "  " << l << "\n";
   } else {
     for (int i = 0; i < a.n_ops; ++i)
       s << "  " << op_line(a.kind[i], a.arg[i], a.c[i], fast) << "\n";
