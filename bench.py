@@ -152,22 +152,6 @@ def time_calls(torch, fn, reps: int, trials: int):
     return res[len(res) // 2], res[max(0, len(res) // 10)], res[min(len(res) - 1, (9 * len(res)) // 10)]
 
 
-def time_isolated(torch, fn, reps: int):
-    """Mean per-launch duration with an event pair around every launch: the
-    marker between launches keeps consecutive kernels from overlapping, so this
-    is the kernel's own duration (what rocprofv3's kernel trace reports)."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    fn()
-    torch.cuda.synchronize()
-    for s, e in ev:
-        s.record()
-        fn()
-        e.record()
-    torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in ev) / reps / 1e3
-
-
 def graph_time(torch, npa, spec, reps: int, trials: int):
     """Per-replay seconds of one call's launches captured in one HIP graph
     (bound inside the capture, so the launches go to the capturing stream)."""
@@ -494,24 +478,48 @@ def main(argv=None):
     step_fns = [W[k]["fused"] for k in order]
     step_bytes = sum(W[k]["bytes"] for k in order)
 
-    def step():
-        for f in step_fns:
-            f()
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
+    # warm-up steps, each call bracketed by events: the step's dominant kernel
+    # (the config with the longest call) is the one the roofline times below
+    warm = {k: [] for k in order}
+    for _ in range(max(args.warmup, 1)):
+        pairs = []
+        for k, f in zip(order, step_fns):
+            a, b = ev(), ev()
+            a.record()
+            f()
+            b.record()
+            pairs.append((k, a, b))
+        torch.cuda.synchronize()
+        for k, a, b in pairs:
+            warm[k].append(a.elapsed_time(b))
+    dom = max(order, key=lambda k: sum(warm[k]) / len(warm[k]))
+
+    # the timed steps; the dominant kernel's launch inside each step is
+    # bracketed by its own event pair on the same (current) stream, so its
+    # per-launch duration is measured over the timed region itself
+    dom_ev = [(ev(), ev()) for _ in range(args.steps)]
+    s = ev()
+    e = ev()
     t0 = time.perf_counter()
     s.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        for k, f in zip(order, step_fns):
+            if k == dom:
+                dom_ev[i][0].record()
+                f()
+                dom_ev[i][1].record()
+            else:
+                f()
     e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_s = s.elapsed_time(e) / 1e3 / args.steps
-    log(f"[bench] {args.steps} steps: {step_s * 1e6:.1f} us/step (wall {wall:.3f}s)")
+    t_dom = sum(a.elapsed_time(b) for a, b in dom_ev) / args.steps / 1e3
+    log(f"[bench] {args.steps} steps: {step_s * 1e6:.1f} us/step (wall {wall:.3f}s); "
+        f"{dom} {t_dom * 1e6:.1f} us per launch in the step")
 
     per = {}
     extra = [k for k in W if k not in order]
@@ -597,9 +605,7 @@ def main(argv=None):
     # roofline of the dominant kernel of the step: HBM for the streaming
     # kernels; the 29-op chain is bound by VALU issue (its algorithmic slots
     # per element far exceed the ~20 that 8 TB/s leaves per fp16 element)
-    dom = max(order, key=lambda k: per[k]["us_med"])
     d = per[dom]
-    t_dom = time_isolated(torch, W[dom]["fused"], 20)
     hbm_frac = d["bytes"] / t_dom / 1e9 / HBM_PEAK_GBPS
     if dom.startswith("c5"):
         n_el = d["bytes"] // 4

@@ -437,6 +437,13 @@ int compile(const std::string& src, std::vector<char>* code, std::string* log) {
 
 }  // namespace
 
+// Kernel names carry the op count and the size written in (0: size at launch),
+// so a profiler tells the specialisations apart.
+static std::string spec_name(const ChainArgs& a, int64_t n, bool scalar) {
+  return std::string(scalar ? "np_chain_scalar" : "np_chain_spec") + "_k" +
+         std::to_string(a.n_ops) + "_n" + std::to_string(n);
+}
+
 std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, int64_t n) {
   const int G = (in_dt != NP_F32 || out_dt != NP_F32) ? 8 : 4;
   const bool fast = out_dt == NP_F16;  // same transcendental policy as the generic kernel
@@ -462,7 +469,7 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
   s << "  return v;\n}\n";
   // vector kernel: one group of NPS_G elements per thread, dwordx4 accesses,
   // non-temporal stores; the < NPS_G leftover elements go to the first threads
-  s << "extern \"C\" __global__ __launch_bounds__(256) void np_chain_spec(";
+  s << "extern \"C\" __global__ __launch_bounds__(256) void " << spec_name(a, n, false) << "(";
   for (int j = 0; j < n_inputs; ++j) s << "const tin* in" << j << ", ";
   s << "tout* out, long long n_rt) {\n"
     << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
@@ -499,7 +506,7 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "x" << j;
   s << ", 0);\n  }\n}\n";
   // scalar kernel: one element per thread (small n, where it fills the chip better)
-  s << "extern \"C\" __global__ __launch_bounds__(256) void np_chain_spec_scalar(";
+  s << "extern \"C\" __global__ __launch_bounds__(256) void " << spec_name(a, n, true) << "(";
   for (int j = 0; j < n_inputs; ++j) s << "const tin* in" << j << ", ";
   s << "tout* out, long long n_rt) {\n"
     << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
@@ -544,8 +551,8 @@ int rtc_prepare(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, std::st
   Entry e;
   e.src_hash = h;
   if (hipModuleLoadData(&e.mod, code.data()) != hipSuccess ||
-      hipModuleGetFunction(&e.fn, e.mod, "np_chain_spec") != hipSuccess ||
-      hipModuleGetFunction(&e.fn_scalar, e.mod, "np_chain_spec_scalar") != hipSuccess) {
+      hipModuleGetFunction(&e.fn, e.mod, spec_name(a, a.n, false).c_str()) != hipSuccess ||
+      hipModuleGetFunction(&e.fn_scalar, e.mod, spec_name(a, a.n, true).c_str()) != hipSuccess) {
     *log = "module load failed";
     if (e.mod) (void)hipModuleUnload(e.mod);
     return NP_ELAUNCH;
