@@ -35,24 +35,29 @@ __global__ __launch_bounds__(kTokBlock) void rope_tok(RopeArgs a) {
   constexpr int E = Vec<T>::N;  // elements per 16-byte chunk; D == 16 * E here
   constexpr int HALF = 8 * E;
   // cos / sin of the token's angles, plain (K) and multiplied by q_scale (Q)
+  static_assert(HALF <= kTokBlock, "one angle per thread at most");
   __shared__ float tab[4][HALF];
   const int64_t t = blockIdx.x;
+  // the angle inputs, then the row's loads, then the angle table: waits count
+  // loads in issue order, so the table is computed while the row is in flight
+  const int ia = threadIdx.x;  // this thread's angle, if any
   const float p = a.pos ? (float)a.pos[t] : (float)t;
-  for (int i = threadIdx.x; i < HALF; i += kTokBlock) {
-    float sv, cv;
-    sincosf(p * a.inv[i], &sv, &cv);  // theta = fp32(pos) * inv_i: one fp32 multiply
-    tab[0][i] = cv;
-    tab[1][i] = sv;
-    tab[2][i] = cv * a.q_scale;
-    tab[3][i] = sv * a.q_scale;
-  }
+  const float inv = ia < HALF ? a.inv[ia] : 0.0f;
   const int total = 3 * a.H * 16;  // chunks in the token's packed row
   const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.qkv)) + t * total;
   u32x4 raw[NC];
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = threadIdx.x + i * kTokBlock;
-    raw[i] = load_raw(src + (c < total ? c : 0));
+  for (int q = 0; q < NC; ++q) {
+    const int c = threadIdx.x + q * kTokBlock;
+    raw[q] = load_raw(src + (c < total ? c : 0));
+  }
+  if (ia < HALF) {
+    float sv, cv;
+    sincosf(p * inv, &sv, &cv);  // theta = fp32(pos) * inv_i: one fp32 multiply
+    tab[0][ia] = cv;
+    tab[1][ia] = sv;
+    tab[2][ia] = cv * a.q_scale;
+    tab[3][ia] = sv * a.q_scale;
   }
   __syncthreads();
   const int l16 = threadIdx.x & 15;

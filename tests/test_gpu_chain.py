@@ -223,6 +223,41 @@ def test_specialised_every_fp16_input(npa, orc, seed):
         npa.np_shutdown()
 
 
+RARE_FORMS = [
+    # tanh of an argument >= 1 (exp then + 1): the exponential form, no branch
+    ([(synth.LOAD, 0, 0.0), (synth.EXP, 0, 0.0), (synth.ADD_C, 0, 1.0), (synth.TANH, 0, 0.0)],
+     "np_fast_tanh_exp_pos(", True),
+    # tanh of an argument <= -0.7 (-exp - 0.7): the negative exponential form
+    ([(synth.LOAD, 0, 0.0), (synth.EXP, 0, 0.0), (synth.MUL_C, 0, -1.0), (synth.ADD_C, 0, -0.7),
+      (synth.TANH, 0, 0.0)], "np_fast_tanh_exp_neg(", True),
+    # an exp whose following factor is zero keeps the plain scaled form
+    ([(synth.LOAD, 0, 0.0), (synth.EXP, 0, 0.0), (synth.MUL_C, 0, 0.0), (synth.ADD_C, 0, 0.5),
+      (synth.TANH, 0, 0.0)], "np_fast_exp_affine(", False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RARE_FORMS)))
+def test_specialised_rare_forms(npa, orc, case):
+    """Forms the seeded chains seldom produce: each hand-made chain must
+    generate the named form and match the oracle (every non-NaN fp16 input
+    where the chain's output is finite for all of them, N(0, 1) draws
+    otherwise)."""
+    ops, form, every_input = RARE_FORMS[case]
+    src = npa.np_chain_source(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    assert form in src[src.index("float chain("):src.index("return v;")]
+    if every_input:
+        x = np.arange(1 << 16, dtype=np.uint16).view(np.float16)
+        x = x[~np.isnan(x)]
+    else:
+        x = synth.c5_inputs(65536 + 7, seed=77)
+    npa.fuse_chain_prepare(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    try:
+        _c5(npa, orc, x, ops)
+    finally:
+        torch.cuda.synchronize()
+        npa.np_shutdown()
+
+
 def test_c5_large_sampled_specialised(npa, orc):
     """The bench's launch: the prepared (folded) kernel on 2^28 elements,
     sampled outputs against the oracle."""
