@@ -75,6 +75,7 @@ def rope_bytes(T, H, D, es=2):
     return 6 * q, 6 * q + 2 * q + 2 * q + 2 * q
 
 
+SETTLE_S = 0.25  # seconds of untimed steps before the warm-up steps
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 VALU_PEAK = 256 * 64 * 2.4e9  # lane-instr/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
 
@@ -480,6 +481,16 @@ def main(argv=None):
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
+
+    # clock settle (set-up, untimed): the GPU ramps its clocks over the first
+    # tens of milliseconds of sustained load (the 2^28-element chain runs
+    # ~500 us per launch at first, ~400 us once settled), so the step runs for
+    # SETTLE_S seconds before the warm-up steps and the timed ones
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for f in step_fns:
+            f()
+        torch.cuda.synchronize()
 
     # warm-up steps, each call bracketed by events: the step's dominant kernel
     # (the config with the longest call) is the one the roofline times below
