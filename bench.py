@@ -487,10 +487,12 @@ def main(argv=None):
     # ~500 us per launch at first, ~400 us once settled), so the step runs for
     # SETTLE_S seconds before the warm-up steps and the timed ones
     t_settle = time.perf_counter()
+    settle_steps = 0
     while time.perf_counter() - t_settle < SETTLE_S:
         for f in step_fns:
             f()
         torch.cuda.synchronize()
+        settle_steps += 1
 
     # warm-up steps, each call bracketed by events: the step's dominant kernel
     # (the config with the longest call) is the one the roofline times below
@@ -664,7 +666,8 @@ def main(argv=None):
     out = {
         "metric": "achieved HBM GB/s (% of peak) + per-call us, fused vs N-launch unfused",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
+        "warmup": args.warmup, "settle_steps": settle_steps,
+        "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded Philox normals; see synth/)",
         "config": {"workload": "one fused pass over all five chains: C1 fp32 relu(a+b)*0.5 1M; "
