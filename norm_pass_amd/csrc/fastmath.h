@@ -68,15 +68,20 @@ NP_FM_INLINE float np_fast_sigmoid_affine(float x, float c, float e) {
 // tanh for |x| < 0.625: the odd polynomial evaluated on x itself. Every step is
 // symmetric under a sign change, so this equals the |x| form with the sign put
 // back, except that -0 gives +0.
-NP_FM_INLINE float np_fast_tanh_poly(float x) {
+#define NP_TANH_P4 -0.005704987328499556f  // leading coefficient of P
+
+// k4: P's leading coefficient, passed in so that a caller can keep it in a
+// register (two constants in one FMA need one of them in a vector register)
+NP_FM_INLINE float np_fast_tanh_poly_k(float x, float k4) {
   const float z = x * x;
-  float p = -0.005704987328499556f;
-  p = __builtin_fmaf(p, z, 0.0206390880048275f);
+  float p = __builtin_fmaf(k4, z, 0.0206390880048275f);
   p = __builtin_fmaf(p, z, -0.05373971536755562f);
   p = __builtin_fmaf(p, z, 0.13331441581249237f);
   p = __builtin_fmaf(p, z, -0.3333328068256378f);
   return __builtin_fmaf(x * z, p, x);
 }
+
+NP_FM_INLINE float np_fast_tanh_poly(float x) { return np_fast_tanh_poly_k(x, NP_TANH_P4); }
 
 // tanh for x >= 0.625 (and +inf): 1 - 2 / (1 + e^(2x)), e^(2x) = 2^(2x log2 e).
 NP_FM_INLINE float np_fast_tanh_exp_pos(float x) {
@@ -91,35 +96,40 @@ NP_FM_INLINE float np_fast_tanh_exp_neg(float x) {
   return __builtin_fmaf(2.0f, __builtin_amdgcn_rcpf(1.0f + e), -1.0f);
 }
 
-NP_FM_INLINE float np_fast_tanh(float x) {
+NP_FM_INLINE float np_fast_tanh_k(float x, float k4) {
   const float a = __builtin_fabsf(x);
   float r;
   if (a < 0.625f)  // a branch, not a select: a wave whose lanes agree runs one side
-    r = np_fast_tanh_poly(a);
+    r = np_fast_tanh_poly_k(a, k4);
   else
     r = np_fast_tanh_exp_pos(a);
   return __builtin_copysignf(r, x);
 }
 
+NP_FM_INLINE float np_fast_tanh(float x) { return np_fast_tanh_k(x, NP_TANH_P4); }
+
 // tanh when the sign of x is known (x >= 0, x <= 0): one branch, no sign
 // handling. NaN takes the exponential side and stays NaN.
-NP_FM_INLINE float np_fast_tanh_pos(float x) {
+NP_FM_INLINE float np_fast_tanh_pos_k(float x, float k4) {
   float r;
   if (x < 0.625f)
-    r = np_fast_tanh_poly(x);
+    r = np_fast_tanh_poly_k(x, k4);
   else
     r = np_fast_tanh_exp_pos(x);
   return r;
 }
 
-NP_FM_INLINE float np_fast_tanh_neg(float x) {
+NP_FM_INLINE float np_fast_tanh_neg_k(float x, float k4) {
   float r;
   if (x > -0.625f)
-    r = np_fast_tanh_poly(x);
+    r = np_fast_tanh_poly_k(x, k4);
   else
     r = np_fast_tanh_exp_neg(x);
   return r;
 }
+
+NP_FM_INLINE float np_fast_tanh_pos(float x) { return np_fast_tanh_pos_k(x, NP_TANH_P4); }
+NP_FM_INLINE float np_fast_tanh_neg(float x) { return np_fast_tanh_neg_k(x, NP_TANH_P4); }
 
 // Casts to fp16 merged with the affine ops around them (fp16-output chains, by
 // the runtime specialiser), on gfx950's mixed-precision FMAs:
@@ -158,4 +168,13 @@ NP_FM_INLINE float np_mul_from_f16(_Float16 h, float m) {
   float r;
   asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "s"(m));
   return r;
+}
+
+// An opaque copy of x in a vector register. Generated kernels pin the
+// constants an instruction cannot take as a literal (gfx9 allows one literal or
+// scalar operand per instruction) once per thread: left to itself, the compiler
+// rematerialises them with a move for every element it unrolls.
+NP_FM_INLINE float np_pin(float x) {
+  asm("" : "+v"(x));
+  return x;
 }

@@ -159,6 +159,20 @@ std::vector<Range> op_ranges(const ChainArgs& a) {
   return before;
 }
 
+// ---- constants held in vector registers -------------------------------------
+// Operands that cannot be literals (a second constant in one FMA, the addend of
+// a mixed-precision FMA) are pinned once per thread, kp[i] = np_pin(c), and
+// referred to by index in the chain, so the unrolled elements share them.
+struct Pins {
+  std::vector<float> v;
+  std::string ref(float c) {
+    for (size_t i = 0; i < v.size(); ++i)
+      if (std::memcmp(&v[i], &c, 4) == 0) return "kp[" + std::to_string(i) + "]";
+    v.push_back(c);
+    return "kp[" + std::to_string(v.size() - 1) + "]";
+  }
+};
+
 // ---- tanh on a known range -------------------------------------------------
 // Odd Taylor series tanh x = x + sum_k T_k x^(2k+1) (coefficients from the
 // Bernoulli numbers: -1/3, 2/15, -17/315, 62/2835, -1382/155925). For
@@ -170,8 +184,11 @@ std::vector<Range> op_ranges(const ChainArgs& a) {
 constexpr double kTanhT[6] = {1.0,           -1.0 / 3.0,       2.0 / 15.0,
                               -17.0 / 315.0, 62.0 / 2835.0,   -1382.0 / 155925.0};
 constexpr double kTanhTau = 0x1p-26;
+// the leading coefficient of the minimax polynomial in fastmath.h (NP_TANH_P4),
+// which the generated code passes to np_fast_tanh_*_k from a pinned register
+constexpr float kTanhP4 = -0.005704987328499556f;
 
-std::string tanh_on(const Range& r) {
+std::string tanh_on(const Range& r, Pins* pins) {
   const double m = std::fmax(std::fabs(r.lo), std::fabs(r.hi));
   const double shrink = 1.0 / (1.0 - m * m / 3.0);
   if (m <= 0.5) {
@@ -180,17 +197,18 @@ std::string tanh_on(const Range& r) {
       if (std::fabs(kTanhT[k + 1]) * std::pow(m, 2 * k + 2) * shrink > kTanhTau) continue;
       std::string l = "{ const float z = v * v; ";
       if (k == 1) return l + "v = __builtin_fmaf(v * z, " + hexf((float)kTanhT[1]) + ", v); }";
-      l += "float p = " + hexf((float)kTanhT[k]) + "; ";
+      l += "float p = " + pins->ref((float)kTanhT[k]) + "; ";
       for (int j = k - 1; j >= 1; --j) l += "p = __builtin_fmaf(p, z, " + hexf((float)kTanhT[j]) + "); ";
       return l + "v = __builtin_fmaf(v * z, p, v); }";
     }
   }
-  if (m < 0.625) return "v = np_fast_tanh_poly(v);";
   if (r.lo >= 0.625) return "v = np_fast_tanh_exp_pos(v);";
   if (r.hi <= -0.625) return "v = np_fast_tanh_exp_neg(v);";
-  if (r.lo >= 0.0) return "v = np_fast_tanh_pos(v);";
-  if (r.hi <= 0.0) return "v = np_fast_tanh_neg(v);";
-  return "v = np_fast_tanh(v);";
+  const std::string k4 = pins->ref(kTanhP4);
+  if (m < 0.625) return "v = np_fast_tanh_poly_k(v, " + k4 + ");";
+  if (r.lo >= 0.0) return "v = np_fast_tanh_pos_k(v, " + k4 + ");";
+  if (r.hi <= 0.0) return "v = np_fast_tanh_neg_k(v, " + k4 + ");";
+  return "v = np_fast_tanh_k(v, " + k4 + ");";
 }
 
 // ---- folded op list --------------------------------------------------------
@@ -301,7 +319,7 @@ std::vector<Node> fold_fast(const ChainArgs& a) {
   return out;
 }
 
-std::string emit(const Node& n) {
+std::string emit(const Node& n, Pins* pins) {
   switch (n.kind) {
     case K_FMA:
       return "v = __builtin_fmaf(v, " + hexf((float)n.m) + ", " + hexf((float)n.b) + ");";
@@ -310,17 +328,18 @@ std::string emit(const Node& n) {
       if (n.b == 0.0)
         return "v = np_fast_exp_affine(v, " + hexf((float)n.m) + ", " + hexf(0.0f) + ");";
       const std::string call = "np_fast_exp_shifted(v, " + hexf((float)n.m) + ", " +
-                               hexf((float)std::log2(std::fabs(n.b))) + ")";
+                               pins->ref((float)std::log2(std::fabs(n.b))) + ")";
       return n.b < 0.0 ? "v = -" + call + ";" : "v = " + call + ";";
     }
     case K_SIGA:
-      return "v = np_fast_sigmoid_affine(v, " + hexf((float)n.m) + ", " + hexf((float)n.b) + ");";
+      return "v = np_fast_sigmoid_affine(v, " + hexf((float)n.m) + ", " + pins->ref((float)n.b) +
+             ");";
     case NP_MUL_C: return "v = v * " + hexf((float)n.m) + ";";
     case NP_ADD_C: return "v = v + " + hexf((float)n.b) + ";";
     case NP_TANH: {
       char buf[96];
       std::snprintf(buf, sizeof buf, "// tanh argument in [%a, %a]", n.in.lo, n.in.hi);
-      const std::string f = tanh_on(n.in);
+      const std::string f = tanh_on(n.in, pins);
       return std::string(buf) + (f.empty() ? " (tanh x = x there)" : "\n  " + f);
     }
     default: return op_line(n.kind, n.arg, (float)n.m, true);
@@ -336,14 +355,14 @@ bool affine_node(const Node& n) {
   return n.kind == NP_MUL_C || n.kind == NP_ADD_C || n.kind == K_FMA;
 }
 
-std::vector<std::string> emit_all(const std::vector<Node>& nodes) {
+std::vector<std::string> emit_all(const std::vector<Node>& nodes, Pins* pins) {
   std::vector<std::string> out;
   const size_t n = nodes.size();
   size_t i = 0;
   while (i < n) {
     const bool before = affine_node(nodes[i]) && i + 1 < n && nodes[i + 1].kind == NP_CAST_F16;
     if (!before && nodes[i].kind != NP_CAST_F16) {
-      out.push_back(emit(nodes[i]));
+      out.push_back(emit(nodes[i], pins));
       ++i;
       continue;
     }
@@ -355,7 +374,7 @@ std::vector<std::string> emit_all(const std::vector<Node>& nodes) {
       else if (f.kind == NP_ADD_C)
         l += "np_add_to_f16(v, " + hexf((float)f.b) + "); ";
       else
-        l += "np_fma_to_f16(v, " + hexf((float)f.m) + ", " + hexf((float)f.b) + "); ";
+        l += "np_fma_to_f16(v, " + hexf((float)f.m) + ", " + pins->ref((float)f.b) + "); ";
       i += 2;  // the op and the cast
     } else {
       l += "(_Float16)v; ";
@@ -363,7 +382,7 @@ std::vector<std::string> emit_all(const std::vector<Node>& nodes) {
     }
     const Node* g = i < n ? &nodes[i] : nullptr;
     if (g && g->kind == K_FMA) {
-      l += "v = np_fma_from_f16(h, " + hexf((float)g->m) + ", " + hexf((float)g->b) + "); }";
+      l += "v = np_fma_from_f16(h, " + hexf((float)g->m) + ", " + pins->ref((float)g->b) + "); }";
       ++i;
     } else if (g && g->kind == NP_MUL_C) {
       l += "v = np_mul_from_f16(h, " + hexf((float)g->m) + "); }";
@@ -459,14 +478,22 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
     << "#define NPS_OUT_PER_VEC " << 16 / (out_dt == NP_F32 ? 4 : 2) << "\n"
     << "__device__ __forceinline__ float chain(";
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "const float* x" << j;
-  s << ", int e) {\n  float v = 0.0f;\n";
+  s << ", int e, const float* kp) {\n  float v = 0.0f;\n";
+  Pins pins;
   if (fast) {
-    for (const std::string& l : emit_all(fold_fast(a))) s << "  " << l << "\n";
+    for (const std::string& l : emit_all(fold_fast(a), &pins)) s << "  " << l << "\n";
   } else {
     for (int i = 0; i < a.n_ops; ++i)
       s << "  " << op_line(a.kind[i], a.arg[i], a.c[i], fast) << "\n";
   }
   s << "  return v;\n}\n";
+  // the pinned constants, once per thread
+  std::string kp_decl = "  const float* const kp = nullptr;\n";
+  if (!pins.v.empty()) {
+    kp_decl = "  const float kp[" + std::to_string(pins.v.size()) + "] = {";
+    for (size_t i = 0; i < pins.v.size(); ++i) kp_decl += (i ? ", np_pin(" : "np_pin(") + hexf(pins.v[i]) + ")";
+    kp_decl += "};\n";
+  }
   // vector kernel: one group of NPS_G elements per thread, dwordx4 accesses,
   // non-temporal stores; the < NPS_G leftover elements go to the first threads
   s << "extern \"C\" __global__ __launch_bounds__(256) void " << spec_name(a, n, false) << "(";
@@ -475,6 +502,7 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
     << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
     << "  const long long ngroups = n / NPS_G;\n"
     << "  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;\n"
+    << kp_decl
     << "  if (g < ngroups) {\n";
   for (int j = 0; j < n_inputs; ++j) {
     s << "    float x" << j << "[NPS_G];\n"
@@ -491,7 +519,7 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
     << "#pragma unroll\n"
     << "    for (int e = 0; e < NPS_G; ++e) o[e] = (tout)chain(";
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "x" << j;
-  s << ", e);\n"
+  s << ", e, kp);\n"
     << "#pragma unroll\n"
     << "    for (int q = 0; q < NPS_G / NPS_OUT_PER_VEC; ++q) {\n"
     << "      u32x4 raw; __builtin_memcpy(&raw, o + q * NPS_OUT_PER_VEC, 16);\n"
@@ -504,18 +532,19 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
   for (int j = 0; j < n_inputs; ++j) s << "    float x" << j << "[1] = {(float)in" << j << "[i]};\n";
   s << "    out[i] = (tout)chain(";
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "x" << j;
-  s << ", 0);\n  }\n}\n";
+  s << ", 0, kp);\n  }\n}\n";
   // scalar kernel: one element per thread (small n, where it fills the chip better)
   s << "extern \"C\" __global__ __launch_bounds__(256) void " << spec_name(a, n, true) << "(";
   for (int j = 0; j < n_inputs; ++j) s << "const tin* in" << j << ", ";
   s << "tout* out, long long n_rt) {\n"
     << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
     << "  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;\n"
-    << "  if (i >= n) return;\n";
+    << "  if (i >= n) return;\n"
+    << kp_decl;
   for (int j = 0; j < n_inputs; ++j) s << "  float x" << j << "[1] = {(float)in" << j << "[i]};\n";
   s << "  out[i] = (tout)chain(";
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "x" << j;
-  s << ", 0);\n}\n";
+  s << ", 0, kp);\n}\n";
   return s.str();
 }
 

@@ -60,9 +60,9 @@ def test_seed29_tanh_forms(npa):
     ranges, src = tanh_ranges(npa, synth.c5_chain())
     assert len(ranges) == 5
     body = src[src.index("float chain("):src.index("return v;")]
-    assert "np_fast_tanh(" not in body
+    assert "np_fast_tanh_k(" not in body
     assert ranges[0][1] == 0.0 and all(lo > 0 and hi < 0.625 for lo, hi in ranges[1:])
-    assert body.count("np_fast_tanh_neg(") == 1 and body.count("np_fast_tanh_poly(") == 1
+    assert body.count("np_fast_tanh_neg_k(") == 1 and body.count("np_fast_tanh_poly_k(") == 1
 
 
 def test_general_tanh_when_the_range_is_unknown(npa):
@@ -70,10 +70,10 @@ def test_general_tanh_when_the_range_is_unknown(npa):
     tanh after an exp (argument >= 0) takes the one-signed one."""
     ops = [(synth.LOAD, 0, 0.0), (synth.TANH, 0, 0.0)]
     ranges, src = tanh_ranges(npa, ops)
-    assert ranges == [(-np.inf, np.inf)] and "np_fast_tanh(v)" in src
+    assert ranges == [(-np.inf, np.inf)] and "np_fast_tanh_k(v, " in src
     ops = [(synth.LOAD, 0, 0.0), (synth.EXP, 0, 0.0), (synth.TANH, 0, 0.0)]
     ranges, src = tanh_ranges(npa, ops)
-    assert ranges[0][0] == 0.0 and "np_fast_tanh_pos(v)" in src
+    assert ranges[0][0] == 0.0 and "np_fast_tanh_pos_k(v, " in src
 
 
 def test_identity_for_tiny_arguments(npa):
@@ -82,3 +82,22 @@ def test_identity_for_tiny_arguments(npa):
            (synth.TANH, 0, 0.0)]
     ranges, src = tanh_ranges(npa, ops)
     assert ranges[1][1] <= 2.0 ** -13 and "(tanh x = x there)" in src
+
+
+def test_pinned_tanh_coefficient_matches_fastmath(npa):
+    """The specialiser passes the minimax polynomial's leading coefficient to
+    np_fast_tanh_*_k from a pinned register: its value must be the one
+    fastmath.h's own np_fast_tanh_poly uses (NP_TANH_P4)."""
+    import os
+    import struct
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "norm_pass_amd", "csrc", "fastmath.h")).read()
+    m = re.search(r"#define NP_TANH_P4 (\S+)f", hdr)
+    want = struct.unpack("f", struct.pack("f", float(m.group(1))))[0]
+    ops = [(synth.LOAD, 0, 0.0), (synth.TANH, 0, 0.0)]
+    src = npa.np_chain_source(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    k = re.search(r"np_fast_tanh_k\(v, kp\[(\d+)\]\)", src)
+    pins = re.search(r"const float kp\[\d+\] = \{([^}]*)\}", src).group(1)
+    # np_pin(<hex float>f): the exponent is decimal, so the only trailing f is the suffix
+    vals = [float.fromhex(p.strip()[len("np_pin("):-1].rstrip("f")) for p in pins.split(",")]
+    assert vals[int(k.group(1))] == want
