@@ -414,6 +414,29 @@ def cpu_baseline(synth, quick: bool):
     xl = synth.c5_inputs(nl, seed=77)
     rates["c5_large"] = 4 * nl / timed(lambda: oracle.chain(ops, [xl], 1))
     samples.append(f"c5 {nl:,} of 268,435,456 elements")
+    # the next rows (not in the step): the same oracle, each on its own sample
+    # (their GPU figures are reported beside these)
+    gam = synth.normal((4096,), 1013, "bf16", mean=1.0, std=0.1)
+    bet = synth.normal((4096,), 1014, "bf16", std=0.1)
+    rates["ln"] = ln_bytes(rows, 4096)[0] / timed(
+        lambda: oracle.add_layernorm(x, r, gam, bet, 1e-5, 2))
+    samples.append(f"ln {rows} of 16384 rows")
+    tr_rows = 256 if quick else 1024
+    xt = synth.transpose_inputs((1, tr_rows, 8192, 1))
+    rates["tr"] = 2 * xt.nbytes / timed(lambda: oracle.transpose021(xt))
+    samples.append(f"tr {tr_rows} of 8192 rows")
+    nb = 16 if quick else 128
+    for name, layout in (("shuffle_nchw", 0), ("shuffle_nhwc", 1)):
+        xs_ = synth.shuffle_inputs((nb,) + synth.SHUFFLE_NCHW[1:], layout=layout)
+        rates[name] = 2 * xs_.nbytes / timed(
+            lambda: oracle.channel_shuffle(xs_, synth.SHUFFLE_GROUPS, layout))
+        samples.append(f"{name} batch {nb} of 1024")
+    mr = 2 if quick else 8
+    xr, wr, Wr, br = synth.rmsnorm_linear_inputs()
+    M, K, N = synth.RMS_LINEAR_SHAPE
+    rates["rl_flops"] = 2 * mr * K * N / timed(
+        lambda: oracle.rmsnorm_linear(xr[:mr], wr, Wr, br, 1e-6, synth.RMS_LINEAR_SCALE, 2))
+    samples.append(f"rl {mr} of {M} rows (flop/s)")
     return rates, "; ".join(samples)
 
 
@@ -658,8 +681,19 @@ def main(argv=None):
         est = sum(W[k]["bytes"] / rates[k] for k in order)
         cpu = {"value": round(step_bytes / est / 1e9, 4), "unit": "GB/s", "cores": 1,
                "kind": "oracle", "sample": sample,
-               "per_config_GBps": {k: round(v / 1e9, 4) for k, v in rates.items()},
+               "per_config_GBps": {k: round(v / 1e9, 4) for k, v in rates.items()
+                                   if k != "rl_flops"},
+               "rl_GFLOPs": round(rates["rl_flops"] / 1e9, 4),
                "seconds": round(time.perf_counter() - t0, 1)}
+        # beside each row's GPU figure: the oracle's rate on its sample
+        for k in order + extra:
+            if k in rates:
+                per[k]["cpu_oracle_GBps"] = round(rates[k] / 1e9, 4)
+                per[k]["gpu_over_cpu_oracle"] = round(per[k]["GBps"] * 1e9 / rates[k], 1)
+        if "rl" in per:
+            per["rl"]["cpu_oracle_GFLOPs"] = round(rates["rl_flops"] / 1e9, 4)
+            per["rl"]["gpu_over_cpu_oracle"] = round(
+                per["rl"]["TFLOPs"] * 1e12 / rates["rl_flops"], 1)
         log(f"[bench] cpu oracle {cpu['value']} GB/s ({cpu['seconds']} s)")
 
     value = step_bytes / step_s / 1e9

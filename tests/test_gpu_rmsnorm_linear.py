@@ -198,3 +198,19 @@ def test_empty_and_rejects(npa):
     with pytest.raises(npa.NPError):  # misaligned x
         npa.fuse_rmsnorm_linear(buf[1:1 + 256].view(4, 64), None, Wt, None,
                                 torch.zeros(4, 32, dtype=torch.bfloat16, device="cuda"))
+
+
+@pytest.mark.parametrize("with_w", [False, True])
+def test_deterministic(npa, with_w):
+    """Two runs on the same inputs give bit-identical outputs (fixed MFMA and
+    row-sum order; no atomics)."""
+    M, N, K = 513, 257, 192
+    x, w, Wt, b = _inputs(M, K, N, 7100, "bf16")
+    outs = []
+    for _ in range(2):
+        out = empty((M, N), "bf16")
+        npa.fuse_rmsnorm_linear(to_dev(x, "bf16"), to_dev(w, "bf16") if with_w else None,
+                                to_dev(Wt, "bf16"), to_dev(b, "bf16"), out, 1e-6, 0.5)
+        torch.cuda.synchronize()
+        outs.append(to_host(out))
+    assert np.array_equal(outs[0], outs[1])
