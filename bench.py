@@ -93,6 +93,7 @@ _CHAIN_SRC = ["norm_pass_amd/csrc/chain.hip", "norm_pass_amd/csrc/device.h",
 KERNEL_SOURCES = {
     "c1": _CHAIN_SRC,
     "c5_large": _CHAIN_SRC,
+    "c5_large_pe": _CHAIN_SRC,  # the 2^28 chain evaluated per element (not its table)
     "c5_small": _CHAIN_SRC,
     "c2": ["norm_pass_amd/csrc/det_decode.hip", "norm_pass_amd/csrc/device.h"],
     "c3": ["norm_pass_amd/csrc/add_rmsnorm.hip", "norm_pass_amd/csrc/device.h"],
@@ -283,15 +284,28 @@ def build_workloads(torch, npa, synth, quick: bool):
     t0 = time.perf_counter()
     npa.fuse_chain_prepare(ops, 1, npa.NP_F16, npa.NP_F16, 0)
     compile_ms["c5"] = round((time.perf_counter() - t0) * 1e3, 1)
+    table_min = npa.np_set_chain_table_min(-1)
     for name, n in (("c5_small", 1 << 16), ("c5_large", (1 << 24) if quick else (1 << 28))):
         xin = tdev(synth.c5_inputs(n), "f16")
         yo = torch.empty_like(xin)
+        fused = npa.bind("fuse_chain", ops, [xin], yo)
+
+        def per_element(fused=fused):
+            # the same call with the table threshold out of reach: the chain
+            # evaluated per element by the specialised kernel
+            old = npa.np_set_chain_table_min(1 << 62)
+            fused()
+            npa.np_set_chain_table_min(old)
+
         W[name] = dict(
             desc=f"seeded 29-op fp16 chain, {n:,} elements",
-            fused=npa.bind("fuse_chain", ops, [xin], yo),
+            fused=fused,
             unfused=npa.bind("unfused_chain", ops, [xin], yo),
             unfused_spec=("unfused_chain", (ops, [xin], yo)),
-            bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29, kernel="chain_vec<_Float16")
+            bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29, kernel="chain_vec<_Float16",
+            path="table" if n >= table_min else "per element")
+        if n >= table_min:
+            W[name]["fused_per_element"] = per_element
     # Layout (the runtime page's strided transpose / ChannelShuffle; not in the
     # step): the LDS-staged kernels against the naive strided copy, and torch's
     # own permute().contiguous() for context. Three buffer sets each for the
@@ -494,6 +508,9 @@ def main(argv=None):
                 w["fused"]()
             for _ in range(2):
                 w["unfused"]()
+        if "c5_large_pe" in only and "fused_per_element" in W["c5_large"]:
+            for _ in range(20):  # the per-element kernel on the same data
+                W["c5_large"]["fused_per_element"]()
         torch.cuda.synchronize()
         log("[bench] profile pass done")
         return 0
@@ -598,6 +615,12 @@ def main(argv=None):
             per[k]["torch_us_med"] = round(t_med * 1e6, 3)
             if w.get("plan") is not None:
                 per[k]["plan"] = w["plan"]
+        if "path" in w:
+            per[k]["path"] = w["path"]
+        if "fused_per_element" in w:
+            pe_med, _, _ = time_calls(torch, w["fused_per_element"], reps, max(5, args.trials // 2))
+            per[k]["per_element_us_med"] = round(pe_med * 1e6, 3)
+            per[k]["per_element_GBps"] = round(w["bytes"] / pe_med / 1e9, 1)
         if "fused_unfolded" in w:
             fu_med, _, _ = time_calls(torch, w["fused_unfolded"], reps, max(5, args.trials // 2))
             per[k]["fused_unfolded_us_med"] = round(fu_med * 1e6, 3)
@@ -643,7 +666,7 @@ def main(argv=None):
     # per element far exceed the ~20 that 8 TB/s leaves per fp16 element)
     d = per[dom]
     hbm_frac = d["bytes"] / t_dom / 1e9 / HBM_PEAK_GBPS
-    if dom.startswith("c5"):
+    if dom.startswith("c5") and W[dom].get("path") != "table":
         n_el = d["bytes"] // 4
         # executed VALU instructions per element from the committed rocprofv3
         # SQ_INSTS_VALU count; none (and no achieved figure) once the kernel
@@ -670,9 +693,11 @@ def main(argv=None):
                                    / HBM_PEAK_GBPS, 4)
     for k in ("c5_small", "c5_large"):
         n_el = per[k]["bytes"] // 4
-        v = measured_valu_per_element(k)
-        per[k]["valu_frac"] = (round(v * n_el / (per[k]["us_med"] * 1e-6) / VALU_PEAK, 4)
-                               if v is not None else None)
+        v = measured_valu_per_element(k if W[k].get("path") != "table" else "c5_large_pe")
+        t_pe = (per[k]["us_med"] if W[k].get("path") != "table"
+                else per[k].get("per_element_us_med"))
+        per[k]["valu_frac"] = (round(v * n_el / (t_pe * 1e-6) / VALU_PEAK, 4)
+                               if v is not None and t_pe else None)
 
     cpu = None
     if not args.no_cpu:

@@ -149,6 +149,23 @@ int fuse_chain_prepare(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt
                        np_dtype out_dt, int64_t n_or_0);
 
 /*
+ * Tabulated chains. A chain over a single fp16 / bf16 input with an fp16 /
+ * bf16 output is a function of the 65,536 input bit patterns: the specialised
+ * module then also holds that function as a table, filled once by
+ * fuse_chain_prepare with the module's own chain code (a launch on a private
+ * stream that prepare waits for), and fuse_chain streams the input through the
+ * table -- one gather per element from a copy staged in LDS -- once n reaches
+ * a threshold (default 2^22; below it staging the 128 KiB table on every CU
+ * costs more than evaluating the chain). The outputs are the same bits as the
+ * per-element kernel's. np_set_chain_table_min sets the threshold for later
+ * calls (INT64_MAX: never use the table) and returns the previous value; a
+ * negative n only returns the current one. This is a specialisation detail,
+ * not a separate operation (the DeepJIT write-up, section 3.3: constants
+ * folded into the generated code at warm-up time, here the whole function).
+ */
+int64_t np_set_chain_table_min(int64_t n);
+
+/*
  * fuse_det_decode: YOLO-style detection-head decode in one kernel (DeepJIT
  * write-up, sections 1.1, 2.2 and 5.2: the sigmoid / exp / mul / add / slice /
  * concat / cast tail of a detector). level_logits[l]: device NCHW tensor

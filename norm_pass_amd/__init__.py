@@ -71,12 +71,14 @@ def _load():
         "fuse_channel_shuffle": [P, P, I64, I64, I64, I64, I64, I, I, P],
         "naive_channel_shuffle": [P, P, I64, I64, I64, I64, I64, I, I, P],
         "np_transpose_plan": [P, P, I64, I64, I64, I64, I, I],
+        "np_set_chain_table_min": [I64],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = (None if name == "np_shutdown" else
-                      C.c_int64 if name == "np_chain_source" else C.c_int)
+                      C.c_int64 if name in ("np_chain_source", "np_set_chain_table_min")
+                      else C.c_int)
     L.np_last_error.restype = C.c_char_p
     L.np_last_error.argtypes = []
     return L
@@ -329,6 +331,13 @@ def fuse_chain(ops, inputs, out, stream=None):
     """out[i] = chain(inputs[0][i], ...); ops = [(kind, arg, const), ...]."""
     _check(_lib.fuse_chain(*_a_fuse_chain(ops, inputs, out, stream)), "fuse_chain")
     return out
+
+
+def np_set_chain_table_min(n: int) -> int:
+    """Element count from which a tabulated chain (one 16-bit input, 16-bit
+    output) runs from its table; returns the previous value. n < 0 only
+    queries; a huge n keeps every call on the per-element kernel."""
+    return int(_lib.np_set_chain_table_min(n))
 
 
 def fuse_chain_prepare(ops, n_inputs: int, in_dt: int, out_dt: int, n: int = 0):

@@ -13,6 +13,7 @@
 
 #include <hip/hiprtc.h>
 
+#include <atomic>
 #include <chrono>
 #include <cfloat>
 #include <cmath>
@@ -402,8 +403,13 @@ struct Entry {
   hipModule_t mod = nullptr;
   hipFunction_t fn = nullptr;         // vector kernel
   hipFunction_t fn_scalar = nullptr;  // one element per thread
+  hipFunction_t fn_lut = nullptr;     // table gather (tabulable chains, table built)
   size_t src_hash = 0;
 };
+
+// From this many elements the table gather wins: below it, staging the
+// 128 KiB table on every CU costs more than evaluating the chain.
+std::atomic<int64_t> g_lut_min_n{int64_t(1) << 22};
 
 // Same threshold as the generic kernel: below it, one element per thread.
 constexpr int64_t kMinVecGroups = 65536;
@@ -458,6 +464,14 @@ int compile(const std::string& src, std::vector<char>* code, std::string* log) {
 
 // Kernel names carry the op count and the size written in (0: size at launch),
 // so a profiler tells the specialisations apart.
+// A chain over one 16-bit input with a 16-bit output is a function of the
+// 65,536 input bit patterns: the specialised module also carries that function
+// as a table (np_lut, filled once at prepare time by the module's own chain
+// code) and a kernel that streams the input through it.
+static bool tabulable(int n_inputs, int in_dt, int out_dt) {
+  return n_inputs == 1 && in_dt != NP_F32 && out_dt != NP_F32;
+}
+
 static std::string spec_name(const ChainArgs& a, int64_t n, bool scalar) {
   return std::string(scalar ? "np_chain_scalar" : "np_chain_spec") + "_k" +
          std::to_string(a.n_ops) + "_n" + std::to_string(n);
@@ -545,6 +559,57 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
   s << "  out[i] = (tout)chain(";
   for (int j = 0; j < n_inputs; ++j) s << (j ? ", " : "") << "x" << j;
   s << ", 0, kp);\n}\n";
+  if (tabulable(n_inputs, in_dt, out_dt)) {
+    const std::string base = spec_name(a, n, false);
+    // the table: out bits for every input bit pattern, by the chain code above
+    s << "__device__ __attribute__((aligned(16))) unsigned short np_lut[65536];\n"
+      << "extern \"C\" __global__ __launch_bounds__(256) void " << base << "_tab(void) {\n"
+      << "  const int i = blockIdx.x * 256 + threadIdx.x;\n"
+      << kp_decl
+      << "  const unsigned short bits = (unsigned short)i;\n"
+      << "  tin x; __builtin_memcpy(&x, &bits, 2);\n"
+      << "  float x0[1] = {(float)x};\n"
+      << "  const tout y = (tout)chain(x0, 0, kp);\n"
+      << "  unsigned short yb; __builtin_memcpy(&yb, &y, 2);\n"
+      << "  np_lut[i] = yb;\n"
+      << "}\n";
+    // the gather kernel: one workgroup per CU stages the 128 KiB table in LDS,
+    // then streams 16-byte vectors through it, four in flight per thread
+    s << "extern \"C\" __global__ __launch_bounds__(1024) void " << base
+      << "_lut(const tin* in0, tout* out, long long n_rt) {\n"
+      << "  __shared__ __attribute__((aligned(16))) unsigned short lut[65536];\n"
+      << "  for (int i = threadIdx.x; i < 8192; i += 1024)\n"
+      << "    reinterpret_cast<u32x4*>(lut)[i] = reinterpret_cast<const u32x4*>(np_lut)[i];\n"
+      << "  __syncthreads();\n"
+      << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
+      << "  const long long nv = n / 8;\n"
+      << "  const long long stride = (long long)gridDim.x * 1024;\n"
+      << "  const u32x4* src = reinterpret_cast<const u32x4*>(in0);\n"
+      << "  u32x4* dst = reinterpret_cast<u32x4*>(out);\n"
+      << "  auto map = [&](u32x4 r) {\n"
+      << "    u32x4 o;\n"
+      << "#pragma unroll\n"
+      << "    for (int j = 0; j < 4; ++j)\n"
+      << "      o[j] = (unsigned)lut[r[j] & 0xffffu] | ((unsigned)lut[r[j] >> 16] << 16);\n"
+      << "    return o;\n"
+      << "  };\n"
+      << "  long long v = (long long)blockIdx.x * 1024 + threadIdx.x;\n"
+      << "  for (; v + 3 * stride < nv; v += 4 * stride) {\n"
+      << "    u32x4 r[4];\n"
+      << "#pragma unroll\n"
+      << "    for (int u = 0; u < 4; ++u) r[u] = src[v + u * stride];\n"
+      << "#pragma unroll\n"
+      << "    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(map(r[u]), dst + v + u * stride);\n"
+      << "  }\n"
+      << "  for (; v < nv; v += stride) __builtin_nontemporal_store(map(src[v]), dst + v);\n"
+      << "  const long long t = nv * 8 + (long long)blockIdx.x * 1024 + threadIdx.x;\n"
+      << "  if (t < n) {\n"
+      << "    unsigned short b; __builtin_memcpy(&b, in0 + t, 2);\n"
+      << "    const unsigned short y = lut[b];\n"
+      << "    __builtin_memcpy(out + t, &y, 2);\n"
+      << "  }\n"
+      << "}\n";
+  }
   return s.str();
 }
 
@@ -586,6 +651,23 @@ int rtc_prepare(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, std::st
     if (e.mod) (void)hipModuleUnload(e.mod);
     return NP_ELAUNCH;
   }
+  if (tabulable(n_inputs, in_dt, out_dt)) {
+    // fill the module's table once (65,536 threads), on a private stream
+    // waited for here: prepare is the warm-up-time call; without a table the
+    // chain is evaluated per element
+    const std::string base = spec_name(a, a.n, false);
+    hipFunction_t tab = nullptr, lut = nullptr;
+    hipStream_t st = nullptr;
+    if (hipModuleGetFunction(&tab, e.mod, (base + "_tab").c_str()) == hipSuccess &&
+        hipModuleGetFunction(&lut, e.mod, (base + "_lut").c_str()) == hipSuccess &&
+        hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess) {
+      if (hipModuleLaunchKernel(tab, 256, 1, 1, 256, 1, 1, 0, st, nullptr, nullptr) == hipSuccess &&
+          hipStreamSynchronize(st) == hipSuccess)
+        e.fn_lut = lut;
+      (void)hipStreamDestroy(st);
+    }
+    (void)hipGetLastError();  // a failed table leaves the per-element kernels in use
+  }
   std::lock_guard<std::mutex> lk(g_mu);
   g_cache[key] = e;
   return NP_OK;
@@ -599,17 +681,28 @@ bool rtc_launch(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, hipStre
   const int64_t ngroups = a.n / G;
   const bool scalar = ngroups < kMinVecGroups;
   hipFunction_t fn = nullptr;
+  bool lut = false;
   {
     std::lock_guard<std::mutex> lk(g_mu);
     if (g_cache.empty()) return false;
     auto it = g_cache.find(spec_key(a, n_inputs, in_dt, out_dt, a.n, dev));
     if (it == g_cache.end()) it = g_cache.find(spec_key(a, n_inputs, in_dt, out_dt, 0, dev));
     if (it == g_cache.end()) return false;
-    fn = scalar ? it->second.fn_scalar : it->second.fn;
+    lut = it->second.fn_lut != nullptr && a.n >= g_lut_min_n.load(std::memory_order_relaxed);
+    fn = lut ? it->second.fn_lut : scalar ? it->second.fn_scalar : it->second.fn;
   }
   const int64_t work = scalar ? a.n : ngroups;
   int64_t blocks = (work + 255) / 256;
   if (blocks < 1) blocks = 1;
+  unsigned threads = 256;
+  if (lut) {  // one workgroup per CU (the table takes 128 KiB of its LDS)
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    blocks = cus;
+    threads = 1024;
+  }
   void* params[NP_MAX_INPUTS + 2];
   const void* ins[NP_MAX_INPUTS];
   void* out = a.out;
@@ -620,7 +713,7 @@ bool rtc_launch(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, hipStre
   }
   params[n_inputs] = &out;
   params[n_inputs + 1] = &n;
-  *err = hipModuleLaunchKernel(fn, (unsigned)blocks, 1, 1, 256, 1, 1, 0, s, params, nullptr);
+  *err = hipModuleLaunchKernel(fn, (unsigned)blocks, 1, 1, threads, 1, 1, 0, s, params, nullptr);
   return true;
 }
 
@@ -682,4 +775,9 @@ extern "C" int np_chain_compile(const np_op* ops, int n_ops, int n_inputs, np_dt
   if (compile_ms) *compile_ms = std::chrono::duration<double, std::milli>(t1 - t0).count();
   if (code_bytes) *code_bytes = code.size();
   return rc;
+}
+
+extern "C" int64_t np_set_chain_table_min(int64_t n) {
+  if (n < 0) return np::g_lut_min_n.load();
+  return np::g_lut_min_n.exchange(n);
 }

@@ -258,6 +258,34 @@ def test_specialised_rare_forms(npa, orc, case):
         npa.np_shutdown()
 
 
+@pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16")])
+def test_table_path_equals_per_element_path(npa, in_dt, out_dt):
+    """A specialised chain over one 16-bit input with a 16-bit output runs from
+    its table once n reaches the threshold: every input bit pattern (NaNs
+    included) must give the same output bits as the per-element kernel."""
+    DT = {"f16": npa.NP_F16, "bf16": npa.NP_BF16}
+    ops = synth.c5_chain()
+    n = (1 << 22) + 13  # the table path, with a ragged tail
+    pats = np.tile(np.arange(1 << 16, dtype=np.uint16), n // (1 << 16) + 1)[:n]
+    x = torch.from_numpy(pats.view(np.int16)).cuda()
+    x = x.view(torch.float16 if in_dt == "f16" else torch.bfloat16)
+    npa.fuse_chain_prepare(ops, 1, DT[in_dt], DT[out_dt], 0)
+    old = npa.np_set_chain_table_min(-1)
+    try:
+        outs = []
+        for thr in (1 << 22, 1 << 62):  # table, then per element
+            npa.np_set_chain_table_min(thr)
+            out = empty((n,), out_dt)
+            npa.fuse_chain(ops, [x], out)
+            torch.cuda.synchronize()
+            outs.append(to_host(out).view(np.uint16))
+    finally:
+        npa.np_set_chain_table_min(old)
+        torch.cuda.synchronize()
+        npa.np_shutdown()
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_c5_large_sampled_specialised(npa, orc):
     """The bench's launch: the prepared (folded) kernel on 2^28 elements,
     sampled outputs against the oracle."""
