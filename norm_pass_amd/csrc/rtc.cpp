@@ -573,36 +573,48 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
       << "  unsigned short yb; __builtin_memcpy(&yb, &y, 2);\n"
       << "  np_lut[i] = yb;\n"
       << "}\n";
-    // the gather kernel: one workgroup per CU stages the 128 KiB table in LDS,
-    // then streams 16-byte vectors through it, four in flight per thread
-    s << "extern \"C\" __global__ __launch_bounds__(1024) void " << base
+    // the gather kernel: one workgroup per CU; each thread issues the loads of
+    // its first eight 16-byte vectors, the workgroup then stages the 128 KiB
+    // table in LDS while they are in flight, and streams the rest eight
+    // vectors at a time
+    s << "extern \"C\" __global__ __launch_bounds__(512) void " << base
       << "_lut(const tin* in0, tout* out, long long n_rt) {\n"
       << "  __shared__ __attribute__((aligned(16))) unsigned short lut[65536];\n"
-      << "  for (int i = threadIdx.x; i < 8192; i += 1024)\n"
-      << "    reinterpret_cast<u32x4*>(lut)[i] = reinterpret_cast<const u32x4*>(np_lut)[i];\n"
-      << "  __syncthreads();\n"
       << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
       << "  const long long nv = n / 8;\n"
-      << "  const long long stride = (long long)gridDim.x * 1024;\n"
+      << "  const long long stride = (long long)gridDim.x * 512;\n"
       << "  const u32x4* src = reinterpret_cast<const u32x4*>(in0);\n"
       << "  u32x4* dst = reinterpret_cast<u32x4*>(out);\n"
-      << "  auto map = [&](u32x4 r) {\n"
+      << "  long long v = (long long)blockIdx.x * 512 + threadIdx.x;\n"
+      << "  u32x4 r[8];\n"
+      << "  const bool first = v + 7 * stride < nv;\n"
+      << "  if (first) {\n"
+      << "#pragma unroll\n"
+      << "    for (int u = 0; u < 8; ++u) r[u] = src[v + u * stride];\n"
+      << "  }\n"
+      << "  for (int i = threadIdx.x; i < 8192; i += 512)\n"
+      << "    reinterpret_cast<u32x4*>(lut)[i] = reinterpret_cast<const u32x4*>(np_lut)[i];\n"
+      << "  __syncthreads();\n"
+      << "  auto map = [&](u32x4 x) {\n"
       << "    u32x4 o;\n"
       << "#pragma unroll\n"
       << "    for (int j = 0; j < 4; ++j)\n"
-      << "      o[j] = (unsigned)lut[r[j] & 0xffffu] | ((unsigned)lut[r[j] >> 16] << 16);\n"
+      << "      o[j] = (unsigned)lut[x[j] & 0xffffu] | ((unsigned)lut[x[j] >> 16] << 16);\n"
       << "    return o;\n"
       << "  };\n"
-      << "  long long v = (long long)blockIdx.x * 1024 + threadIdx.x;\n"
-      << "  for (; v + 3 * stride < nv; v += 4 * stride) {\n"
-      << "    u32x4 r[4];\n"
+      << "  if (first) {\n"
       << "#pragma unroll\n"
-      << "    for (int u = 0; u < 4; ++u) r[u] = src[v + u * stride];\n"
+      << "    for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(map(r[u]), dst + v + u * stride);\n"
+      << "    v += 8 * stride;\n"
+      << "  }\n"
+      << "  for (; v + 7 * stride < nv; v += 8 * stride) {\n"
       << "#pragma unroll\n"
-      << "    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(map(r[u]), dst + v + u * stride);\n"
+      << "    for (int u = 0; u < 8; ++u) r[u] = src[v + u * stride];\n"
+      << "#pragma unroll\n"
+      << "    for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(map(r[u]), dst + v + u * stride);\n"
       << "  }\n"
       << "  for (; v < nv; v += stride) __builtin_nontemporal_store(map(src[v]), dst + v);\n"
-      << "  const long long t = nv * 8 + (long long)blockIdx.x * 1024 + threadIdx.x;\n"
+      << "  const long long t = nv * 8 + (long long)blockIdx.x * 512 + threadIdx.x;\n"
       << "  if (t < n) {\n"
       << "    unsigned short b; __builtin_memcpy(&b, in0 + t, 2);\n"
       << "    const unsigned short y = lut[b];\n"
@@ -701,7 +713,7 @@ bool rtc_launch(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, hipStre
         cus <= 0)
       cus = 256;
     blocks = cus;
-    threads = 1024;
+    threads = 512;
   }
   void* params[NP_MAX_INPUTS + 2];
   const void* ins[NP_MAX_INPUTS];
