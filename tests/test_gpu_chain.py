@@ -286,6 +286,30 @@ def test_table_path_equals_per_element_path(npa, in_dt, out_dt):
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("n", [1 << 22, (1 << 22) + 1, (1 << 22) + 7 * 512 * 256 * 8 + 3])
+def test_table_path_edges_and_in_place(npa, n):
+    """The table path at the threshold itself, with a one-element tail, with a
+    size that leaves every thread a partial last round, and in place (out is
+    the input): the same bits as the per-element kernel out of place."""
+    ops = synth.c5_chain()
+    x = synth.c5_inputs(n, seed=n % 1000)
+    npa.fuse_chain_prepare(ops, 1, npa.NP_F16, npa.NP_F16, 0)
+    old = npa.np_set_chain_table_min(-1)
+    try:
+        npa.np_set_chain_table_min(1 << 62)
+        ref = empty((n,), "f16")
+        npa.fuse_chain(ops, [to_dev(x, "f16")], ref)
+        npa.np_set_chain_table_min(1 << 22)
+        inplace = to_dev(x, "f16")
+        npa.fuse_chain(ops, [inplace], inplace)
+        torch.cuda.synchronize()
+    finally:
+        npa.np_set_chain_table_min(old)
+        torch.cuda.synchronize()
+        npa.np_shutdown()
+    assert np.array_equal(to_host(inplace), to_host(ref))
+
+
 def test_c5_large_sampled_specialised(npa, orc):
     """The bench's launch: the prepared (folded) kernel on 2^28 elements,
     sampled outputs against the oracle."""
