@@ -258,7 +258,8 @@ def test_specialised_rare_forms(npa, orc, case):
         npa.np_shutdown()
 
 
-@pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16")])
+@pytest.mark.parametrize("in_dt,out_dt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16"),
+                                          ("bf16", "f16")])
 def test_table_path_equals_per_element_path(npa, in_dt, out_dt):
     """A specialised chain over one 16-bit input with a 16-bit output runs from
     its table once n reaches the threshold: every input bit pattern (NaNs
