@@ -504,17 +504,19 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_reg4(const T* __restrict__ 
   }
   const int ksteps = (K + Q_BK - 1) / Q_BK;  // K % Q_BK == 0 unless B_REGS
   u32x4 xa[8], xb[8], wa = {0u, 0u, 0u, 0u};
+  uint32_t mask = 0xffffffffu;  // of the step in the registers (B_REGS: zero past K)
   auto gload = [&](int step) {
-    // steps past the end reload the last one; a chunk past K (a partial last
-    // step) is read from a clamped address and masked to zero
+    // steps past the end reload the last one; with B_REGS a chunk past K (a
+    // partial last step) is read from a clamped address and zeroed when it is
+    // staged -- not here, which would wait for the loads right after issuing them
     const int gk = min(step, ksteps - 1) * Q_BK + 8 * ac;
-    const bool kval = gk < K;  // K % 8 == 0: a chunk is wholly inside or outside
+    const bool kval = !B_REGS || gk < K;  // K % 8 == 0: a chunk is wholly inside or outside
     const int lk = kval ? gk : 0;
-    const uint32_t mask = kval ? 0xffffffffu : 0u;
+    mask = kval ? 0xffffffffu : 0u;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      xa[q] = load_raw(xrow[q] + lk) & mask;
-      if (B_REGS) xb[q] = load_raw(wrow[q] + lk) & mask;
+      xa[q] = load_raw(xrow[q] + lk);
+      if (B_REGS) xb[q] = load_raw(wrow[q] + lk);
     }
     if (HAS_W) wa = load_raw(w + lk);
   };
@@ -534,6 +536,10 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_reg4(const T* __restrict__ 
     __builtin_memcpy(wv, &wa, 16);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
+      if (B_REGS) {
+        xa[q] &= mask;
+        xb[q] &= mask;
+      }
       v8 xv;
       __builtin_memcpy(&xv, &xa[q], 16);
       if (NORM) ss[q] = Mfma<T>::sumsq(xv, ss[q]);
