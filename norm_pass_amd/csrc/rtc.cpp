@@ -576,7 +576,10 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
     // the gather kernel: one workgroup per CU; each thread issues the loads of
     // its first eight 16-byte vectors, the workgroup then stages the 128 KiB
     // table in LDS while they are in flight, and streams the rest eight
-    // vectors at a time
+    // vectors at a time. Input loads are non-temporal as well as the stores: a
+    // stream this long cannot stay in the Infinity Cache between calls, and
+    // bypassing it takes the gather from the rate of a cached loop to that of a
+    // plain copy of the same bytes
     s << "extern \"C\" __global__ __launch_bounds__(512) void " << base
       << "_lut(const tin* in0, tout* out, long long n_rt) {\n"
       << "  __shared__ __attribute__((aligned(16))) unsigned short lut[65536];\n"
@@ -590,7 +593,7 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
       << "  const bool first = v + 7 * stride < nv;\n"
       << "  if (first) {\n"
       << "#pragma unroll\n"
-      << "    for (int u = 0; u < 8; ++u) r[u] = src[v + u * stride];\n"
+      << "    for (int u = 0; u < 8; ++u) r[u] = __builtin_nontemporal_load(src + v + u * stride);\n"
       << "  }\n"
       << "  for (int i = threadIdx.x; i < 8192; i += 512)\n"
       << "    reinterpret_cast<u32x4*>(lut)[i] = reinterpret_cast<const u32x4*>(np_lut)[i];\n"
@@ -609,11 +612,12 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
       << "  }\n"
       << "  for (; v + 7 * stride < nv; v += 8 * stride) {\n"
       << "#pragma unroll\n"
-      << "    for (int u = 0; u < 8; ++u) r[u] = src[v + u * stride];\n"
+      << "    for (int u = 0; u < 8; ++u) r[u] = __builtin_nontemporal_load(src + v + u * stride);\n"
       << "#pragma unroll\n"
       << "    for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(map(r[u]), dst + v + u * stride);\n"
       << "  }\n"
-      << "  for (; v < nv; v += stride) __builtin_nontemporal_store(map(src[v]), dst + v);\n"
+      << "  for (; v < nv; v += stride)\n"
+      << "    __builtin_nontemporal_store(map(__builtin_nontemporal_load(src + v)), dst + v);\n"
       << "  const long long t = nv * 8 + (long long)blockIdx.x * 512 + threadIdx.x;\n"
       << "  if (t < n) {\n"
       << "    unsigned short b; __builtin_memcpy(&b, in0 + t, 2);\n"
