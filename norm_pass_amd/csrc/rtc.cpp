@@ -573,29 +573,23 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
       << "  unsigned short yb; __builtin_memcpy(&yb, &y, 2);\n"
       << "  np_lut[i] = yb;\n"
       << "}\n";
-    // the gather kernel: one workgroup per CU; each thread issues the loads of
-    // its first eight 16-byte vectors, the workgroup then stages the 128 KiB
-    // table in LDS while they are in flight, and streams the rest eight
-    // vectors at a time. Input loads are non-temporal as well as the stores: a
-    // stream this long cannot stay in the Infinity Cache between calls, and
-    // bypassing it takes the gather from the rate of a cached loop to that of a
-    // plain copy of the same bytes
+    // the gather kernel: one 512-thread workgroup per CU stages the 128 KiB
+    // table in LDS, then takes contiguous blocks of 2048 16-byte vectors (32
+    // KiB), block b + i * grid on its i-th pass, four vectors per thread at
+    // NT-vector spacing so every load and store instruction of a wave covers
+    // 1 KiB in one piece. Loads and stores are non-temporal: a stream this long
+    // cannot stay in the Infinity Cache between calls. (Each thread's vectors
+    // one grid stride apart, the usual persistent loop, ran 6 % slower here.)
     s << "extern \"C\" __global__ __launch_bounds__(512) void " << base
       << "_lut(const tin* in0, tout* out, long long n_rt) {\n"
       << "  __shared__ __attribute__((aligned(16))) unsigned short lut[65536];\n"
       << "  const long long n = NPS_N ? NPS_N : n_rt;\n"
       << "  const long long nv = n / 8;\n"
-      << "  const long long stride = (long long)gridDim.x * 512;\n"
+      << "  const long long nblk = nv / 2048;\n"
       << "  const u32x4* src = reinterpret_cast<const u32x4*>(in0);\n"
       << "  u32x4* dst = reinterpret_cast<u32x4*>(out);\n"
-      << "  long long v = (long long)blockIdx.x * 512 + threadIdx.x;\n"
-      << "  u32x4 r[8];\n"
-      << "  const bool first = v + 7 * stride < nv;\n"
-      << "  if (first) {\n"
-      << "#pragma unroll\n"
-      << "    for (int u = 0; u < 8; ++u) r[u] = __builtin_nontemporal_load(src + v + u * stride);\n"
-      << "  }\n"
-      << "  for (int i = threadIdx.x; i < 8192; i += 512)\n"
+      << "  const int t = threadIdx.x;\n"
+      << "  for (int i = t; i < 8192; i += 512)\n"
       << "    reinterpret_cast<u32x4*>(lut)[i] = reinterpret_cast<const u32x4*>(np_lut)[i];\n"
       << "  __syncthreads();\n"
       << "  auto map = [&](u32x4 x) {\n"
@@ -605,24 +599,23 @@ std::string rtc_source(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, 
       << "      o[j] = (unsigned)lut[x[j] & 0xffffu] | ((unsigned)lut[x[j] >> 16] << 16);\n"
       << "    return o;\n"
       << "  };\n"
-      << "  if (first) {\n"
+      << "  u32x4 r[4];\n"
+      << "  for (long long k = blockIdx.x; k < nblk; k += gridDim.x) {\n"
+      << "    const long long v = k * 2048 + t;\n"
       << "#pragma unroll\n"
-      << "    for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(map(r[u]), dst + v + u * stride);\n"
-      << "    v += 8 * stride;\n"
+      << "    for (int u = 0; u < 4; ++u) r[u] = __builtin_nontemporal_load(src + v + u * 512);\n"
+      << "#pragma unroll\n"
+      << "    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(map(r[u]), dst + v + u * 512);\n"
       << "  }\n"
-      << "  for (; v + 7 * stride < nv; v += 8 * stride) {\n"
-      << "#pragma unroll\n"
-      << "    for (int u = 0; u < 8; ++u) r[u] = __builtin_nontemporal_load(src + v + u * stride);\n"
-      << "#pragma unroll\n"
-      << "    for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(map(r[u]), dst + v + u * stride);\n"
-      << "  }\n"
-      << "  for (; v < nv; v += stride)\n"
+      << "  // the vectors after the last whole block, then the elements after the last vector\n"
+      << "  for (long long v = nblk * 2048 + (long long)blockIdx.x * 512 + t; v < nv;\n"
+      << "       v += (long long)gridDim.x * 512)\n"
       << "    __builtin_nontemporal_store(map(__builtin_nontemporal_load(src + v)), dst + v);\n"
-      << "  const long long t = nv * 8 + (long long)blockIdx.x * 512 + threadIdx.x;\n"
-      << "  if (t < n) {\n"
-      << "    unsigned short b; __builtin_memcpy(&b, in0 + t, 2);\n"
+      << "  const long long e = nv * 8 + (long long)blockIdx.x * 512 + t;\n"
+      << "  if (e < n) {\n"
+      << "    unsigned short b; __builtin_memcpy(&b, in0 + e, 2);\n"
       << "    const unsigned short y = lut[b];\n"
-      << "    __builtin_memcpy(out + t, &y, 2);\n"
+      << "    __builtin_memcpy(out + e, &y, 2);\n"
       << "  }\n"
       << "}\n";
   }

@@ -287,10 +287,14 @@ def test_table_path_equals_per_element_path(npa, in_dt, out_dt):
     assert np.array_equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("n", [1 << 22, (1 << 22) + 1, (1 << 22) + 7 * 512 * 256 * 8 + 3])
+@pytest.mark.parametrize("n", [1 << 22, (1 << 22) + 1, (1 << 22) + 7 * 512 * 256 * 8 + 3,
+                               (1 << 22) + 8 * (2048 * 37 + 1000) + 5])
 def test_table_path_edges_and_in_place(npa, n):
-    """The table path at the threshold itself, with a one-element tail, with a
-    size that leaves every thread a partial last round, and in place (out is
+    """The table path (blocks of 2048 16-byte vectors dealt round-robin to one
+    workgroup per CU) at the threshold itself (one whole block per workgroup
+    on 256 CUs), with a one-element tail, with block counts that leave some
+    workgroups one block more than others, with 1000 vectors after the last
+    whole block and five elements after the last vector, and in place (out is
     the input): the same bits as the per-element kernel out of place."""
     ops = synth.c5_chain()
     x = synth.c5_inputs(n, seed=n % 1000)
