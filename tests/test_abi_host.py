@@ -264,3 +264,42 @@ def test_rmsnorm_linear_rejects_overlap_and_alignment(npa):
                                          C.c_void_p(1 << 44), 4, 32, 64, 1e-6, 1.0, 2,
                                          NULL) == -1
     assert "aligned" in _err(npa)
+
+
+def test_zero_rows_tokens_and_elements_are_no_ops(npa):
+    """Every entry point with an empty leading size returns NP_OK before it
+    looks for a device: the buffers (addresses that are never dereferenced
+    here) are not touched and nothing is launched."""
+    L = npa.lib()
+    x, r, w, h, out, ws = (C.c_void_p(0x1000 * (i + 1)) for i in range(6))
+    for dt in (0, 1, 2):
+        assert L.fuse_add_rmsnorm(x, r, w, h, out, 0, 4096, 1e-6, dt, NULL) == 0
+        assert L.fuse_add_rmsnorm(x, NULL, NULL, NULL, out, 0, 8, 1e-6, dt, NULL) == 0
+        assert L.unfused_add_rmsnorm(x, r, w, h, out, 0, 4096, 1e-6, dt, ws, 1 << 20, NULL) == 0
+        assert L.fuse_add_layernorm(x, r, w, w, h, out, 0, 4096, 1e-5, dt, NULL) == 0
+        assert L.unfused_add_layernorm(x, r, w, w, h, out, 0, 4096, 1e-5, dt, ws, 1 << 20,
+                                       NULL) == 0
+        p = [C.c_void_p(0x1000 * (i + 1)) for i in range(4)]
+        assert L.fuse_qkv_rope(*p, 0, 24, 128, NULL, 1e4, 0.125, dt, NULL) == 0
+        assert L.unfused_qkv_rope(*p, 0, 24, 128, NULL, 1e4, 0.125, dt, NULL) == 0
+    arr, k = npa._ops(synth.C1_CHAIN)
+    ptrs = (C.c_void_p * 2)(0x1000, 0x3000)
+    assert L.fuse_chain(arr, k, ptrs, 2, 0, out, 0, 0, NULL) == 0
+    assert L.unfused_chain(arr, k, ptrs, 2, 0, out, 0, 0, NULL) == 0
+    for bf in (1, 2):
+        assert L.fuse_rmsnorm_linear(C.c_void_p(1 << 40), None, C.c_void_p(1 << 42), None,
+                                     C.c_void_p(1 << 44), 0, 32, 64, 1e-6, 1.0, bf, NULL) == 0
+
+
+def test_zero_size_rejects_still_apply(npa):
+    """An empty call is still checked: a NULL required buffer or a bad
+    dtype, width or head_dim is NP_EINVAL even when there is nothing to do."""
+    L = npa.lib()
+    out = C.c_void_p(0x2000)
+    assert L.fuse_add_rmsnorm(NULL, NULL, NULL, NULL, out, 0, 8, 1e-6, 2, NULL) == -1
+    assert L.fuse_add_rmsnorm(C.c_void_p(0x1000), NULL, NULL, NULL, out, 0, 0, 1e-6, 2,
+                              NULL) == -1
+    p = [C.c_void_p(0x1000 * (i + 1)) for i in range(4)]
+    assert L.fuse_qkv_rope(*p, 0, 24, 7, NULL, 1e4, 0.125, 2, NULL) == -1
+    assert L.fuse_add_layernorm(C.c_void_p(0x1000), NULL, NULL, NULL, NULL, out, 0, 8, 1e-5, 9,
+                                NULL) == -1
