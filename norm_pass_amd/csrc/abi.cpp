@@ -353,7 +353,8 @@ int run_transpose(const void* in, void* out, int64_t B, int64_t R, int64_t S, in
     for (int64_t b0 = 0; b0 < p.B && e == hipSuccess; b0 += b_step) {
       const int64_t nb = std::min(b_step, p.B - b0);
       a.n_items = (uint32_t)(nb * mat_items);
-      e = np::launch_tr_items(src + b0 * mat_bytes, dst + b0 * mat_bytes, a, p.item, stream);
+      e = np::launch_tr_items(src + b0 * mat_bytes, dst + b0 * mat_bytes, a, p.item, !naive,
+                              stream);
     }
   }
   if (e != hipSuccess) return hip_fail(e, who);

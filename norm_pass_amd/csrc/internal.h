@@ -135,7 +135,7 @@ hipError_t launch_tr_tile(const void* in, void* out, const TileArgs& a, uint32_t
 hipError_t launch_tr_small(const void* in, void* out, const SmallArgs& a, uint32_t grid,
                            int item_bytes, bool vec, hipStream_t s);
 hipError_t launch_tr_items(const void* in, void* out, const ItemArgs& a, int item_bytes,
-                           hipStream_t s);
+                           bool nt, hipStream_t s);
 
 hipError_t launch_cast_to_f32(const void* in, float* out, int64_t n, int dt, hipStream_t s);
 hipError_t launch_empty(hipStream_t s);

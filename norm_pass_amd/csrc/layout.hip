@@ -258,8 +258,11 @@ __global__ __launch_bounds__(256) void tr_small(const uint8_t* __restrict__ in,
   }
 }
 
-// One thread per output item.
-template <int W>
+// One thread per output item. NT: non-temporal stores (the fused path; the
+// naive baseline keeps plain stores, like a generic strided copy). Measured on
+// [16384, 72] units of 256 bytes: 111 us with plain stores, 96 us with
+// non-temporal ones.
+template <int W, bool NT>
 __global__ __launch_bounds__(256) void tr_items(const uint8_t* __restrict__ in,
                                                 uint8_t* __restrict__ out, ItemArgs a) {
   typedef typename Item<W>::T It;
@@ -272,8 +275,12 @@ __global__ __launch_bounds__(256) void tr_items(const uint8_t* __restrict__ in,
   const uint32_t b = fdiv(t, a.s);
   const uint32_t s = t - b * a.s.d;
   const uint32_t src = ((b * a.r.d + r) * a.s.d + s) * a.e.d + e;
-  *reinterpret_cast<It*>(out + (uint64_t)j * W) =
-      *reinterpret_cast<const It*>(in + (uint64_t)src * W);
+  const It v = *reinterpret_cast<const It*>(in + (uint64_t)src * W);
+  It* dst = reinterpret_cast<It*>(out + (uint64_t)j * W);
+  if (NT)
+    __builtin_nontemporal_store(v, dst);
+  else
+    *dst = v;
 }
 
 template <int U>
@@ -295,6 +302,15 @@ hipError_t launch_small_w(const uint8_t* in, uint8_t* out, const SmallArgs& a, u
   else
     hipLaunchKernelGGL((tr_small<W, false>), dim3(grid), dim3(256), 0, s, in, out, a);
   return hipGetLastError();
+}
+
+template <int W>
+void launch_items_w(const uint8_t* in, uint8_t* out, const ItemArgs& a, dim3 grid, bool nt,
+                    hipStream_t s) {
+  if (nt)
+    hipLaunchKernelGGL((tr_items<W, true>), grid, dim3(256), 0, s, in, out, a);
+  else
+    hipLaunchKernelGGL((tr_items<W, false>), grid, dim3(256), 0, s, in, out, a);
 }
 
 }  // namespace
@@ -339,16 +355,16 @@ hipError_t launch_tr_small(const void* in, void* out, const SmallArgs& a, uint32
 }
 
 hipError_t launch_tr_items(const void* in, void* out, const ItemArgs& a, int item_bytes,
-                           hipStream_t s) {
+                           bool nt, hipStream_t s) {
   const uint8_t* i = static_cast<const uint8_t*>(in);
   uint8_t* o = static_cast<uint8_t*>(out);
   const dim3 grid((a.n_items + 255u) / 256u);
   switch (item_bytes) {
-    case 1: hipLaunchKernelGGL(tr_items<1>, grid, dim3(256), 0, s, i, o, a); break;
-    case 2: hipLaunchKernelGGL(tr_items<2>, grid, dim3(256), 0, s, i, o, a); break;
-    case 4: hipLaunchKernelGGL(tr_items<4>, grid, dim3(256), 0, s, i, o, a); break;
-    case 8: hipLaunchKernelGGL(tr_items<8>, grid, dim3(256), 0, s, i, o, a); break;
-    case 16: hipLaunchKernelGGL(tr_items<16>, grid, dim3(256), 0, s, i, o, a); break;
+    case 1: launch_items_w<1>(i, o, a, grid, nt, s); break;
+    case 2: launch_items_w<2>(i, o, a, grid, nt, s); break;
+    case 4: launch_items_w<4>(i, o, a, grid, nt, s); break;
+    case 8: launch_items_w<8>(i, o, a, grid, nt, s); break;
+    case 16: launch_items_w<16>(i, o, a, grid, nt, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
