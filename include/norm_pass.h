@@ -108,9 +108,20 @@ void np_shutdown(void);
  * fuse_chain_prepare would build for this chain; reports the compile time in
  * milliseconds and the code-object size. Needs no GPU (the DeepJIT write-up,
  * sections 3.3 and 6.2, quotes tens to hundreds of ms per runtime compile).
- * Returns NP_OK, NP_EINVAL or NP_ECOMPILE. compile_ms / code_bytes may be NULL. */
+ * Always compiles; when NP_CACHE_DIR is set the code object is also stored in
+ * the disk cache (see fuse_chain_prepare), so a machine without a GPU can fill
+ * the cache ahead of time. Returns NP_OK, NP_EINVAL or NP_ECOMPILE.
+ * compile_ms / code_bytes may be NULL. */
 int np_chain_compile(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt, np_dtype out_dt,
                      int64_t n, double* compile_ms, size_t* code_bytes);
+
+/* Counters of the disk cache of specialised code objects since the process
+ * started (DeepJIT write-up, section 6.2): loads = fuse_chain_prepare found a
+ * valid file and skipped compiling; stores = files written (by prepare or
+ * np_chain_compile); rejects = files present but unusable (another key, a
+ * truncated file, or a code object the runtime would not load), each followed
+ * by a compile. Any pointer may be NULL. */
+void np_chain_cache_stats(int64_t* loads, int64_t* stores, int64_t* rejects);
 
 /* Write the generated kernel source for a chain (what fuse_chain_prepare
  * compiles) into buf (NUL-terminated, truncated to len); returns the full size
@@ -144,6 +155,12 @@ int fuse_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_inp
  * with hipRTC for gfx950 on the current device; cached per process. Returns
  * NP_ECOMPILE (the generic kernel remains in use) if compilation fails, and
  * NP_OK without compiling when NP_DISABLE_RTC=1 is set in the environment.
+ * Disk cache (section 6.2, the cache level that survives a restart): when the
+ * environment variable NP_CACHE_DIR names a directory (created if missing), the
+ * code object is looked up there first, by the exact text of hipRTC's version,
+ * the options and the generated source, and written there after a compile
+ * (a temporary file renamed into place, safe across processes). Unset or
+ * empty: no disk cache. The library never writes files otherwise.
  */
 int fuse_chain_prepare(const np_op* ops, int n_ops, int n_inputs, np_dtype in_dt,
                        np_dtype out_dt, int64_t n_or_0);

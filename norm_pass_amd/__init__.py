@@ -72,11 +72,12 @@ def _load():
         "naive_channel_shuffle": [P, P, I64, I64, I64, I64, I64, I, I, P],
         "np_transpose_plan": [P, P, I64, I64, I64, I64, I, I],
         "np_set_chain_table_min": [I64],
+        "np_chain_cache_stats": [C.POINTER(I64)] * 3,
     }
     for name, args in sig.items():
         fn = getattr(L, name)
         fn.argtypes = args
-        fn.restype = (None if name == "np_shutdown" else
+        fn.restype = (None if name in ("np_shutdown", "np_chain_cache_stats") else
                       C.c_int64 if name in ("np_chain_source", "np_set_chain_table_min")
                       else C.c_int)
     L.np_last_error.restype = C.c_char_p
@@ -331,6 +332,13 @@ def fuse_chain(ops, inputs, out, stream=None):
     """out[i] = chain(inputs[0][i], ...); ops = [(kind, arg, const), ...]."""
     _check(_lib.fuse_chain(*_a_fuse_chain(ops, inputs, out, stream)), "fuse_chain")
     return out
+
+
+def np_chain_cache_stats() -> dict:
+    """Disk cache counters of specialised code objects: {"loads", "stores", "rejects"}."""
+    v = [C.c_int64() for _ in range(3)]
+    _lib.np_chain_cache_stats(*(C.byref(x) for x in v))
+    return {"loads": v[0].value, "stores": v[1].value, "rejects": v[2].value}
 
 
 def np_set_chain_table_min(n: int) -> int:

@@ -8,16 +8,23 @@
 //  - section 3.3 / 6.2: a process-wide cache keyed by a hash of source,
 //    architecture and options; compile only at warm-up (fuse_chain_prepare),
 //    never on the launch path;
+//  - section 6.2: the compiled code object also persisted on disk (when
+//    NP_CACHE_DIR names a directory), so a restarted process loads it instead
+//    of compiling;
 //  - section 6.3: no fast-math; section 6.4: modules live until np_shutdown.
 #include "rtc.h"
 
+#include <errno.h>
 #include <hip/hiprtc.h>
+#include <sys/stat.h>
+#include <unistd.h>
 
 #include <atomic>
 #include <chrono>
 #include <cfloat>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
 #include <map>
@@ -460,6 +467,106 @@ int compile(const std::string& src, std::vector<char>* code, std::string* log) {
   return NP_OK;
 }
 
+// ---- code objects on disk (DeepJIT write-up, section 6.2: the second cache
+// level, compiled output kept on disk so a restarted process skips compiling)
+//
+// A file <dir>/<fnv-1a 64 of the key text>.npco holds the 8-byte magic
+// "NPCHAIN1", the key text's length (u64) and text, the code object's length
+// (u64) and bytes. The key text is the hipRTC version, the library's HIP
+// version, the options and the whole generated source; a file is used only
+// when its key text equals the expected one byte for byte, so a hash
+// collision, a stale file or a truncated one is a miss. Files are written
+// under a unique temporary name and renamed into place, so concurrent
+// processes never read a partial file. The cache is best effort: any I/O
+// failure falls back to compiling.
+constexpr char kMagic[8] = {'N', 'P', 'C', 'H', 'A', 'I', 'N', '1'};
+std::atomic<int64_t> g_disk_loads{0}, g_disk_stores{0}, g_disk_rejects{0};
+std::atomic<uint64_t> g_tmp_counter{0};
+
+// NP_CACHE_DIR, or "" (no disk cache) when it is unset or empty
+std::string cache_dir() {
+  const char* d = std::getenv("NP_CACHE_DIR");
+  return d ? std::string(d) : std::string();
+}
+
+std::string key_text(const std::string& src) {
+  int major = 0, minor = 0;
+  (void)hiprtcVersion(&major, &minor);
+  std::ostringstream k;
+  k << "hiprtc " << major << "." << minor << " | hip " << HIP_VERSION << " |";
+  for (int i = 0; i < kNumOptions; ++i) k << ' ' << kOptions[i];
+  k << '\n' << src;
+  return k.str();
+}
+
+std::string cache_path(const std::string& dir, const std::string& key) {
+  uint64_t h = 1469598103934665603ull;  // FNV-1a, 64-bit
+  for (unsigned char c : key) {
+    h ^= c;
+    h *= 1099511628211ull;
+  }
+  char name[32];
+  std::snprintf(name, sizeof(name), "/%016llx.npco", (unsigned long long)h);
+  return dir + name;
+}
+
+bool make_dirs(const std::string& dir) {
+  for (size_t i = 1; i <= dir.size(); ++i) {
+    if (i == dir.size() || dir[i] == '/') {
+      const std::string part = dir.substr(0, i);
+      if (mkdir(part.c_str(), 0755) != 0 && errno != EEXIST) return false;
+    }
+  }
+  struct stat st;
+  return stat(dir.c_str(), &st) == 0 && S_ISDIR(st.st_mode);
+}
+
+// the cached code object for this key, if a valid file holds it
+bool disk_load(const std::string& dir, const std::string& key, std::vector<char>* code) {
+  FILE* f = std::fopen(cache_path(dir, key).c_str(), "rb");
+  if (!f) return false;
+  bool ok = false;
+  char magic[8];
+  uint64_t klen = 0, clen = 0;
+  if (std::fread(magic, 1, 8, f) == 8 && std::memcmp(magic, kMagic, 8) == 0 &&
+      std::fread(&klen, 8, 1, f) == 1 && klen == key.size()) {
+    std::string k(klen, '\0');
+    if (std::fread(&k[0], 1, klen, f) == klen && k == key && std::fread(&clen, 8, 1, f) == 1 &&
+        clen > 0 && clen < (uint64_t(1) << 30)) {
+      code->resize(clen);
+      char extra;
+      ok = std::fread(code->data(), 1, clen, f) == clen && std::fread(&extra, 1, 1, f) == 0;
+    }
+  }
+  std::fclose(f);
+  if (!ok) {
+    code->clear();
+    g_disk_rejects.fetch_add(1);
+  }
+  return ok;
+}
+
+void disk_store(const std::string& dir, const std::string& key, const std::vector<char>& code) {
+  if (!make_dirs(dir)) return;
+  const std::string path = cache_path(dir, key);
+  char suffix[64];
+  std::snprintf(suffix, sizeof(suffix), ".tmp.%ld.%llu", (long)getpid(),
+                (unsigned long long)g_tmp_counter.fetch_add(1));
+  const std::string tmp = path + suffix;
+  FILE* f = std::fopen(tmp.c_str(), "wb");
+  if (!f) return;
+  const uint64_t klen = key.size(), clen = code.size();
+  bool ok = std::fwrite(kMagic, 1, 8, f) == 8 && std::fwrite(&klen, 8, 1, f) == 1 &&
+            std::fwrite(key.data(), 1, klen, f) == klen && std::fwrite(&clen, 8, 1, f) == 1 &&
+            std::fwrite(code.data(), 1, clen, f) == clen;
+  ok = (std::fclose(f) == 0) && ok;
+  if (ok && std::rename(tmp.c_str(), path.c_str()) == 0) {
+    g_disk_stores.fetch_add(1);
+  } else {
+    std::remove(tmp.c_str());
+  }
+}
+
 }  // namespace
 
 // Kernel names carry the op count and the size written in (0: size at launch),
@@ -648,18 +755,43 @@ int rtc_prepare(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, std::st
       }
     }
   }
+  // the code object: from the disk cache when one is configured and holds it,
+  // else compiled (and then stored there)
+  const std::string dir = cache_dir();
+  const std::string ktext = dir.empty() ? std::string() : key_text(src);
   std::vector<char> code;
-  int rc = compile(src, &code, log);
-  if (rc) return rc;
+  bool from_disk = !dir.empty() && disk_load(dir, ktext, &code);
+  if (!from_disk) {
+    const int rc = compile(src, &code, log);
+    if (rc) return rc;
+    if (!dir.empty()) disk_store(dir, ktext, code);
+  }
   Entry e;
   e.src_hash = h;
-  if (hipModuleLoadData(&e.mod, code.data()) != hipSuccess ||
-      hipModuleGetFunction(&e.fn, e.mod, spec_name(a, a.n, false).c_str()) != hipSuccess ||
-      hipModuleGetFunction(&e.fn_scalar, e.mod, spec_name(a, a.n, true).c_str()) != hipSuccess) {
-    *log = "module load failed";
+  auto load = [&]() {
+    if (hipModuleLoadData(&e.mod, code.data()) == hipSuccess &&
+        hipModuleGetFunction(&e.fn, e.mod, spec_name(a, a.n, false).c_str()) == hipSuccess &&
+        hipModuleGetFunction(&e.fn_scalar, e.mod, spec_name(a, a.n, true).c_str()) == hipSuccess)
+      return true;
     if (e.mod) (void)hipModuleUnload(e.mod);
+    e.mod = nullptr;
+    (void)hipGetLastError();
+    return false;
+  };
+  bool loaded = load();
+  if (!loaded && from_disk) {  // a cached object that does not load: compile it afresh
+    g_disk_rejects.fetch_add(1);
+    from_disk = false;
+    const int rc = compile(src, &code, log);
+    if (rc) return rc;
+    disk_store(dir, ktext, code);
+    loaded = load();
+  }
+  if (!loaded) {
+    *log = "module load failed";
     return NP_ELAUNCH;
   }
+  if (from_disk) g_disk_loads.fetch_add(1);
   if (tabulable(n_inputs, in_dt, out_dt)) {
     // fill the module's table once (65,536 threads), on a private stream
     // waited for here: prepare is the warm-up-time call; without a table the
@@ -778,12 +910,21 @@ extern "C" int np_chain_compile(const np_op* ops, int n_ops, int n_inputs, np_dt
   }
   std::vector<char> code;
   std::string log;
+  const std::string src = np::rtc_source(a, n_inputs, in_dt, out_dt, n);
   const auto t0 = std::chrono::steady_clock::now();
-  int rc = np::compile(np::rtc_source(a, n_inputs, in_dt, out_dt, n), &code, &log);
+  int rc = np::compile(src, &code, &log);
   const auto t1 = std::chrono::steady_clock::now();
   if (compile_ms) *compile_ms = std::chrono::duration<double, std::milli>(t1 - t0).count();
   if (code_bytes) *code_bytes = code.size();
+  const std::string dir = np::cache_dir();
+  if (rc == NP_OK && !dir.empty()) np::disk_store(dir, np::key_text(src), code);
   return rc;
+}
+
+extern "C" void np_chain_cache_stats(int64_t* loads, int64_t* stores, int64_t* rejects) {
+  if (loads) *loads = np::g_disk_loads.load();
+  if (stores) *stores = np::g_disk_stores.load();
+  if (rejects) *rejects = np::g_disk_rejects.load();
 }
 
 extern "C" int64_t np_set_chain_table_min(int64_t n) {
