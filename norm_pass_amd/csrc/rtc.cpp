@@ -28,6 +28,7 @@
 #include <cstring>
 #include <functional>
 #include <map>
+#include <unordered_map>
 #include <mutex>
 #include <sstream>
 #include <vector>
@@ -412,6 +413,8 @@ struct Entry {
   hipFunction_t fn_scalar = nullptr;  // one element per thread
   hipFunction_t fn_lut = nullptr;     // table gather (tabulable chains, table built)
   size_t src_hash = 0;
+  int dev = 0;
+  int cus = 256;                      // compute units of dev (the gather's grid)
 };
 
 // From this many elements the table gather wins: below it, staging the
@@ -422,18 +425,26 @@ std::atomic<int64_t> g_lut_min_n{int64_t(1) << 22};
 constexpr int64_t kMinVecGroups = 65536;
 
 std::mutex g_mu;
-std::map<std::string, Entry> g_cache;  // spec key -> loaded kernel
+std::unordered_map<std::string, Entry> g_cache;  // spec key -> loaded kernel
 
+// The key of a specialisation, built on every fuse_chain call: the device,
+// dtypes, input count, op count and n, then each op's kind, input index and
+// constant bits, copied as fixed-size bytes (formatting them as text took
+// microseconds per call for a 30-op chain). n sits at byte kKeyN.
+constexpr size_t kKeyN = 5 * sizeof(int32_t);
 std::string spec_key(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, int64_t n,
                      int dev) {
-  std::ostringstream k;
-  k << dev << '|' << in_dt << '|' << out_dt << '|' << n_inputs << '|' << n << '|';
+  const int32_t head[5] = {dev, in_dt, out_dt, n_inputs, a.n_ops};
+  std::string k;
+  k.reserve(sizeof(head) + sizeof(n) + (size_t)a.n_ops * 12);
+  k.append(reinterpret_cast<const char*>(head), sizeof(head));
+  k.append(reinterpret_cast<const char*>(&n), sizeof(n));
   for (int i = 0; i < a.n_ops; ++i) {
-    uint32_t cb;
-    std::memcpy(&cb, &a.c[i], 4);
-    k << a.kind[i] << ',' << a.arg[i] << ',' << cb << ';';
+    int32_t op[3] = {a.kind[i], a.arg[i], 0};
+    std::memcpy(&op[2], &a.c[i], 4);
+    k.append(reinterpret_cast<const char*>(op), sizeof(op));
   }
-  return k.str();
+  return k;
 }
 
 const char* kOptions[] = {"--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang",
@@ -749,7 +760,7 @@ int rtc_prepare(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, std::st
   {
     std::lock_guard<std::mutex> lk(g_mu);
     for (auto& kv : g_cache) {
-      if (kv.second.src_hash == h && kv.first.rfind(std::to_string(dev) + "|", 0) == 0) {
+      if (kv.second.src_hash == h && kv.second.dev == dev) {
         g_cache[key] = kv.second;
         return NP_OK;
       }
@@ -768,6 +779,13 @@ int rtc_prepare(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, std::st
   }
   Entry e;
   e.src_hash = h;
+  e.dev = dev;
+  {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      e.cus = cus;
+  }
   auto load = [&]() {
     if (hipModuleLoadData(&e.mod, code.data()) == hipSuccess &&
         hipModuleGetFunction(&e.fn, e.mod, spec_name(a, a.n, false).c_str()) == hipSuccess &&
@@ -823,24 +841,27 @@ bool rtc_launch(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, hipStre
   const bool scalar = ngroups < kMinVecGroups;
   hipFunction_t fn = nullptr;
   bool lut = false;
+  int cus = 0;
+  std::string key = spec_key(a, n_inputs, in_dt, out_dt, a.n, dev);
   {
     std::lock_guard<std::mutex> lk(g_mu);
     if (g_cache.empty()) return false;
-    auto it = g_cache.find(spec_key(a, n_inputs, in_dt, out_dt, a.n, dev));
-    if (it == g_cache.end()) it = g_cache.find(spec_key(a, n_inputs, in_dt, out_dt, 0, dev));
+    auto it = g_cache.find(key);
+    if (it == g_cache.end()) {  // the same chain prepared for any n
+      const int64_t zero = 0;
+      key.replace(kKeyN, sizeof(zero), reinterpret_cast<const char*>(&zero), sizeof(zero));
+      it = g_cache.find(key);
+    }
     if (it == g_cache.end()) return false;
     lut = it->second.fn_lut != nullptr && a.n >= g_lut_min_n.load(std::memory_order_relaxed);
     fn = lut ? it->second.fn_lut : scalar ? it->second.fn_scalar : it->second.fn;
+    cus = it->second.cus;
   }
   const int64_t work = scalar ? a.n : ngroups;
   int64_t blocks = (work + 255) / 256;
   if (blocks < 1) blocks = 1;
   unsigned threads = 256;
   if (lut) {  // one workgroup per CU (the table takes 128 KiB of its LDS)
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
     blocks = cus;
     threads = 512;
   }
