@@ -18,9 +18,6 @@
 
 namespace {
 
-#ifndef NP_DET_TILE_CELLS
-#define NP_DET_TILE_CELLS 32
-#endif
 
 thread_local std::string g_err;
 
@@ -173,10 +170,7 @@ int fill_det_args(np::DetArgs& a, const void* const* lv, int n_levels, const int
   a.n_ch = n_ch;
   a.batch = batch;
   a.out = out;
-  // NP_DET_TILE_CELLS cells per tile (32: a 10.9 KiB LDS tile at 85 channels,
-  // ~800 workgroups for the three YOLO levels; measured best among 16/32/64 on
-  // MI355X); wide rows (n_ch > 256) use 8 cells to keep the tile within 32 KiB
-  const int tp = n_ch <= 256 ? NP_DET_TILE_CELLS : 8;
+  const int tp = np::det_tile_cells(n_ch);
   a.tile_cells = tp;
   int64_t row = 0;
   int64_t tiles_total = 0;

@@ -40,6 +40,7 @@ struct DetArgs {
   int32_t tile_cells;     // cells per tile
 };
 hipError_t launch_det_decode(const DetArgs& a, int in_dt, bool vec_in, hipStream_t s);
+int det_tile_cells(int n_ch);  // cells per workgroup tile of the decode kernel
 
 // residual add + RMSNorm
 hipError_t launch_add_rmsnorm(const void* x, const void* r, const void* w, void* h, void* out,

@@ -828,7 +828,9 @@ int rtc_prepare(const ChainArgs& a, int n_inputs, int in_dt, int out_dt, std::st
     (void)hipGetLastError();  // a failed table leaves the per-element kernels in use
   }
   std::lock_guard<std::mutex> lk(g_mu);
-  g_cache[key] = e;
+  // another thread may have prepared the same chain meanwhile: keep its entry
+  // (launches may already use it) and release this module
+  if (!g_cache.emplace(key, e).second) (void)hipModuleUnload(e.mod);
   return NP_OK;
 }
 
