@@ -142,7 +142,7 @@ int64_t np_chain_source(const np_op* ops, int n_ops, int n_inputs, np_dtype in_d
  * specialisation prepared by fuse_chain_prepare for this exact op list, dtypes
  * and n when one exists, else the precompiled generic kernel; never compiles.
  * Errors: NP_EINVAL for n_ops outside 1..NP_MAX_OPS, an unknown op, an input
- * index >= n_inputs, a NULL pointer, n < 0.
+ * index >= n_inputs, a NULL pointer, n < 0 or n >= 2^40.
  */
 int fuse_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_inputs,
                np_dtype in_dt, void* out, np_dtype out_dt, int64_t n, hipStream_t stream);

@@ -76,6 +76,8 @@ int validate_chain(const np_op* ops, int n_ops, const void* const* inputs, int n
     return fail(NP_EINVAL, "n_inputs = %d, must be 1..%d", n_inputs, NP_MAX_INPUTS);
   if (!valid_dt(in_dt) || !valid_dt(out_dt)) return fail(NP_EINVAL, "unknown dtype");
   if (n < 0) return fail(NP_EINVAL, "n = %lld < 0", (long long)n);
+  if (n >= ((int64_t)1 << 40))  // beyond any device's memory; keeps grid sizes below 2^31
+    return fail(NP_EINVAL, "n = %lld is not below 2^40", (long long)n);
   if (ops[0].kind != NP_LOAD) return fail(NP_EINVAL, "ops[0] must be NP_LOAD");
   for (int i = 0; i < n_ops; ++i) {
     const int k = ops[i].kind;

@@ -44,3 +44,26 @@ def misaligned(t: torch.Tensor) -> torch.Tensor:
 
 
 ORACLE_DT = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def gpu_normal(shape, dt: str, seed: int, mean: float = 0.0, std: float = 1.0) -> torch.Tensor:
+    """N(mean, std^2) draws made on the device by a seeded torch generator (fp32,
+    rounded once to dt), in 2^26-element chunks: for inputs of billions of
+    elements, where a host draw and copy would dominate the test. The oracle
+    gets the values back from the device (sampled)."""
+    n = 1
+    for s in shape:
+        n *= int(s)
+    out = empty((n,), dt)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    chunk = 1 << 26
+    for i in range(0, n, chunk):
+        m = min(chunk, n - i)
+        v = torch.randn(m, generator=g, device="cuda", dtype=torch.float32)
+        if std != 1.0:
+            v.mul_(std)
+        if mean != 0.0:
+            v.add_(mean)
+        out[i:i + m].copy_(v)
+    return out.view(shape)

@@ -55,6 +55,7 @@ def _err(npa):
     ([(synth.LOAD, 0, 0)], 5, 4, "n_inputs"),
     ([(synth.LOAD, 0, 0)] * 33, 1, 4, "n_ops"),
     ([(synth.LOAD, 0, 0)], 1, -1, "n = -1"),
+    ([(synth.LOAD, 0, 0)], 1, 1 << 40, "not below 2^40"),
 ])
 def test_fuse_chain_rejects(npa, ops, n_inputs, n, msg):
     arr, k = npa._ops(ops)
