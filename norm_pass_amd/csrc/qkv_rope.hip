@@ -28,7 +28,14 @@ namespace np {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kTokBlock = 384;
+// Threads per token workgroup. At H = 24, D = 128 bf16 a token is 1152 chunks:
+// 768 threads take two passes (the second half full). Measured on MI355X,
+// 16384 tokens, warm / cold: 384 threads 100-103 / 107-108 us; 640-896
+// threads 100-101 / 100-101 us; 288 threads 104-105 / 109 us.
+#ifndef NP_ROPE_TOK_BLOCK
+#define NP_ROPE_TOK_BLOCK 768
+#endif
+constexpr int kTokBlock = NP_ROPE_TOK_BLOCK;
 
 template <typename T, int NC>
 __global__ __launch_bounds__(kTokBlock) void rope_tok(RopeArgs a) {
