@@ -16,12 +16,13 @@
 namespace np {
 namespace {
 
-template <typename T, int VPT, bool HAS_R, bool HAS_G, bool HAS_B, bool HAS_H>
-__global__ __launch_bounds__(256) void ln_vec(const T* x, const T* r, const T* g, const T* b,
-                                              T* h, T* out, int cols, float eps) {
+template <typename T, int VPT, int WAVES, bool HAS_R, bool HAS_G, bool HAS_B, bool HAS_H>
+__global__ __launch_bounds__(64 * WAVES) void ln_vec(const T* x, const T* r, const T* g,
+                                                     const T* b, T* h, T* out, int cols,
+                                                     float eps) {
   constexpr int N = Vec<T>::N;
-  constexpr int THREADS = 256;
-  __shared__ float part_mu[4], part_var[4];
+  constexpr int THREADS = 64 * WAVES;
+  __shared__ float part_mu[WAVES], part_var[WAVES];
   const int64_t off = (int64_t)blockIdx.x * cols;
   const int nvec = cols / N;
   float hv[VPT][N];
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256) void ln_vec(const T* x, const T* r, const T* g
     }
     if (HAS_H && vi < nvec) store_vec_nt<T>(h + off + vi * N, hv[j]);
   }
-  const float mu = block_sum<4>(s, part_mu) / (float)cols;
+  const float mu = block_sum<WAVES>(s, part_mu) / (float)cols;
   float sq = 0.0f;
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) void ln_vec(const T* x, const T* r, const T* g
       if (vi < nvec) sq += hv[j][e] * hv[j][e];
     }
   }
-  const float rstd = 1.0f / sqrtf(block_sum<4>(sq, part_var) / (float)cols + eps);
+  const float rstd = 1.0f / sqrtf(block_sum<WAVES>(sq, part_var) / (float)cols + eps);
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int vi = threadIdx.x + j * THREADS;
@@ -115,22 +116,22 @@ __global__ __launch_bounds__(256) void ln_generic(const T* x, const T* r, const 
   }
 }
 
-template <typename T, int VPT, bool HAS_R, bool HAS_G, bool HAS_B, bool HAS_H>
+template <typename T, int VPT, int WAVES, bool HAS_R, bool HAS_G, bool HAS_B, bool HAS_H>
 void launch5(const void* x, const void* r, const void* g, const void* b, void* h, void* out,
              int64_t rows, int cols, float eps, hipStream_t s) {
-  hipLaunchKernelGGL((ln_vec<T, VPT, HAS_R, HAS_G, HAS_B, HAS_H>), dim3((unsigned)rows),
-                     dim3(256), 0, s, static_cast<const T*>(x), static_cast<const T*>(r),
+  hipLaunchKernelGGL((ln_vec<T, VPT, WAVES, HAS_R, HAS_G, HAS_B, HAS_H>), dim3((unsigned)rows),
+                     dim3(64 * WAVES), 0, s, static_cast<const T*>(x), static_cast<const T*>(r),
                      static_cast<const T*>(g), static_cast<const T*>(b), static_cast<T*>(h),
                      static_cast<T*>(out), cols, eps);
 }
 
-template <typename T, int VPT>
+template <typename T, int VPT, int WAVES>
 void launch_flags(const void* x, const void* r, const void* g, const void* b, void* h, void* out,
                   int64_t rows, int cols, float eps, hipStream_t s) {
   const int key = (r ? 8 : 0) | (g ? 4 : 0) | (b ? 2 : 0) | (h ? 1 : 0);
   switch (key) {
 #define NP_LN_CASE(K, R, G, B, H) \
-  case K: launch5<T, VPT, R, G, B, H>(x, r, g, b, h, out, rows, cols, eps, s); break;
+  case K: launch5<T, VPT, WAVES, R, G, B, H>(x, r, g, b, h, out, rows, cols, eps, s); break;
     NP_LN_CASE(15, true, true, true, true)
     NP_LN_CASE(14, true, true, true, false)
     NP_LN_CASE(13, true, true, false, true)
@@ -156,16 +157,18 @@ hipError_t launch_t(const void* x, const void* r, const void* g, const void* b, 
                     void* out, int64_t rows, int64_t cols, float eps, bool vec, hipStream_t s) {
   constexpr int N = Vec<T>::N;
   const int64_t nvec = cols / N;
-  if (vec && cols % N == 0 && nvec <= 256 * 8) {
+  // the row-length policy of the RMSNorm kernel: 4 waves up to 256 vectors,
+  // then 8 waves with 1, 2 or 4 vectors per thread
+  if (vec && cols % N == 0 && nvec <= 512 * 4) {
     const int c = (int)cols;
     if (nvec <= 256)
-      launch_flags<T, 1>(x, r, g, b, h, out, rows, c, eps, s);
+      launch_flags<T, 1, 4>(x, r, g, b, h, out, rows, c, eps, s);
     else if (nvec <= 512)
-      launch_flags<T, 2>(x, r, g, b, h, out, rows, c, eps, s);
+      launch_flags<T, 1, 8>(x, r, g, b, h, out, rows, c, eps, s);
     else if (nvec <= 1024)
-      launch_flags<T, 4>(x, r, g, b, h, out, rows, c, eps, s);
+      launch_flags<T, 2, 8>(x, r, g, b, h, out, rows, c, eps, s);
     else
-      launch_flags<T, 8>(x, r, g, b, h, out, rows, c, eps, s);
+      launch_flags<T, 4, 8>(x, r, g, b, h, out, rows, c, eps, s);
   } else {
     hipLaunchKernelGGL((ln_generic<T>), dim3((unsigned)rows), dim3(256), 0, s,
                        static_cast<const T*>(x), static_cast<const T*>(r),
