@@ -209,7 +209,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         fused=npa.bind("fuse_chain", synth.C1_CHAIN, [ta, tb], y1),
         unfused=npa.bind("unfused_chain", synth.C1_CHAIN, [ta, tb], y1),
         unfused_spec=("unfused_chain", (synth.C1_CHAIN, [ta, tb], y1)),
-        bytes=12 * n1, unfused_bytes=28 * n1, launches=3, kernel="chain_vec<float, float, 2")
+        bytes=12 * n1, unfused_bytes=28 * n1, launches=3, kernel="np_chain_spec_k4_n1048576")
     # C2
     lv = [tdev(x, "f16") for x in synth.c2_inputs()]
     hw = [(h, w) for h, w, _ in synth.YOLO_LEVELS]
@@ -278,7 +278,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         fused=npa.bind("fuse_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
         unfused=npa.bind("unfused_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
         unfused_spec=("unfused_qkv_rope", (qkv, q4, k4, v4, 24, 128, None, 10000.0, qs)),
-        bytes=fb, unfused_bytes=ub, launches=4, kernel="rope_vec")
+        bytes=fb, unfused_bytes=ub, launches=4, kernel="rope_tok")
     # C5
     ops = synth.c5_chain()
     t0 = time.perf_counter()
@@ -302,7 +302,8 @@ def build_workloads(torch, npa, synth, quick: bool):
             fused=fused,
             unfused=npa.bind("unfused_chain", ops, [xin], yo),
             unfused_spec=("unfused_chain", (ops, [xin], yo)),
-            bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29, kernel="chain_vec<_Float16",
+            bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29,
+            kernel="np_chain_spec_k30_n0_lut" if n >= table_min else "np_chain_scalar_k30_n0",
             path="table" if n >= table_min else "per element")
         if n >= table_min:
             W[name]["fused_per_element"] = per_element
@@ -354,7 +355,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         layout(nm, f"fp16 ChannelShuffle {nm[8:].upper()} [{N_}, {C_}, {H_}, {Wd}], groups {g} "
                    "(not in the step; baseline: naive strided copy)",
                xs, "f16", shp, "fuse_channel_shuffle", "naive_channel_shuffle", (g, lay), tf,
-               "tr_items<16>" if lay == 0 else "tr_small<2, true>")
+               "tr_items<16, true>" if lay == 0 else "tr_small<2, true>")
     # RMSNorm + linear + scale on the matrix cores (not in the step): fused
     # kernel vs RMSNorm -> GEMM + bias -> scale, and torch's bf16 linear
     # (the vendor GEMM) on the stored RMSNorm output, for context
