@@ -100,8 +100,9 @@ __device__ __forceinline__ int xcd_tile(int bid, int nb) {
 // the wave's LDS base + 16 l), through a ring of four 32-wide K stages, so the
 // loads of step s + 3 are in flight while step s runs on the matrix cores and
 // no registers hold staged data. LDS rows are 64 bytes (four 16-byte chunks);
-// chunk c of row r is stored at position c ^ ((r >> 1) & 3), so the 8 rows read
-// together by an MFMA fragment load hit distinct banks. The row sums of x^2
+// chunk c of row r is stored at position c ^ ((r >> 2) & 3), so the 16 rows
+// read together by an MFMA fragment load (gfx950: 16 lanes per cycle, 64
+// four-byte banks, 4 rows per 256-byte bank line) hit distinct banks. The row sums of x^2
 // come from the A fragments the MFMAs already read (packed dot products, in
 // the two waves with wn == wm: one per 128-row half, on different SIMDs).
 // Rows past M or N are loaded from the last valid row (outputs discarded); K
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(NTHR) void rms_linear_dma(const T* __restrict__ x,
 #pragma unroll
   for (int j = 0; j < D_NJ; ++j) {
     const int p = (wave * D_NJ + j) * 64 + lane;
-    const int r = p >> 2, c = (p & 3) ^ ((r >> 1) & 3);
+    const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
     oa[j] = (uint32_t)(((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2);
     ob[j] = (uint32_t)(((min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
   }
@@ -195,13 +196,13 @@ __global__ __launch_bounds__(NTHR) void rms_linear_dma(const T* __restrict__ x,
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * 32 * FM + 32 * i + l32;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 64 + ((c ^ ((r >> 1) & 3)) << 4));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
         __builtin_memcpy(&a[ks][i], &v, 16);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = wn * 32 * FN + 32 * j + l32;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 64 + ((c ^ ((r >> 1) & 3)) << 4));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
         __builtin_memcpy(&b[ks][j], &v, 16);
       }
     }
@@ -283,8 +284,12 @@ __global__ __launch_bounds__(NTHR) void rms_linear_dma(const T* __restrict__ x,
 // slice's MFMAs run (two register sets, reads spread between the MFMAs). Each
 // K step is 64 wide, so every row's 128 bytes -- one cache line -- arrive in
 // one step; two 64 KiB stages form the ring. LDS rows are 128 bytes and chunk
-// c of row r sits at position c ^ (r & 7), conflict free for the 8 rows an
-// MFMA fragment load reads together. The row sums of x^2 come from the A
+// c of row r sits at position c ^ ((r >> 1) & 7): gfx950 serves a 16-byte LDS
+// read 16 lanes per cycle from 64 four-byte banks, so the 16 rows of a phase
+// must fall in 16 different 16-byte bank groups (2 rows share a 256-byte bank
+// line, hence r & 1 and r >> 1). The earlier c ^ (r & 7) suits 8-lane
+// phases; rocprofv3 showed it stalled every fragment read for a 2-way bank
+// conflict (SQ_LDS_BANK_CONFLICT = 4 cycles per read). The row sums of x^2 come from the A
 // fragments the MFMAs read: each of the two waves sharing a 128-row half takes
 // two of its four 32-row blocks, so every wave runs the same code (a branch
 // around the sums would split the MFMA / LDS-read interleave of the waves that
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ 
 #pragma unroll
   for (int j = 0; j < Q_NJ; ++j) {
     const int p = (wave * Q_NJ + j) * 64 + lane;
-    const int r = p >> 3, c = (p & 7) ^ (r & 7);
+    const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
     oa[j] = (uint32_t)(((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2);
     ob[j] = (uint32_t)(((min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
   }
@@ -357,13 +362,13 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + 32 * rb(i) + l32;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 128 + ((c ^ (r & 7)) << 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
       __builtin_memcpy(&fa[buf][i], &v, 16);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 128 + 32 * j + l32;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 128 + ((c ^ (r & 7)) << 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
       __builtin_memcpy(&fb[buf][j], &v, 16);
     }
   };
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_reg4(const T* __restrict__ 
 #pragma unroll
   for (int j = 0; j < Q_NJ; ++j) {
     const int p = (wave * Q_NJ + j) * 64 + lane;
-    const int r = p >> 3, c = (p & 7) ^ (r & 7);
+    const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
     ob[j] = (uint32_t)(((min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
   }
   // staging map: vector q of this thread is row arow0 + 32 q, k chunk ac (the
@@ -551,7 +556,7 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_reg4(const T* __restrict__ 
         __builtin_memcpy(&av, e, 16);
       }
       const int r = arow0 + 32 * q;
-      const int off = r * 128 + ((ac ^ (r & 7)) << 4);
+      const int off = r * 128 + ((ac ^ ((r >> 1) & 7)) << 4);
       *reinterpret_cast<u32x4*>(As + off) = av;
       if (B_REGS) *reinterpret_cast<u32x4*>(As + Q_ABYTES + off) = xb[q];
     }
@@ -572,13 +577,13 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_reg4(const T* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + 32 * i + l32;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 128 + ((c ^ (r & 7)) << 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
       __builtin_memcpy(&fa[buf][i], &v, 16);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 128 + 32 * j + l32;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 128 + ((c ^ (r & 7)) << 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
       __builtin_memcpy(&fb[buf][j], &v, 16);
     }
   };
