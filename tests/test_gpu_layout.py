@@ -126,6 +126,7 @@ def test_empty_is_a_no_op(npa):
 @pytest.mark.parametrize("es,shape,groups", [
     (2, (3, 116, 28, 28), 2), (2, (2, 464, 7, 7), 2), (4, (2, 24, 5, 3), 3),
     (1, (4, 12, 6, 6), 4), (8, (2, 10, 3, 3), 5), (2, (1, 6, 1, 1), 6), (2, (2, 8, 4, 4), 1),
+    (4, (3, 22, 5, 7), 2), (8, (2, 14, 3, 5), 2), (1, (5, 18, 3, 3), 2), (2, (7, 6, 2, 3), 2),
 ])
 @pytest.mark.parametrize("fn", ["fuse", "naive"])
 def test_channel_shuffle_matches_oracle(npa, orc, layout, es, shape, groups, fn):
