@@ -473,9 +473,12 @@ int oracle_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, con
     for (int64_t k = 0; k < K; ++k) {
       const double xv = load(x, dt, m * K + k);
       const double wv = w_norm ? load(w_norm, dt, k) : 1.0;
-      // fused: the operand is x * w in dt; eager: the stored RMSNorm output
+      // fused: the operand is the product x * w held in fp32, as the
+      // section's kernel holds it (exact for 16-bit dt: the product of two
+      // such values fits binary32); eager: the RMSNorm kernel's output
+      // x * rstd * w, stored in dt
       a[k] = eager ? round_to((double)((long double)xv * rstd * (long double)wv), f)
-                   : round_to(xv * wv, f);
+                   : round_to(xv * wv, F32);
     }
     for (int64_t n = 0; n < N; ++n) {
       long double acc = 0.0L, mag = 0.0L;

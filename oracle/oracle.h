@@ -133,8 +133,13 @@ int oracle_rope_inv_freq(float base, int head_dim, float* inv);
  * (NULL: weight 1), Wt [N, K] (the linear weight with K contiguous: out = y
  * Wt^T), bias [N] (NULL: 0), out [M, N], all of dt:
  *   rstd_m = 1 / sqrt(mean_k x_mk^2 + eps)
- *   a_mk   = round_dt(x_mk * w_k)       (the linear layer's operand, in dt)
+ *   a_mk   = fp32(x_mk * w_k)           (the section's kernel keeps the
+ *                                        weighted input in an fp32 array; for
+ *                                        16-bit dt the product is exact there,
+ *                                        so a_mk is x_mk * w_k itself)
  *   out_mn = round_dt(scale * (rstd_m * sum_k a_mk * Wt_nk + bias_n))
+ * The mean square is taken of x (RMSNorm's definition), not of x * w as the
+ * section's listing squares it; the two agree when w = 1.
  * eager = 1: the unfused form, three stored steps: y = round_dt(x rstd w);
  * z = round_dt(sum_k y_mk Wt_nk + bias_n); out = round_dt(scale * z).
  * exact: optional [M, N] unrounded values. cond: optional [M, N]

@@ -181,3 +181,52 @@ def test_c5_eager_differs_but_close(orc):
     d = ulp_dist16(f.view(np.uint16), e.view(np.uint16))
     assert d.max() > 0  # rounding after every op changes bits (NaiveRT pitfalls list)
     assert np.abs(f.astype(np.float64) - e.astype(np.float64)).max() < 0.05
+
+
+# Hand-worked eager (unfused) cases. The unfused chain stores the running value
+# in the storage type after every operator (each small kernel writes its
+# tensor: DeepJIT write-up, section 1.1), the fused chain rounds once at the
+# end. Each case is op, then "subtract the stored value", so the eager result
+# is exactly 0 and the fused one is the rounding residual; an eager mode that
+# skipped the rounding after that op would return the residual instead.
+_EAGER_CASES = [
+    # 1 + 2^-11 is the midpoint of 1 and 1 + 2^-10: ties-to-even gives 1;
+    # the fused value 2^-11 is an fp16 normal (bits 0x1000)
+    ("add_c", [(LOAD, 0, 0.0), (ADD_C, 0, 2.0 ** -11), (ADD_C, 0, -1.0)], [[1.0]], 0x1000),
+    ("add_in", [(LOAD, 0, 0.0), (ADD_IN, 1, 0.0), (ADD_C, 0, -1.0)], [[1.0], [2.0 ** -11]], 0x1000),
+    # (1 + 2^-10)^2 = 1 + 2^-9 + 2^-20 -> fp16 1 + 2^-9; fused residual 2^-20,
+    # the fp16 subnormal 16 * 2^-24 (bits 0x0010)
+    ("mul_c", [(LOAD, 0, 0.0), (MUL_C, 0, 1 + 2.0 ** -10), (ADD_C, 0, -(1 + 2.0 ** -9))],
+     [[1 + 2.0 ** -10]], 0x0010),
+    ("scale", [(LOAD, 0, 0.0), (SCALE, 0, 1 + 2.0 ** -10), (ADD_C, 0, -(1 + 2.0 ** -9))],
+     [[1 + 2.0 ** -10]], 0x0010),
+    ("mul_in", [(LOAD, 0, 0.0), (MUL_IN, 1, 0.0), (ADD_C, 0, -(1 + 2.0 ** -9))],
+     [[1 + 2.0 ** -10], [1 + 2.0 ** -10]], 0x0010),
+    # sigma(1) = 0.7310585786 -> fp16 0.73095703125 (1497 * 2^-11); residual
+    # 1.015474e-4 -> 1704 * 2^-24 = 1.015663e-4 (bits 0x06A8)
+    ("sigmoid", [(LOAD, 0, 0.0), (SIGMOID, 0, 0.0), (ADD_C, 0, -0.73095703125)], [[1.0]], 0x06A8),
+    # e = 2.7182818285 -> fp16 2.71875 (1392 * 2^-9); residual -4.681715e-4
+    # -> -1964 * 2^-22 (bits 0x8FAC)
+    ("exp", [(LOAD, 0, 0.0), (EXP, 0, 0.0), (ADD_C, 0, -2.71875)], [[1.0]], 0x8FAC),
+    # tanh(1/2) = 0.4621171573 -> fp16 0.462158203125 (1893 * 2^-12); residual
+    # -4.104586e-5 -> -689 * 2^-24 (bits 0x82B1)
+    ("tanh", [(LOAD, 0, 0.0), (TANH, 0, 0.0), (ADD_C, 0, -0.462158203125)], [[0.5]], 0x82B1),
+]
+
+
+@pytest.mark.parametrize("name,ops,ins,fused_bits", _EAGER_CASES, ids=[c[0] for c in _EAGER_CASES])
+def test_eager_rounds_after_every_op_hand_worked(orc, name, ops, ins, fused_bits):
+    arrays = [np.array(v, np.float16) for v in ins]
+    e = orc.chain(ops, arrays, F16, eager=True).view(np.uint16)
+    f = orc.chain(ops, arrays, F16).view(np.uint16)
+    assert int(e[0]) == 0x0000, name
+    assert int(f[0]) == fused_bits, name
+
+
+def test_eager_bf16_storage_hand_worked(orc):
+    """bf16 storage: 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7, stored as 1;
+    the fused chain keeps 2^-8 (bf16 bits 0x3B80)."""
+    x = synth.to_bf16_bits(np.array([1.0], np.float32))
+    ops = [(LOAD, 0, 0.0), (ADD_C, 0, 2.0 ** -8), (ADD_C, 0, -1.0)]
+    assert int(orc.chain(ops, [x], BF16, in_dt=BF16, eager=True)[0]) == 0x0000
+    assert int(orc.chain(ops, [x], BF16, in_dt=BF16)[0]) == 0x3B80

@@ -130,3 +130,37 @@ def test_eager_close_to_fused(orc):
 def test_rejects_bad_arguments(orc):
     with pytest.raises(ValueError):
         orc.det_decode(_zero_levels([(2, 2)], 3, 4), [(2, 2)], [8.0], ANCH[:1], 3, 4)  # n_ch < 5
+
+
+def test_eager_hand_worked(orc):
+    """The unfused tail stores every step in fp16 (23 small kernels, each
+    writing its tensor: DeepJIT write-up, section 1.1); only the final cast to
+    fp32 is exact. One level of 8 x 8 cells, one anchor (30, 45), six channels,
+    stride 12 (not a power of two, so the stride multiply rounds); the logits
+    of cell (y, x) = (6, 6) as below, 0 elsewhere. Worked by hand:
+    - x and y: sigma(3.638671875) = 0.9743860854 -> fp16 0.974609375; + 6 =
+      6.974609375 -> fp16 6.9765625; x 12 = 83.71875 -> fp16 83.75. Fused:
+      (0.9743860854 + 6) x 12 = 83.692633 in fp32.
+    - w: e^1.2392578125 = 3.4530497032 -> fp16 3.453125; x 30 = 103.59375 ->
+      fp16 103.625. Fused: 103.591491.
+    - h: e^2.361328125 = 10.605026905 -> fp16 10.6015625; x 45 = 477.0703125
+      -> fp16 477.0. Fused: 477.226211.
+    - objectness and class: sigma(-0.07989501953125) = 0.4800368631 -> fp16
+      0.47998046875.
+    Skipping any one of the roundings (sigma, + cell, x stride on either
+    coordinate, exp, x anchor on either size, the class sigma) changes the
+    stored value. The other cells (logit 0) are exact in both forms."""
+    lv = np.zeros((1, 6, 8, 8), np.float16)
+    lv[0, :, 6, 6] = [3.638671875, 3.638671875, 1.2392578125, 2.361328125,
+                      -0.07989501953125, -0.07989501953125]
+    e = orc.det_decode([lv], [(8, 8)], [12.0], [[30.0, 45.0]], 1, 6, eager=True)
+    assert e[0, 6 * 8 + 6].tolist() == [83.75, 83.75, 103.625, 477.0, 0.47998046875,
+                                          0.47998046875]
+    f = orc.det_decode([lv], [(8, 8)], [12.0], [[30.0, 45.0]], 1, 6)
+    np.testing.assert_allclose(f[0, 6 * 8 + 6], [83.692633, 83.692633, 103.591491, 477.226211,
+                                                 0.4800368631, 0.4800368631], rtol=2e-7)
+    zero = np.zeros_like(lv)
+    base = orc.det_decode([zero], [(8, 8)], [12.0], [[30.0, 45.0]], 1, 6, eager=True)
+    others = np.ones(64, bool)
+    others[6 * 8 + 6] = False
+    assert np.array_equal(e[0, others], base[0, others])

@@ -126,3 +126,30 @@ def test_eager_close(orc):
 def test_rejects_bad_eps(orc):
     with pytest.raises(ValueError):
         orc.add_layernorm(np.zeros((1, 8), np.uint16), None, None, None, -1.0, BF16)
+
+
+def test_eager_hand_worked(orc):
+    """The nine-kernel unfused form stores each step in bf16. One row h =
+    (1.828125, 2.28125, -0.27734375), gamma = (1.1875, 0.82421875, 0.859375),
+    beta = (-0.009765625, -0.255859375, 0.1845703125), eps 1e-5, by hand:
+      mean = 3.83203125 / 3 = 1.27734375 -> bf16 1.28125
+      h - mean = 0.546875, 1, -1.55859375 -> bf16 0.546875, 1, -1.5625
+      squares = 0.299072265625, 1, 2.44140625 -> bf16 0.298828125, 1, 2.4375
+      var = 3.736328125 / 3 = 1.245442708 -> bf16 1.2421875
+      1/sqrt(1.2421875 + 1e-5) = 0.897231835 -> bf16 0.8984375
+      x rstd = 0.491333008, 0.8984375, -1.403808594 -> bf16 0.4921875,
+               0.8984375, -1.40625
+      x gamma = 0.58447265625, 0.740509033, -1.20849609375 -> bf16 0.5859375,
+               0.7421875, -1.2109375
+      + beta = 0.576171875, 0.486328125, -1.0263671875 -> bf16 0.578125,
+               0.486328125, -1.0234375 (bits 0x3F14, 0x3EF9, 0xBF83)
+    Fused: 0x3F14, 0x3EF9, 0xBF82. Skipping any one of the seven intermediate
+    roundings changes the eager result."""
+    bf = lambda v: synth.to_bf16_bits(np.array(v, np.float32))
+    h = bf([[1.828125, 2.28125, -0.27734375]])
+    g = bf([1.1875, 0.82421875, 0.859375])
+    b = bf([-0.009765625, -0.255859375, 0.1845703125])
+    _, e = orc.add_layernorm(h, None, g, b, 1e-5, BF16, eager=True)
+    assert [int(v) for v in e[0]] == [0x3F14, 0x3EF9, 0xBF83]
+    _, f = orc.add_layernorm(h, None, g, b, 1e-5, BF16)
+    assert [int(v) for v in f[0]] == [0x3F14, 0x3EF9, 0xBF82]

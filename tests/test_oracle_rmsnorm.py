@@ -131,3 +131,26 @@ def test_rejects_bad_eps(orc):
     x = np.zeros((1, 8), np.uint16)
     with pytest.raises(ValueError):
         orc.add_rmsnorm(x, None, None, 0.0, BF16)
+
+
+def test_eager_hand_worked(orc):
+    """The six-kernel unfused form stores each step in bf16 (add; square; row
+    mean; +eps and 1/sqrt; x rstd; x w). One row h = (-2.421875, 0.6640625,
+    0.7109375) (r = NULL), w = (0.8671875, 1.1640625, 0.88671875), worked by
+    hand:
+      h^2 = 5.865478515625, 0.44097900390625, 0.505432128906 -> bf16 5.875,
+            0.44140625, 0.50390625
+      mean = 6.8203125 / 3 = 2.2734375 -> bf16 2.28125
+      1/sqrt(2.28125 + 1e-6) = 0.662084566 -> bf16 0.66015625
+      h rstd = -1.598815918, 0.438385010, 0.469329834 -> bf16 -1.6015625,
+            0.4375, 0.46875
+      x w = -1.388854980, 0.50927734375, 0.415649414 -> bf16 -1.390625,
+            0.5078125, 0.416015625 (bits 0xBFB2, 0x3F02, 0x3ED5)
+    The fused form (one rounding) gives 0xBFB2, 0x3F03, 0x3ED6; skipping any
+    one of the four intermediate roundings changes the eager result."""
+    h = synth.to_bf16_bits(np.array([[-2.421875, 0.6640625, 0.7109375]], np.float32))
+    w = synth.to_bf16_bits(np.array([0.8671875, 1.1640625, 0.88671875], np.float32))
+    _, e = orc.add_rmsnorm(h, None, w, 1e-6, BF16, eager=True)
+    assert [int(v) for v in e[0]] == [0xBFB2, 0x3F02, 0x3ED5]
+    _, f = orc.add_rmsnorm(h, None, w, 1e-6, BF16)
+    assert [int(v) for v in f[0]] == [0xBFB2, 0x3F03, 0x3ED6]

@@ -125,3 +125,25 @@ def test_eager_q_double_rounding_close(orc):
     assert np.array_equal(k1, k2)
     d = np.abs(q1.view(np.int16).astype(np.int32) - q2.view(np.int16).astype(np.int32))
     assert d.max() <= 1
+
+
+def test_eager_hand_worked(orc):
+    """The unfused form stores the rotated Q in bf16 before the scale kernel.
+    T = 2, one head, head_dim 2 (one pair, inv_0 = 1), so token 1 has angle
+    exactly 1 rad. With (u, w) = (2.546875, 0.005035400390625), by hand:
+      o = (u cos 1 - w sin 1, w cos 1 + u sin 1) = (1.371845292, 2.145842053)
+      eager Q: bf16(o) = (1.375, 2.140625); x fl32(1/sqrt 128) =
+               (0.121533976, 0.189207...) -> bf16 (0.12158203125, 0.189453125)
+               (bits 0x3DF9, 0x3E42)
+      fused Q: o x q_scale = (0.121255137, ...) -> bf16 (0.12109375, ...)
+               (bits 0x3DF8, 0x3E42)
+    K carries no intermediate rounding, so both forms give bf16(o) = (1.375,
+    2.140625) (bits 0x3FB0, 0x4009)."""
+    u, w = 2.546875, 0.005035400390625
+    qkv = synth.to_bf16_bits(np.array([[0, 0, 0, 0, 0, 0], [u, w, u, w, u, w]], np.float32))
+    q, k, _ = orc.qkv_rope(qkv, 1, 2, 10000.0, QS, BF16, eager=True)
+    assert [int(x) for x in q[0, 1]] == [0x3DF9, 0x3E42]
+    assert [int(x) for x in k[0, 1]] == [0x3FB0, 0x4009]
+    q2, k2, _ = orc.qkv_rope(qkv, 1, 2, 10000.0, QS, BF16)
+    assert [int(x) for x in q2[0, 1]] == [0x3DF8, 0x3E42]
+    assert [int(x) for x in k2[0, 1]] == [0x3FB0, 0x4009]
