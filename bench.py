@@ -76,6 +76,7 @@ def rope_bytes(T, H, D, es=2):
 
 
 SETTLE_S = 0.25  # seconds of untimed steps before the warm-up steps
+PROFILE_FUSED, PROFILE_UNFUSED = 20, 2  # calls per workload in a counter run
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 VALU_PEAK = 256 * 64 * 2.4e9  # lane-instr/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
 
@@ -106,33 +107,165 @@ KERNEL_SOURCES = {
 }
 
 
+COUNTER_TABLE = os.path.join(PROFILES, "counters_hbm_traffic.md")
+# columns of a row of the committed counter table
+COUNTER_COLS = ["workload", "source hash", "FETCH bytes", "WRITE bytes", "traffic bytes",
+                "algorithmic bytes", "traffic / algorithmic", "VALU lane-instr / element"]
+
+
+def _sources_of(name: str):
+    base = name[:-len("_unfused")] if name.endswith("_unfused") else name
+    srcs = list(KERNEL_SOURCES[base])
+    if name.endswith("_unfused"):
+        srcs += ["norm_pass_amd/csrc/unfused.hip"]
+    return srcs
+
+
 def _counter_row(name: str):
-    """Row `| name | source hash | traffic bytes | ... | valu insts/element |` of
-    the committed rocprofv3 counter summary, if the kernel sources still hash
-    to what they were when the counters were taken."""
-    path = os.path.join(PROFILES, "counters_hbm_traffic.md")
-    if not os.path.exists(path):
+    """The committed counter table's row for `name` as a dict, if the kernel
+    sources still hash to what they were when the counters were taken."""
+    if not os.path.exists(COUNTER_TABLE):
         return None
-    for line in open(path):
+    for line in open(COUNTER_TABLE):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) >= 3 and cells[0] == name and re.fullmatch(r"[0-9a-f]{16}", cells[1]):
-            return cells if cells[1] == file_hash(*KERNEL_SOURCES[name]) else None
+        if len(cells) == len(COUNTER_COLS) and cells[0] == name and \
+                re.fullmatch(r"[0-9a-f]{16}", cells[1]):
+            if name.split("_unfused")[0] not in KERNEL_SOURCES or \
+                    cells[1] != file_hash(*_sources_of(name)):
+                return None
+            return dict(zip(COUNTER_COLS, cells))
     return None
+
+
+def _num(v):
+    try:
+        return float(v)
+    except (TypeError, ValueError):
+        return None
 
 
 def measured_traffic(name: str):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) or None."""
     row = _counter_row(name)
-    return float(row[2]) if row else None
+    return _num(row["traffic bytes"]) if row else None
 
 
 def measured_valu_per_element(name: str):
-    """Dynamic VALU lane-instructions per element (SQ_INSTS_VALU) or None."""
+    """Dynamic VALU lane-instructions per element (SQ_INSTS_VALU x 64) or None."""
     row = _counter_row(name)
-    try:
-        return float(row[-1]) if row else None
-    except ValueError:
-        return None
+    return _num(row["VALU lane-instr / element"]) if row else None
+
+
+def counter_fields(name: str) -> dict:
+    """fetch_B / write_B / bytes_ratio / valu_insts_per_elem of one call from
+    the committed counter table ({} when the sources changed since)."""
+    row = _counter_row(name)
+    if not row:
+        return {}
+    return {"fetch_B": _num(row["FETCH bytes"]), "write_B": _num(row["WRITE bytes"]),
+            "bytes_ratio": _num(row["traffic / algorithmic"]),
+            "valu_insts_per_elem": _num(row["VALU lane-instr / element"])}
+
+
+def _pmc_dispatches(run_dir: str, counter: str):
+    """[(kernel name, value)] per dispatch, in dispatch order, from a
+    rocprofv3 --pmc <counter> --output-format csv run under run_dir/counter."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, counter, "**", "*counter_collection.csv"),
+                      recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}/{counter}")
+    rows = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+                name, val = rows.get(key, (r.get("Kernel_Name", ""), 0.0))
+                rows[key] = (name, val + float(r["Counter_Value"]))
+    return [rows[k] for k in sorted(rows)]
+
+
+def summarize_counters(manifest_path: str, run_dir: str) -> str:
+    """The committed counter table from three counter runs of the profile pass
+    (FETCH_SIZE, WRITE_SIZE and SQ_INSTS_VALU, each its own rocprofv3 run).
+    The last dispatches of each run are the manifest's, in order, preceded by
+    the three calibration copies of 2^30 bytes each way: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are scaled by what they read for that copy.
+    SQ_INSTS_VALU counts wave instructions: x 64 lanes / elements."""
+    man = json.load(open(manifest_path))
+    disp = man["dispatches"]
+    total = sum(d["fused"] + d["unfused"] for d in disp)
+    cal_bytes = man["calibration_bytes"]
+    per = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE", "SQ_INSTS_VALU"):
+        vals = _pmc_dispatches(run_dir, counter)
+        if len(vals) < total + 3:
+            raise ValueError(f"{counter}: {len(vals)} dispatches, expected at least {total + 3}")
+        body = vals[len(vals) - total:]
+        cal = vals[len(vals) - total - 3:len(vals) - total]
+        scale = 1.0
+        if counter != "SQ_INSTS_VALU":
+            scale = cal_bytes / (sum(v for _, v in cal) / 3 * 1024.0)
+            per.setdefault("_factors", {})[counter] = scale
+        i = 0
+        for d in disp:
+            f = body[i:i + d["fused"]]
+            i += d["fused"]
+            u = body[i:i + d["unfused"]]
+            i += d["unfused"]
+            unit = 1024.0 * scale if counter != "SQ_INSTS_VALU" else 64.0
+            per.setdefault(d["workload"], {})[counter] = sum(v for _, v in f) / len(f) * unit
+            if d["unfused"]:
+                calls = d["unfused"] // d["unfused_launches"]
+                per.setdefault(d["workload"] + "_unfused", {})[counter] = \
+                    sum(v for _, v in u) / calls * unit
+    lines = ["| " + " | ".join(COUNTER_COLS) + " |", "|" + "---|" * len(COUNTER_COLS)]
+    for d in disp:
+        for name, alg in ((d["workload"], d["bytes"]), (d["workload"] + "_unfused",
+                                                         d["unfused_bytes"])):
+            if name not in per:
+                continue
+            c = per[name]
+            tr = c["FETCH_SIZE"] + c["WRITE_SIZE"]
+            lines.append("| " + " | ".join([
+                name, file_hash(*_sources_of(name)), f"{c['FETCH_SIZE']:.0f}",
+                f"{c['WRITE_SIZE']:.0f}", f"{tr:.0f}", str(alg), f"{tr / alg:.3f}",
+                f"{c['SQ_INSTS_VALU'] / d['elements']:.2f}"]) + " |")
+    fac = per["_factors"]
+    lines.append("")
+    lines.append(f"Calibration factors (bytes of the 2^30-byte copy / counter bytes): FETCH_SIZE "
+                 f"{fac['FETCH_SIZE']:.4f}, WRITE_SIZE {fac['WRITE_SIZE']:.4f}.")
+    return "\n".join(lines)
+
+
+def summarize_graph_trace(path: str, launches: int) -> str:
+    """Kernel durations, gaps between the kernels of one call and gaps between
+    calls, from a kernel trace of --graph-trace (its last 300 calls' worth of
+    dispatches: 100 eager calls, 100 one-call graph replays, 100 calls in two
+    replays of a 50-call graph)."""
+    import csv
+    import statistics as st
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    seq = rows[-300 * launches:]
+    out = ["| form | kernel us (median) | gap inside a call us | gap between calls us | "
+           "call period us |", "|---|---|---|---|---|"]
+    for i, name in enumerate(("eager launches", "one call per graph replay",
+                              "50 calls per graph replay")):
+        part = seq[i * 100 * launches:(i + 1) * 100 * launches]
+        s = [int(r["Start_Timestamp"]) for r in part]
+        e = [int(r["End_Timestamp"]) for r in part]
+        dur = [b - a for a, b in zip(s, e)]
+        inside = [s[j] - e[j - 1] for j in range(1, len(part)) if j % launches]
+        between = [s[j] - e[j - 1] for j in range(launches, len(part), launches)]
+        period = (s[-launches] - s[0]) / 99
+        f = lambda v: f"{v / 1e3:.2f}"
+        out.append(f"| {name} | {f(st.median(dur))} | "
+                   f"{f(st.median(inside)) if inside else '-'} | {f(st.median(between))} | "
+                   f"{f(period)} |")
+    return "\n".join(out)
 
 
 # ------------------------------------------------------------------ timing
@@ -154,21 +287,51 @@ def time_calls(torch, fn, reps: int, trials: int):
     return res[len(res) // 2], res[max(0, len(res) // 10)], res[min(len(res) - 1, (9 * len(res)) // 10)]
 
 
-def graph_time(torch, npa, spec, reps: int, trials: int):
-    """Per-replay seconds of one call's launches captured in one HIP graph
-    (bound inside the capture, so the launches go to the capturing stream)."""
+def graph_time(torch, npa, spec, copies: int, trials: int):
+    """Per-call seconds of one call's launches captured in a HIP graph and
+    replayed: (a) `copies` calls captured back to back in one graph, one replay
+    per trial, divided by `copies` -- launch cost removed, every kernel and its
+    HBM round trip kept; (b) one call per graph, replayed back to back. On this
+    ROCm stack a graph launch costs ~16 us of host time however small the
+    graph (one empty node: 16 us per replay against 2 us for an eager launch),
+    which (b) shows and (a) amortises. Calls are bound inside the capture, so
+    their launches go to the capturing stream."""
     name, args = spec
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         npa.bind(name, *args)()
     torch.cuda.current_stream().wait_stream(s)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    copies = max(1, min(copies, 64))
+    gm = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gm):
+        call = npa.bind(name, *args)
+        for _ in range(copies):
+            call()
+    many, _, _ = time_calls(torch, gm.replay, 1, trials)
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
         npa.bind(name, *args)()
-    med, _, _ = time_calls(torch, g.replay, reps, trials)
+    one, _, _ = time_calls(torch, g1.replay, max(3, copies), trials)
     torch.cuda.synchronize()
-    return med
+    return many / copies, one
+
+
+def single_launch(torch, fn, trials: int = 41):
+    """Median device time of one isolated call: synchronise, event, the call,
+    event (the launch latency a lone small kernel pays)."""
+    res = []
+    for _ in range(trials):
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        res.append(a.elapsed_time(b) / 1e3)
+    res.sort()
+    return res[len(res) // 2]
 
 
 def pick_reps(torch, fn, target_s=0.003):
@@ -182,10 +345,34 @@ def pick_reps(torch, fn, target_s=0.003):
 
 # ------------------------------------------------------------- workloads
 
+def _bits(t):
+    """Host copy of a device tensor: fp32 as float32, fp16 / bf16 as uint16 bits."""
+    import numpy as np
+    t = t.detach().contiguous().cpu()
+    if t.dtype == np.float32 or str(t.dtype) == "torch.float32":
+        return t.numpy()
+    return t.view(dtype=__import__("torch").int16).numpy().view(np.uint16)
+
+
+def _rotation(torch, make, set_bytes: int, total=1 << 30):
+    """Bound calls over fresh buffer sets of `set_bytes` each, enough sets to
+    touch `total` bytes (4x the 256 MB Infinity Cache): rotating through them
+    measures HBM-to-HBM rather than cache-served repeats."""
+    return [make() for _ in range(max(3, -(-total // set_bytes)))]
+
+
 def build_workloads(torch, npa, synth, quick: bool):
     dev = "cuda"
     W = {}
     import numpy as np
+    S = cpu_samples(quick)
+
+    def sampler(fused, grab):
+        def run():
+            fused()
+            torch.cuda.synchronize()
+            return grab()
+        return run
 
     def tdev(a, dt):
         a = np.ascontiguousarray(a)
@@ -204,12 +391,21 @@ def build_workloads(torch, npa, synth, quick: bool):
     t0 = time.perf_counter()
     npa.fuse_chain_prepare(synth.C1_CHAIN, 2, npa.NP_F32, npa.NP_F32, n1)
     compile_ms = {"c1": round((time.perf_counter() - t0) * 1e3, 1)}
+    def c1_set():
+        a_, b_ = torch.empty_like(ta), torch.empty_like(tb)
+        a_.copy_(ta)
+        b_.copy_(tb)
+        return npa.bind("fuse_chain", synth.C1_CHAIN, [a_, b_], torch.empty_like(y1))
+    f1 = npa.bind("fuse_chain", synth.C1_CHAIN, [ta, tb], y1)
     W["c1"] = dict(
         desc="fp32 relu(a+b)*0.5, 1,048,576 elements",
-        fused=npa.bind("fuse_chain", synth.C1_CHAIN, [ta, tb], y1),
+        cold=_rotation(torch, c1_set, 12 * n1), single=True,
+        sample_out=sampler(f1, lambda: _bits(y1)),
+        fused=f1,
         unfused=npa.bind("unfused_chain", synth.C1_CHAIN, [ta, tb], y1),
         unfused_spec=("unfused_chain", (synth.C1_CHAIN, [ta, tb], y1)),
-        bytes=12 * n1, unfused_bytes=28 * n1, launches=3, kernel="np_chain_spec_k4_n1048576")
+        bytes=12 * n1, unfused_bytes=28 * n1, launches=3, kernel="np_chain_spec_k4_n1048576",
+        elements=n1)
     # C2
     lv = [tdev(x, "f16") for x in synth.c2_inputs()]
     hw = [(h, w) for h, w, _ in synth.YOLO_LEVELS]
@@ -218,12 +414,21 @@ def build_workloads(torch, npa, synth, quick: bool):
     out2 = torch.empty((1, 25200, 85), device=dev)
     ws2 = torch.empty(npa.det_workspace_bytes(lv), dtype=torch.uint8, device=dev)
     fb, ub = det_bytes(hw)
+    def c2_set():
+        lv_ = [torch.empty_like(t) for t in lv]
+        for a_, b_ in zip(lv_, lv):
+            a_.copy_(b_)
+        return npa.bind("fuse_det_decode", lv_, st, an, torch.empty_like(out2))
+    f2 = npa.bind("fuse_det_decode", lv, st, an, out2)
     W["c2"] = dict(
         desc="YOLO decode fp16 [1,255,80|40|20] -> fp32 [1,25200,85]",
-        fused=npa.bind("fuse_det_decode", lv, st, an, out2),
+        cold=_rotation(torch, c2_set, fb), single=True,
+        sample_out=sampler(f2, lambda: _bits(out2)),
+        fused=f2,
         unfused=npa.bind("unfused_det_decode", lv, st, an, out2, ws2),
         unfused_spec=("unfused_det_decode", (lv, st, an, out2, ws2)),
-        bytes=fb, unfused_bytes=ub, launches=23, kernel="det_decode_kernel")
+        bytes=fb, unfused_bytes=ub, launches=23, kernel="det_decode_kernel",
+        elements=sum(t.numel() for t in lv))
     # C3
     rows = 2048 if quick else 16384
     x, r, w = synth.c3_inputs(rows=rows)
@@ -241,12 +446,14 @@ def build_workloads(torch, npa, synth, quick: bool):
         st3[0].copy_(tx)
         st3[1].copy_(tr)
     cold3 = [npa.bind("fuse_add_rmsnorm", a_, b_, tw, c_, d_, 1e-6) for a_, b_, c_, d_ in sets3]
+    f3 = npa.bind("fuse_add_rmsnorm", tx, tr, tw, h3, o3, 1e-6)
     W["c3"] = dict(cold=cold3,
         desc=f"bf16 residual add + RMSNorm [{rows}, 4096], eps 1e-6",
-        fused=npa.bind("fuse_add_rmsnorm", tx, tr, tw, h3, o3, 1e-6),
+        sample_out=sampler(f3, lambda: (_bits(h3[:S["rows"]]), _bits(o3[:S["rows"]]))),
+        fused=f3,
         unfused=npa.bind("unfused_add_rmsnorm", tx, tr, tw, h3, o3, ws3, 1e-6),
         unfused_spec=("unfused_add_rmsnorm", (tx, tr, tw, h3, o3, ws3, 1e-6)),
-        bytes=fb, unfused_bytes=ub, launches=6, kernel="rms_vec")
+        bytes=fb, unfused_bytes=ub, launches=6, kernel="rms_vec", elements=rows * 4096)
     # LayerNorm (the next row on the same machinery): same shape as C3, not in the step
     gam = tdev(synth.normal((4096,), 1013, "bf16", mean=1.0, std=0.1), "bf16")
     bet = tdev(synth.normal((4096,), 1014, "bf16", std=0.1), "bf16")
@@ -255,12 +462,14 @@ def build_workloads(torch, npa, synth, quick: bool):
     wsl = torch.empty(npa.layernorm_workspace_bytes(rows, 4096, torch.bfloat16),
                       dtype=torch.uint8, device=dev)
     fb, ub = ln_bytes(rows, 4096)
+    fl = npa.bind("fuse_add_layernorm", tx, tr, gam, bet, hl, ol, 1e-5)
     W["ln"] = dict(
         desc=f"bf16 residual add + LayerNorm [{rows}, 4096], eps 1e-5 (not in the step)",
-        fused=npa.bind("fuse_add_layernorm", tx, tr, gam, bet, hl, ol, 1e-5),
+        sample_out=sampler(fl, lambda: (_bits(hl[:S["rows"]]), _bits(ol[:S["rows"]]))),
+        fused=fl,
         unfused=npa.bind("unfused_add_layernorm", tx, tr, gam, bet, hl, ol, wsl, 1e-5),
         unfused_spec=("unfused_add_layernorm", (tx, tr, gam, bet, hl, ol, wsl, 1e-5)),
-        bytes=fb, unfused_bytes=ub, launches=9, kernel="ln_vec")
+        bytes=fb, unfused_bytes=ub, launches=9, kernel="ln_vec", elements=rows * 4096)
     # C4
     T = 2048 if quick else 16384
     qkv = tdev(synth.c4_inputs(tokens=T), "bf16")
@@ -273,12 +482,15 @@ def build_workloads(torch, npa, synth, quick: bool):
         st4[0].copy_(qkv)
     cold4 = [npa.bind("fuse_qkv_rope", a_, b_, c_, d_, 24, 128, None, 10000.0, qs)
              for a_, b_, c_, d_ in sets4]
+    f4 = npa.bind("fuse_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs)
+    nt = S["tokens"]
     W["c4"] = dict(cold=cold4,
         desc=f"bf16 QKV split + RoPE + scale, [{T}, 3x24x128] -> 3 x [24, {T}, 128]",
-        fused=npa.bind("fuse_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
+        sample_out=sampler(f4, lambda: tuple(_bits(t[:, :nt]) for t in (q4, k4, v4))),
+        fused=f4,
         unfused=npa.bind("unfused_qkv_rope", qkv, q4, k4, v4, 24, 128, None, 10000.0, qs),
         unfused_spec=("unfused_qkv_rope", (qkv, q4, k4, v4, 24, 128, None, 10000.0, qs)),
-        bytes=fb, unfused_bytes=ub, launches=4, kernel="rope_tok")
+        bytes=fb, unfused_bytes=ub, launches=4, kernel="rope_tok", elements=qkv.numel())
     # C5
     ops = synth.c5_chain()
     t0 = time.perf_counter()
@@ -297,16 +509,25 @@ def build_workloads(torch, npa, synth, quick: bool):
             fused()
             npa.np_set_chain_table_min(old)
 
+        ns = n if name == "c5_small" else S["c5_large"]
         W[name] = dict(
             desc=f"seeded 29-op fp16 chain, {n:,} elements",
+            sample_out=sampler(fused, lambda yo=yo, ns=ns: _bits(yo[:ns])),
             fused=fused,
             unfused=npa.bind("unfused_chain", ops, [xin], yo),
             unfused_spec=("unfused_chain", (ops, [xin], yo)),
-            bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29,
+            bytes=4 * n, unfused_bytes=29 * 4 * n, launches=29, elements=n,
             kernel="np_chain_spec_k30_n0_lut" if n >= table_min else "np_chain_scalar_k30_n0",
             path="table" if n >= table_min else "per element")
         if n >= table_min:
             W[name]["fused_per_element"] = per_element
+        if name == "c5_small":
+            def c5_set(xin=xin, yo=yo):
+                x_ = torch.empty_like(xin)
+                x_.copy_(xin)
+                return npa.bind("fuse_chain", ops, [x_], torch.empty_like(yo))
+            W[name]["cold"] = _rotation(torch, c5_set, 4 * n)
+            W[name]["single"] = True
     # Layout (the runtime page's strided transpose / ChannelShuffle; not in the
     # step): the LDS-staged kernels against the naive strided copy, and torch's
     # own permute().contiguous() for context. Three buffer sets each for the
@@ -321,14 +542,20 @@ def build_workloads(torch, npa, synth, quick: bool):
             sets.append((y, torch.empty_like(x)))
         xo = sets[0][1]
         nbytes = x.numel() * x.element_size()
-        W[name] = dict(
+        fz = npa.bind(fused_name, x, xo, *extra_args)
+        if name == "tr":
+            # out [1, S, R, 1]: the oracle's sample is the first tr_rows input rows
+            grab = lambda: _bits(xo.view(S_, R_)[:, :S["tr_rows"]]).reshape(1, S_, S["tr_rows"], 1)
+        else:
+            grab = lambda: _bits(xo[:S["shuffle_batch"]])
+        W[name] = dict(sample_out=sampler(fz, grab),
             cold=[npa.bind(fused_name, a_, b_, *extra_args) for a_, b_ in sets],
             desc=desc,
             fused=npa.bind(fused_name, x, xo, *extra_args),
             unfused=npa.bind(naive_name, x, xo, *extra_args),
             unfused_spec=(naive_name, (x, xo) + tuple(extra_args)),
             torch=lambda: torch_fn(x), bytes=2 * nbytes, unfused_bytes=2 * nbytes,
-            launches=1, kernel=kernel,
+            launches=1, kernel=kernel, elements=x.numel(),
             plan=npa.np_transpose_plan(x.data_ptr(), xo.data_ptr(), shape, x.element_size()))
 
     B_, R_, S_, E_ = synth.TRANSPOSE_2D
@@ -373,17 +600,19 @@ def build_workloads(torch, npa, synth, quick: bool):
     # into LDS. The call with the norm weight kept separate is timed as well.
     Wf = torch.empty_like(Wr)
     npa.np_fold_norm_weight(wr, Wr, Wf)
+    frl = npa.bind("fuse_rmsnorm_linear", xr, None, Wf, br, orl, 1e-6, sc)
     W["rl"] = dict(
         desc=f"bf16 RMSNorm + linear + scale, x [{Mr}, {Kr}] x Wt [{Nr}, {Kr}]^T, norm weight "
              "folded into Wt (not in the step)",
-        fused=npa.bind("fuse_rmsnorm_linear", xr, None, Wf, br, orl, 1e-6, sc),
+        sample_out=sampler(frl, lambda: _bits(orl[:S["rl_rows"]])),
+        fused=frl,
         fused_unfolded=npa.bind("fuse_rmsnorm_linear", xr, wr, Wr, br, orl, 1e-6, sc),
         unfused=npa.bind("unfused_rmsnorm_linear", xr, wr, Wr, br, orl, wsr, 1e-6, sc),
         unfused_spec=("unfused_rmsnorm_linear", (xr, wr, Wr, br, orl, wsr, 1e-6, sc)),
         torch=lambda: torch.nn.functional.linear(yr, Wr, br).mul_(sc),
         plan=None, bytes=2 * (Mr * Kr + Nr * Kr + Mr * Nr + Kr + Nr),
         unfused_bytes=2 * (3 * Mr * Kr + Nr * Kr + 3 * Mr * Nr + Kr + Nr),
-        flops=2 * Mr * Nr * Kr, launches=3, kernel="rms_linear_dma4")
+        flops=2 * Mr * Nr * Kr, launches=3, kernel="rms_linear_dma4", elements=Mr * Nr)
     W["_compile_ms"] = compile_ms
     return W
 
@@ -426,69 +655,269 @@ def disk_cache_timing(torch, npa, synth):
             "rejects": s1["rejects"] - s0["rejects"]}
 
 
-def cpu_baseline(synth, quick: bool):
-    """The oracle, untuned, timed on the host on a bounded sample of every config;
-    the step time is extrapolated from each config's measured oracle rate."""
+def host_cores():
+    """(threads the oracle leg uses = this process's CPU affinity, the
+    machine's hardware concurrency, the CPU model name)."""
+    P = len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return P, os.cpu_count(), model
+
+
+def _split(n: int, parts: int):
+    """Contiguous [lo, hi) ranges covering range(n) in at most `parts` pieces."""
+    parts = max(1, min(parts, n))
+    b = [n * i // parts for i in range(parts + 1)]
+    return [(b[i], b[i + 1]) for i in range(parts)]
+
+
+def cpu_samples(quick: bool) -> dict:
+    """Sizes of the oracle's samples: each a prefix of the workload (the seeded
+    generator draws a prefix of a tensor the same way the whole tensor is
+    drawn), so the GPU's outputs on the same prefix are compared with it."""
+    return {"rows": 256 if quick else 2048, "tokens": 256 if quick else 2048,
+            "c5_large": (1 << 20) if quick else (1 << 23), "tr_rows": 256 if quick else 1024,
+            "shuffle_batch": 16 if quick else 128, "rl_rows": 2 if quick else 8}
+
+
+def oracle_jobs(synth, quick: bool, P: int) -> dict:
+    """Per config: the oracle on its sample, as P contiguous chunks (rows,
+    tokens, elements or levels) whose results `combine` joins; `bytes` are the
+    sample's algorithmic bytes (flop for rl)."""
     import numpy as np
     import oracle
-    rates = {}
-    samples = []
-
-    def timed(fn):
-        t0 = time.perf_counter()
-        fn()
-        return time.perf_counter() - t0
+    S = cpu_samples(quick)
+    J = {}
+    cat = np.concatenate
 
     a, b = synth.c1_inputs()
-    rates["c1"] = 12 * a.size / timed(lambda: oracle.chain(synth.C1_CHAIN, [a, b], 0))
-    samples.append("c1 full")
+    J["c1"] = dict(sample="c1 full", bytes=12 * a.size, combine=cat, chunks=[
+        (lambda lo=lo, hi=hi: oracle.chain(synth.C1_CHAIN, [a[lo:hi], b[lo:hi]], 0))
+        for lo, hi in _split(a.size, P)])
     lv = synth.c2_inputs()
     hw = [(h, w) for h, w, _ in synth.YOLO_LEVELS]
+    st = [s_ for _, _, s_ in synth.YOLO_LEVELS]
     anc = np.array(synth.YOLO_ANCHORS, np.float32).reshape(3, 3, 2)
-    rates["c2"] = det_bytes(hw)[0] / timed(
-        lambda: oracle.det_decode(lv, hw, [8.0, 16.0, 32.0], anc, 3, 85, in_dt=1))
-    samples.append("c2 full")
-    rows = 256 if quick else 2048
+    J["c2"] = dict(sample="c2 full (one chunk per level)", bytes=det_bytes(hw)[0],
+                   combine=lambda r: cat(r, axis=1), chunks=[
+        (lambda l=l: oracle.det_decode([lv[l]], [hw[l]], [st[l]], anc[l:l + 1], 3, 85, in_dt=1))
+        for l in range(3)])
+    rows = S["rows"]
     x, r, w = synth.c3_inputs(rows=rows)
-    rates["c3"] = rms_bytes(rows, 4096)[0] / timed(lambda: oracle.add_rmsnorm(x, r, w, 1e-6, 2))
-    samples.append(f"c3 {rows} of 16384 rows")
-    toks = 256 if quick else 2048
+    pair = lambda res: tuple(cat([t[i] for t in res]) for i in range(2))
+    J["c3"] = dict(sample=f"c3 {rows} of 16384 rows", bytes=rms_bytes(rows, 4096)[0],
+                   combine=pair, chunks=[
+        (lambda lo=lo, hi=hi: oracle.add_rmsnorm(x[lo:hi], r[lo:hi], w, 1e-6, 2))
+        for lo, hi in _split(rows, P)])
+    toks = S["tokens"]
     qkv = synth.c4_inputs(tokens=toks)
-    rates["c4"] = rope_bytes(toks, 24, 128)[0] / timed(
-        lambda: oracle.qkv_rope(qkv, 24, 128, 10000.0, 0.08838834764831845, 2))
-    samples.append(f"c4 {toks} of 16384 tokens")
+    qs = float(np.float32(1.0 / math.sqrt(128.0)))
+    J["c4"] = dict(sample=f"c4 {toks} of 16384 tokens", bytes=rope_bytes(toks, 24, 128)[0],
+                   combine=lambda res: tuple(cat([t[i] for t in res], axis=1) for i in range(7)),
+                   chunks=[
+        (lambda lo=lo, hi=hi: oracle.qkv_rope(qkv[lo:hi], 24, 128, 10000.0, qs, 2,
+                                              positions=np.arange(lo, hi, dtype=np.int32),
+                                              want_bound=True))
+        for lo, hi in _split(toks, P)])
     ops = synth.c5_chain()
-    xs = synth.c5_inputs(1 << 16)
-    rates["c5_small"] = 4 * xs.size / timed(lambda: oracle.chain(ops, [xs], 1))
-    samples.append("c5 65,536 full")
-    nl = (1 << 20) if quick else (1 << 23)
-    xl = synth.c5_inputs(nl, seed=77)
-    rates["c5_large"] = 4 * nl / timed(lambda: oracle.chain(ops, [xl], 1))
-    samples.append(f"c5 {nl:,} of 268,435,456 elements")
-    # the next rows (not in the step): the same oracle, each on its own sample
-    # (their GPU figures are reported beside these)
+    triple = lambda res: tuple(cat([t[i] for t in res]) for i in range(3))
+    for name, n in (("c5_small", 1 << 16), ("c5_large", S["c5_large"])):
+        xs = synth.c5_inputs(n)
+        J[name] = dict(sample=(f"{name} {n:,} full" if name == "c5_small"
+                               else f"c5_large {n:,} of 268,435,456 elements"),
+                       bytes=4 * n, combine=triple, chunks=[
+            (lambda lo=lo, hi=hi, xs=xs: oracle.chain(ops, [xs[lo:hi]], 1, want_bound=True))
+            for lo, hi in _split(n, P)])
     gam = synth.normal((4096,), 1013, "bf16", mean=1.0, std=0.1)
     bet = synth.normal((4096,), 1014, "bf16", std=0.1)
-    rates["ln"] = ln_bytes(rows, 4096)[0] / timed(
-        lambda: oracle.add_layernorm(x, r, gam, bet, 1e-5, 2))
-    samples.append(f"ln {rows} of 16384 rows")
-    tr_rows = 256 if quick else 1024
-    xt = synth.transpose_inputs((1, tr_rows, 8192, 1))
-    rates["tr"] = 2 * xt.nbytes / timed(lambda: oracle.transpose021(xt))
-    samples.append(f"tr {tr_rows} of 8192 rows")
-    nb = 16 if quick else 128
+    J["ln"] = dict(sample=f"ln {rows} of 16384 rows", bytes=ln_bytes(rows, 4096)[0],
+                   combine=lambda res: tuple(cat([t[i] for t in res]) for i in range(3)), chunks=[
+        (lambda lo=lo, hi=hi: oracle.add_layernorm(x[lo:hi], r[lo:hi], gam, bet, 1e-5, 2,
+                                                   want_exact=True))
+        for lo, hi in _split(rows, P)])
+    tr_rows = S["tr_rows"]
+    tr_cols = 2048 if quick else synth.TRANSPOSE_2D[2]
+    xt = synth.transpose_inputs((1, tr_rows, tr_cols, 1))
+    J["tr"] = dict(sample=f"tr {tr_rows} of {tr_cols} rows", bytes=2 * xt.nbytes,
+                   combine=lambda res: cat(res, axis=2), chunks=[
+        (lambda lo=lo, hi=hi: oracle.transpose021(np.ascontiguousarray(xt[:, lo:hi])))
+        for lo, hi in _split(tr_rows, P)])
+    nb = S["shuffle_batch"]
     for name, layout in (("shuffle_nchw", 0), ("shuffle_nhwc", 1)):
         xs_ = synth.shuffle_inputs((nb,) + synth.SHUFFLE_NCHW[1:], layout=layout)
-        rates[name] = 2 * xs_.nbytes / timed(
-            lambda: oracle.channel_shuffle(xs_, synth.SHUFFLE_GROUPS, layout))
-        samples.append(f"{name} batch {nb} of 1024")
-    mr = 2 if quick else 8
+        J[name] = dict(sample=f"{name} batch {nb} of 1024", bytes=2 * xs_.nbytes, combine=cat,
+                       chunks=[
+            (lambda lo=lo, hi=hi, xs_=xs_, layout=layout:
+             oracle.channel_shuffle(xs_[lo:hi], synth.SHUFFLE_GROUPS, layout))
+            for lo, hi in _split(nb, P)])
+    mr = S["rl_rows"]
     xr, wr, Wr, br = synth.rmsnorm_linear_inputs()
     M, K, N = synth.RMS_LINEAR_SHAPE
-    rates["rl_flops"] = 2 * mr * K * N / timed(
-        lambda: oracle.rmsnorm_linear(xr[:mr], wr, Wr, br, 1e-6, synth.RMS_LINEAR_SCALE, 2))
-    samples.append(f"rl {mr} of {M} rows (flop/s)")
-    return rates, "; ".join(samples)
+    J["rl"] = dict(sample=f"rl {mr} of {M} rows (flop/s)", bytes=2 * mr * K * N,
+                   combine=cat, chunks=[
+        (lambda lo=lo, hi=hi: oracle.rmsnorm_linear(xr[lo:hi], wr, Wr, br, 1e-6,
+                                                    synth.RMS_LINEAR_SCALE, 2))
+        for lo, hi in _split(mr, P)])
+    return J
+
+
+def _ord16(bits):
+    import numpy as np
+    b = np.asarray(bits).view(np.uint16).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def _ulp16_dist(a, b):
+    import numpy as np
+    return np.abs(_ord16(a) - _ord16(b))
+
+
+def _spacing(v, p, emin):
+    import numpy as np
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), emin)
+    return np.ldexp(1.0, (e - (p - 1)).astype(np.int64))
+
+
+def _half_vals(bits, dt):
+    import numpy as np
+    bits = np.asarray(bits).view(np.uint16)
+    if dt == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _half_parity(got, ref, dt, exact=None, bound=None) -> dict:
+    """<= 2 ulp of the output type; an element beyond counts as an exemption
+    when it lies within the oracle's fp32 bound plus one ulp of the exact
+    value (cancellation), else as a failure."""
+    import numpy as np
+    d = _ulp16_dist(got, ref).ravel()
+    beyond = d > 2
+    ex = fail = 0
+    if beyond.any():
+        if exact is not None and bound is not None:
+            p, emin = (11, -14) if dt == "f16" else (8, -126)
+            gv = _half_vals(np.asarray(got).ravel()[beyond], dt)
+            e = np.asarray(exact).ravel()[beyond]
+            ok = np.abs(gv - e) <= np.asarray(bound).ravel()[beyond] + _spacing(e, p, emin)
+            ex, fail = int(ok.sum()), int((~ok).sum())
+        else:
+            fail = int(beyond.sum())
+    return {"max_ulp": int(d.max()) if d.size else 0, "exempt_count": ex, "fail_count": fail,
+            "n": int(d.size)}
+
+
+def _f32_parity(got, ref) -> dict:
+    import numpy as np
+    g = np.asarray(got, np.float64).ravel()
+    r = np.asarray(ref, np.float64).ravel()
+    rel = np.abs(g - r) / np.where(r == 0, 1.0, np.abs(r))
+    bad = np.where(r == 0, g != 0, rel > 1e-6)
+    return {"max_rel": float(rel.max()) if rel.size else 0.0, "fail_count": int(bad.sum()),
+            "n": int(g.size),
+            "bitexact": bool(np.array_equal(np.asarray(got, np.float32).view(np.uint32),
+                                            np.asarray(ref, np.float32).view(np.uint32)))}
+
+
+def parity_of(k: str, gpu, ref) -> dict:
+    """Compare the GPU's outputs on the oracle's sample (fp32: <= 1e-6
+    relative; fp16 / bf16: <= 2 ulp with counted exemptions; layout and copies
+    bit for bit)."""
+    import numpy as np
+    if k == "c1":
+        p = _f32_parity(gpu, ref)
+        p["bitexact_layout"] = p["bitexact"]
+        return p
+    if k == "c2":
+        p = _f32_parity(gpu, ref)
+        # placement: every (row, column) holds the value the oracle puts there
+        p["bitexact_layout"] = None
+        p["layout_checked"] = p["fail_count"] == 0
+        return p
+    if k == "c3":
+        gh, go = gpu
+        rh, ro = ref
+        p = _half_parity(go, ro, "bf16")
+        p["bitexact_layout"] = bool(np.array_equal(gh, rh))  # the stored residual sum h
+        return p
+    if k == "ln":
+        # gamma * y + beta can cancel: an element beyond 2 ulp counts as an
+        # exemption when it lies within one bf16 ulp of its row's largest
+        # |value| of the exact result (the LayerNorm parity test's rule)
+        gh, go = gpu
+        rh, ro, ex = ref
+        p = _half_parity(go, ro, "bf16")
+        d = _ulp16_dist(go, ro)
+        bad = d > 2
+        if bad.any():
+            scale = np.abs(ex).max(axis=1, keepdims=True) * np.ones_like(ex)
+            ok = np.abs(_half_vals(go, "bf16").reshape(ex.shape) - ex)[bad] <= \
+                scale[bad] * 2.0 ** -7
+            p["exempt_count"], p["fail_count"] = int(ok.sum()), int((~ok).sum())
+        p["bitexact_layout"] = bool(np.array_equal(gh, rh))
+        return p
+    if k == "c4":
+        gq, gk, gv = gpu
+        rq, rk, rv, eq, ek, bq, bk = ref
+        pq = _half_parity(gq, rq, "bf16", eq, bq)
+        pk = _half_parity(gk, rk, "bf16", ek, bk)
+        return {"max_ulp": max(pq["max_ulp"], pk["max_ulp"]),
+                "exempt_count": pq["exempt_count"] + pk["exempt_count"],
+                "fail_count": pq["fail_count"] + pk["fail_count"], "n": pq["n"] + pk["n"],
+                "bitexact_layout": bool(np.array_equal(gv, rv))}  # V: a bit copy
+    if k in ("c5_small", "c5_large"):
+        out, exact, bound = ref
+        p = _half_parity(gpu, out.view(np.uint16), "f16", exact, bound)
+        p["bitexact_layout"] = None
+        return p
+    if k in ("tr", "shuffle_nchw", "shuffle_nhwc"):
+        eq = bool(np.array_equal(np.asarray(gpu).view(np.uint8).ravel(),
+                                 np.asarray(ref).view(np.uint8).ravel()))
+        return {"bitexact_layout": eq, "fail_count": 0 if eq else 1, "n": int(np.asarray(ref).size)}
+    if k == "rl":
+        # against the page's unrounded operand: the matrix cores take the
+        # folded bf16 weight, so elements beyond 2 ulp are expected and
+        # counted (the tests bound each one)
+        d = _ulp16_dist(gpu, ref).ravel()
+        return {"max_ulp": int(d.max()), "beyond_2ulp": int((d > 2).sum()), "n": int(d.size),
+                "bit_equal_frac": round(float((d == 0).mean()), 4), "bitexact_layout": None}
+    return {}
+
+
+def cpu_leg(synth, quick: bool, gpu_samples: dict):
+    """The oracle, untuned, on the host: a bounded sample of every config,
+    once on one thread and once split into contiguous chunks over P threads
+    (the oracle's C calls release the GIL). Each config's rate extrapolates
+    the step time; the P-thread outputs are compared with the GPU's outputs on
+    the same sample (the parity block)."""
+    from concurrent.futures import ThreadPoolExecutor
+    P, hw_threads, model = host_cores()
+    jobs = oracle_jobs(synth, quick, P)
+    rate1, rateP, parity = {}, {}, {}
+    samples = []
+    with ThreadPoolExecutor(P) as pool:
+        for k, job in jobs.items():
+            t0 = time.perf_counter()
+            for c in job["chunks"]:
+                c()
+            t1 = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            res = list(pool.map(lambda c: c(), job["chunks"]))
+            tP = time.perf_counter() - t0
+            rate1[k] = job["bytes"] / t1
+            rateP[k] = job["bytes"] / tP
+            samples.append(job["sample"])
+            if k in gpu_samples:
+                parity[k] = parity_of(k, gpu_samples[k], job["combine"](res))
+    return rate1, rateP, parity, "; ".join(samples), (P, hw_threads, model)
 
 
 # ------------------------------------------------------------------- main
@@ -504,7 +933,24 @@ def main(argv=None):
     ap.add_argument("--profile", action="store_true",
                     help="only a few launches of each kernel (for rocprofv3 runs)")
     ap.add_argument("--only", default="", help="profile mode: comma-separated workloads")
+    ap.add_argument("--manifest", default="", help="profile mode: write the dispatch manifest here")
+    ap.add_argument("--graph-trace", default="", metavar="WORKLOAD",
+                    help="for a kernel trace: the workload's unfused call 100 times eagerly, "
+                         "then 100 replays of a graph holding one call, then 2 replays of a "
+                         "graph holding 50 calls")
+    ap.add_argument("--summarize-graph-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "LAUNCHES"),
+                    help="print kernel durations and gaps of a --graph-trace kernel trace")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("MANIFEST", "RUN_DIR"),
+                    help="print the counter table from rocprofv3 --pmc runs: RUN_DIR holds "
+                         "one sub-directory per counter (FETCH_SIZE, WRITE_SIZE, SQ_INSTS_VALU)")
     args = ap.parse_args(argv)
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters))
+        return 0
+    if args.summarize_graph_trace:
+        print(summarize_graph_trace(args.summarize_graph_trace[0],
+                                    int(args.summarize_graph_trace[1])))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: the fused chains shard without any exchange, so "
               "there is no multi-GPU path to run (use --gpus 1).", file=sys.stderr)
@@ -530,26 +976,72 @@ def main(argv=None):
         f"({getattr(props, 'gcnArchName', '?')}, {props.multi_processor_count} CUs)")
 
     if args.profile:
-        # a copy of known size for counter calibration, then each kernel a few times
-        import numpy as _np  # noqa: F401
+        # a copy of known size for counter calibration, then each workload's
+        # fused call PROFILE_FUSED times and unfused call PROFILE_UNFUSED
+        # times, in W's order; the manifest lists the dispatches so that
+        # --summarize-counters can split the counter run by workload
         n = 1 << 28
         src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
+        only = [x for x in args.only.split(",") if x]
+        for _ in range(20):  # clocks up before anything is counted
+            W["c5_large"]["fused"]()
+        torch.cuda.synchronize()
         for _ in range(3):
             npa.unfused_chain([(synth.LOAD, 0, 0.0)], [src], dst)
-        only = [x for x in args.only.split(",") if x]
+        manifest = []
         for name, w in W.items():
             if only and name not in only:
                 continue
-            for _ in range(20):  # warm clocks: rocprofv3 averages every dispatch
+            for _ in range(PROFILE_FUSED):
                 w["fused"]()
-            for _ in range(2):
+            for _ in range(PROFILE_UNFUSED):
                 w["unfused"]()
+            manifest.append({"workload": name, "fused": PROFILE_FUSED,
+                             "unfused": PROFILE_UNFUSED * w["launches"],
+                             "unfused_launches": w["launches"], "elements": w["elements"],
+                             "bytes": w["bytes"], "unfused_bytes": w["unfused_bytes"]})
         if "c5_large_pe" in only and "fused_per_element" in W["c5_large"]:
-            for _ in range(20):  # the per-element kernel on the same data
+            for _ in range(PROFILE_FUSED):  # the per-element kernel on the same data
                 W["c5_large"]["fused_per_element"]()
+            w = W["c5_large"]
+            manifest.append({"workload": "c5_large_pe", "fused": PROFILE_FUSED, "unfused": 0,
+                             "unfused_launches": 0, "elements": w["elements"],
+                             "bytes": w["bytes"], "unfused_bytes": w["unfused_bytes"]})
         torch.cuda.synchronize()
+        if args.manifest:
+            with open(args.manifest, "w") as f:
+                json.dump({"calibration_bytes": 4 * n, "dispatches": manifest}, f, indent=1)
         log("[bench] profile pass done")
+        return 0
+
+    if args.graph_trace:
+        name, a_ = W[args.graph_trace]["unfused_spec"]
+        eager = npa.bind(name, *a_)
+        for _ in range(100):
+            eager()
+        torch.cuda.synchronize()
+        graphs = []
+        for copies in (1, 50):
+            s_ = torch.cuda.Stream()
+            s_.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s_):
+                npa.bind(name, *a_)()
+            torch.cuda.current_stream().wait_stream(s_)
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_):
+                c_ = npa.bind(name, *a_)
+                for _ in range(copies):
+                    c_()
+            graphs.append(g_)
+        torch.cuda.synchronize()
+        for _ in range(100):
+            graphs[0].replay()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graphs[1].replay()
+        torch.cuda.synchronize()
+        log(f"[bench] graph trace of {args.graph_trace} done")
         return 0
 
     order = ["c1", "c2", "c3", "c4", "c5_small", "c5_large"]
@@ -611,6 +1103,24 @@ def main(argv=None):
     log(f"[bench] {args.steps} steps: {step_s * 1e6:.1f} us/step (wall {wall:.3f}s); "
         f"{dom} {t_dom * 1e6:.1f} us per launch in the step")
 
+    # the same steps with the 2^28 chain evaluated per element (its
+    # specialised kernel, not the prepared table): the fused chain's own rate
+    step_pe_s = None
+    if "fused_per_element" in W["c5_large"]:
+        pe_fns = [W[k]["fused_per_element"] if k == "c5_large" else W[k]["fused"] for k in order]
+        for _ in range(max(args.warmup, 1)):
+            for f in pe_fns:
+                f()
+        s2, e2 = ev(), ev()
+        s2.record()
+        for _ in range(args.steps):
+            for f in pe_fns:
+                f()
+        e2.record()
+        torch.cuda.synchronize()
+        step_pe_s = s2.elapsed_time(e2) / 1e3 / args.steps
+        log(f"[bench] steps with the 2^28 chain per element: {step_pe_s * 1e6:.1f} us/step")
+
     per = {}
     extra = [k for k in W if k not in order]
     for k in order + extra:
@@ -619,9 +1129,10 @@ def main(argv=None):
         f_med, f_p10, f_p90 = time_calls(torch, w["fused"], reps, args.trials)
         reps_u = pick_reps(torch, w["unfused"])
         u_med, _, _ = time_calls(torch, w["unfused"], reps_u, max(5, args.trials // 2))
-        # the same unfused launches captured once in a HIP graph and replayed:
+        # the same unfused launches captured in a HIP graph and replayed:
         # launch cost removed, every intermediate HBM round trip kept
-        g_med = graph_time(torch, npa, w["unfused_spec"], reps_u, max(5, args.trials // 2))
+        g_med, g_one = graph_time(torch, npa, w["unfused_spec"], reps_u,
+                                  max(5, args.trials // 2))
         gbps = w["bytes"] / f_med / 1e9
         cold = None
         if "cold" in w:
@@ -642,11 +1153,21 @@ def main(argv=None):
             "unfused": {"launches": w["launches"], "us_med": round(u_med * 1e6, 3),
                         "GBps": round(w["unfused_bytes"] / u_med / 1e9, 1),
                         "bytes": w["unfused_bytes"],
-                        "graph_us_med": round(g_med * 1e6, 3)},
+                        "graph_us_med": round(g_med * 1e6, 3),
+                        "graph_one_call_per_replay_us_med": round(g_one * 1e6, 3)},
             "speedup": round(u_med / f_med, 2),
         }
         if cold:
             per[k]["cold"] = cold
+        if w.get("single"):
+            per[k]["single_launch_us"] = round(single_launch(torch, w["fused"]) * 1e6, 3)
+            per[k]["unfused"]["single_call_us"] = round(single_launch(torch, w["unfused"]) * 1e6, 3)
+        cr = counter_fields(k)
+        if cr:
+            per[k].update(cr)
+        cu = counter_fields(k + "_unfused")
+        if cu:
+            per[k]["unfused"].update(cu)
         if "torch" in w:
             t_med, _, _ = time_calls(torch, w["torch"], reps, max(5, args.trials // 2))
             per[k]["torch_us_med"] = round(t_med * 1e6, 3)
@@ -738,25 +1259,40 @@ def main(argv=None):
 
     cpu = None
     if not args.no_cpu:
+        # the GPU's outputs on the oracle's samples (fused call re-run first:
+        # the unfused and cold runs share some output buffers), then the
+        # oracle on the host: one thread, then P threads; the P-thread
+        # outputs are the parity reference
+        gpu_samples = {k: W[k]["sample_out"]() for k in order + extra if "sample_out" in W[k]}
         t0 = time.perf_counter()
-        rates, sample = cpu_baseline(synth, args.quick)
-        est = sum(W[k]["bytes"] / rates[k] for k in order)
-        cpu = {"value": round(step_bytes / est / 1e9, 4), "unit": "GB/s", "cores": 1,
+        rate1, rateP, parity, sample, (P, hw_threads, model) = cpu_leg(synth, args.quick,
+                                                                        gpu_samples)
+        est1 = sum(W[k]["bytes"] / rate1[k] for k in order)
+        estP = sum(W[k]["bytes"] / rateP[k] for k in order)
+        cpu = {"value": round(step_bytes / estP / 1e9, 4), "unit": "GB/s", "cores": P,
                "kind": "oracle", "sample": sample,
-               "per_config_GBps": {k: round(v / 1e9, 4) for k, v in rates.items()
-                                   if k != "rl_flops"},
-               "rl_GFLOPs": round(rates["rl_flops"] / 1e9, 4),
+               "value_1_thread": round(step_bytes / est1 / 1e9, 4),
+               "threads": P, "hardware_concurrency": hw_threads, "cpu_model": model,
+               "per_config_GBps": {k: round(v / 1e9, 4) for k, v in rateP.items() if k != "rl"},
+               "per_config_GBps_1_thread": {k: round(v / 1e9, 4) for k, v in rate1.items()
+                                            if k != "rl"},
+               "rl_GFLOPs": round(rateP["rl"] / 1e9, 4),
+               "rl_GFLOPs_1_thread": round(rate1["rl"] / 1e9, 4),
                "seconds": round(time.perf_counter() - t0, 1)}
-        # beside each row's GPU figure: the oracle's rate on its sample
+        # beside each row's GPU figure: the oracle's rate on its sample, and
+        # the parity of the GPU's outputs on that sample
         for k in order + extra:
-            if k in rates:
-                per[k]["cpu_oracle_GBps"] = round(rates[k] / 1e9, 4)
-                per[k]["gpu_over_cpu_oracle"] = round(per[k]["GBps"] * 1e9 / rates[k], 1)
+            if k in rateP and k != "rl":
+                per[k]["cpu_oracle_GBps"] = round(rateP[k] / 1e9, 4)
+                per[k]["gpu_over_cpu_oracle"] = round(per[k]["GBps"] * 1e9 / rateP[k], 1)
+            if k in parity:
+                per[k]["parity"] = parity[k]
         if "rl" in per:
-            per["rl"]["cpu_oracle_GFLOPs"] = round(rates["rl_flops"] / 1e9, 4)
+            per["rl"]["cpu_oracle_GFLOPs"] = round(rateP["rl"] / 1e9, 4)
             per["rl"]["gpu_over_cpu_oracle"] = round(
-                per["rl"]["TFLOPs"] * 1e12 / rates["rl_flops"], 1)
-        log(f"[bench] cpu oracle {cpu['value']} GB/s ({cpu['seconds']} s)")
+                per["rl"]["TFLOPs"] * 1e12 / rateP["rl"], 1)
+        log(f"[bench] cpu oracle {cpu['value']} GB/s on {P} threads, {cpu['value_1_thread']} "
+            f"GB/s on one ({cpu['seconds']} s)")
 
     disk = disk_cache_timing(torch, npa, synth)
     log(f"[bench] prepare of the 29-op chain: {disk['compile_ms']} ms compiling, "
@@ -770,10 +1306,15 @@ def main(argv=None):
         "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded Philox normals; see synth/)",
+        "value_per_element": (round(step_bytes / step_pe_s / 1e9, 1) if step_pe_s else None),
+        "ms_per_step_per_element": round(step_pe_s * 1e3, 4) if step_pe_s else None,
         "config": {"workload": "one fused pass over all five chains: C1 fp32 relu(a+b)*0.5 1M; "
                                "C2 YOLO decode fp16 3 levels; C3 bf16 add+RMSNorm 16384x4096; "
                                "C4 bf16 QKV split+RoPE+scale 16384x24x128; C5 29-op fp16 chain "
-                               "65,536 and 268,435,456",
+                               "65,536 (evaluated per element) and 268,435,456 (streamed "
+                               "through the chain's 65,536-entry table, filled once by "
+                               "fuse_chain_prepare; value_per_element: the same step with the "
+                               "chain evaluated per element)",
                    "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 1),
                    "step_bytes": step_bytes, "quick": args.quick},
         "roofline": roof,

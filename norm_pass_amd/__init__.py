@@ -115,6 +115,48 @@ def _keep(stream, *tensors):
             t.record_stream(stream)
 
 
+def _need(cond: bool, fn: str, msg: str):
+    if not cond:
+        raise ValueError(f"{fn}: {msg}")
+
+
+def _dev(fn: str, name: str, t, dtype=None, numel=None):
+    """A device buffer argument: a contiguous tensor, of `dtype` and with
+    `numel` elements when those are given. Returns t (None passes)."""
+    if t is None:
+        return None
+    _need(isinstance(t, torch.Tensor), fn, f"{name} must be a torch tensor")
+    _need(t.is_contiguous(), fn, f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, fn, f"{name} is {t.dtype}, expected {dtype}")
+    if numel is not None:
+        _need(t.numel() == numel, fn, f"{name} has {t.numel()} elements, expected {numel}")
+    return t
+
+
+def _on_gpu(fn: str, *tensors):
+    """Last check of a builder (after every shape and type check): all device
+    buffers live on a GPU."""
+    for t in tensors:
+        if isinstance(t, (list, tuple)):
+            _on_gpu(fn, *t)
+        elif t is not None:
+            _need(t.is_cuda, fn, "every tensor must be on a GPU")
+
+
+def _float_dtype(fn: str, t):
+    _need(isinstance(t, torch.Tensor) and t.dtype in _DT, fn,
+          "tensors must be float32, float16 or bfloat16")
+    return t.dtype
+
+
+def _rows_cols(fn: str, x):
+    """[..., cols] viewed as rows of cols (every leading axis is a row index)."""
+    _need(x.dim() >= 1 and x.shape[-1] >= 1, fn, "x needs a last axis of at least one element")
+    cols = x.shape[-1]
+    return x.numel() // cols, cols
+
+
 def _ops(ops):
     arr = (np_op * len(ops))()
     for i, (k, a, c) in enumerate(ops):
@@ -171,6 +213,14 @@ def np_empty_launches(count: int, stream=None):
 # hand back a zero-argument callable for tight launch loops.
 
 def _a_fuse_chain(ops, inputs, out, stream=None):
+    fn = "fuse_chain"
+    _need(1 <= len(inputs) <= MAX_INPUTS, fn, f"1..{MAX_INPUTS} inputs")
+    dt = _float_dtype(fn, inputs[0])
+    _float_dtype(fn, out)
+    for j, t in enumerate(inputs):
+        _dev(fn, f"inputs[{j}]", t, dt, out.numel())
+    _dev(fn, "out", out)
+    _on_gpu(fn, inputs, out)
     arr, k = _ops(ops)
     ptrs = (C.c_void_p * len(inputs))(*[t.data_ptr() for t in inputs])
     _keep(stream, out, *inputs)
@@ -195,35 +245,81 @@ def det_rows(levels, n_anchors: int) -> int:
 
 def _a_fuse_det_decode(levels, strides, anchors, out, n_anchors: int = 3, n_ch: int = 85,
                        stream=None):
+    fn = "fuse_det_decode"
+    _need(len(levels) >= 1 and len(strides) == len(levels) and len(anchors) == len(levels), fn,
+          "one stride and one anchor list per level")
+    dt = _float_dtype(fn, levels[0])
+    batch = levels[0].shape[0] if levels[0].dim() == 4 else 0
+    for l, t in enumerate(levels):
+        _need(t.dim() == 4 and t.shape[0] == batch and t.shape[1] == n_anchors * n_ch, fn,
+              f"levels[{l}] must be [batch, n_anchors * n_ch, H, W] with one batch size")
+        _dev(fn, f"levels[{l}]", t, dt)
+        _need(len(anchors[l]) == n_anchors and all(len(p) == 2 for p in anchors[l]), fn,
+              f"anchors[{l}] must hold n_anchors (w, h) pairs")
+    _dev(fn, "out", out, torch.float32, batch * det_rows(levels, n_anchors) * n_ch)
+    _on_gpu(fn, levels, out)
     ptrs, nl, H, W, st, an = _det_args(levels, strides, anchors)
     _keep(stream, out, *levels)
     return (ptrs, nl, H, W, st, an, n_anchors, n_ch, levels[0].shape[0], dtype_code(levels[0]),
             _ptr(out), _stream(stream))
 
 
+def _norm_checks(fn, x, r, weights, h_out, out):
+    dt = _float_dtype(fn, x)
+    rows, cols = _rows_cols(fn, x)
+    _dev(fn, "x", x, dt)
+    for name, t in (("r", r), ("h_out", h_out), ("out", out)):
+        _dev(fn, name, t, dt, x.numel())
+    for name, t in weights:
+        _dev(fn, name, t, dt, cols)
+    _on_gpu(fn, x, r, h_out, out, [t for _, t in weights])
+    return rows, cols
+
+
 def _a_fuse_add_rmsnorm(x, r, w, h_out, out, eps: float = 1e-6, stream=None):
+    rows, cols = _norm_checks("fuse_add_rmsnorm", x, r, (("w", w),), h_out, out)
     _keep(stream, x, r, w, h_out, out)
-    return (_ptr(x), _ptr(r), _ptr(w), _ptr(h_out), _ptr(out), x.shape[0], x.shape[-1], eps,
+    return (_ptr(x), _ptr(r), _ptr(w), _ptr(h_out), _ptr(out), rows, cols, eps,
             dtype_code(x), _stream(stream))
 
 
 def _a_fuse_qkv_rope(qkv, q, k, v, n_heads: int, head_dim: int, positions=None,
                      base: float = 10000.0, q_scale: float | None = None, stream=None):
+    fn = "fuse_qkv_rope"
     if q_scale is None:
         q_scale = 1.0 / math.sqrt(head_dim)
+    dt = _float_dtype(fn, qkv)
+    _need(qkv.dim() >= 1, fn, "qkv must be [T, 3 * n_heads * head_dim]")
+    T = qkv.shape[0]
+    _dev(fn, "qkv", qkv, dt, T * 3 * n_heads * head_dim)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t is not None, fn, f"{name} is required")
+        _dev(fn, name, t, dt, n_heads * T * head_dim)
+    _dev(fn, "positions", positions, torch.int32, T)
+    _on_gpu(fn, qkv, q, k, v, positions)
     _keep(stream, qkv, q, k, v, positions)
-    return (_ptr(qkv), _ptr(q), _ptr(k), _ptr(v), qkv.shape[0], n_heads, head_dim,
+    return (_ptr(qkv), _ptr(q), _ptr(k), _ptr(v), T, n_heads, head_dim,
             _ptr(positions), base, q_scale, dtype_code(qkv), _stream(stream))
 
 
 def _a_fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps: float = 1e-5, stream=None):
+    rows, cols = _norm_checks("fuse_add_layernorm", x, r, (("gamma", gamma), ("beta", beta)),
+                              h_out, out)
     _keep(stream, x, r, gamma, beta, h_out, out)
-    return (_ptr(x), _ptr(r), _ptr(gamma), _ptr(beta), _ptr(h_out), _ptr(out), x.shape[0],
-            x.shape[-1], eps, dtype_code(x), _stream(stream))
+    return (_ptr(x), _ptr(r), _ptr(gamma), _ptr(beta), _ptr(h_out), _ptr(out), rows, cols, eps,
+            dtype_code(x), _stream(stream))
+
+
+def _workspace(fn, t):
+    _need(t is not None, fn, "a workspace tensor is required")
+    _dev(fn, "workspace", t)
+    _on_gpu(fn, t)
+    return t
 
 
 def _a_unfused_add_layernorm(x, r, gamma, beta, h_out, out, workspace, eps: float = 1e-5,
                              stream=None):
+    _workspace("unfused_add_layernorm", workspace)
     a = _a_fuse_add_layernorm(x, r, gamma, beta, h_out, out, eps, stream)
     _keep(stream, workspace)
     return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
@@ -235,6 +331,18 @@ _a_unfused_qkv_rope = _a_fuse_qkv_rope
 
 def _a_fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps: float = 1e-6, scale: float = 1.0,
                            stream=None):
+    fn = "fuse_rmsnorm_linear"
+    dt = _float_dtype(fn, x)
+    _need(x.dim() == 2 and Wt.dim() == 2 and Wt.shape[1] == x.shape[1], fn,
+          "x must be [M, K] and Wt [N, K]")
+    M, K = x.shape
+    N = Wt.shape[0]
+    _dev(fn, "x", x, dt)
+    _dev(fn, "Wt", Wt, dt)
+    _dev(fn, "w_norm", w_norm, dt, K)
+    _dev(fn, "bias", bias, dt, N)
+    _dev(fn, "out", out, dt, M * N)
+    _on_gpu(fn, x, Wt, w_norm, bias, out)
     _keep(stream, x, w_norm, Wt, bias, out)
     return (_ptr(x), _ptr(w_norm), _ptr(Wt), _ptr(bias), _ptr(out), x.shape[0], Wt.shape[0],
             x.shape[-1], eps, scale, dtype_code(x), _stream(stream))
@@ -242,6 +350,7 @@ def _a_fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps: float = 1e-6, scale: f
 
 def _a_unfused_rmsnorm_linear(x, w_norm, Wt, bias, out, workspace, eps: float = 1e-6,
                               scale: float = 1.0, stream=None):
+    _workspace("unfused_rmsnorm_linear", workspace)
     a = _a_fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps, scale, stream)
     _keep(stream, workspace)
     return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
@@ -251,6 +360,8 @@ def _dense(*ts):
     for t in ts:
         if not t.is_contiguous():
             raise ValueError("layout calls need contiguous (dense row-major) tensors")
+        if not t.is_cuda:
+            raise ValueError("layout calls need GPU tensors")
 
 
 def _tr_shape(x, shape):
@@ -298,12 +409,14 @@ _a_naive_channel_shuffle = _a_fuse_channel_shuffle
 
 def _a_unfused_det_decode(levels, strides, anchors, out, workspace, n_anchors: int = 3,
                           n_ch: int = 85, stream=None):
+    _workspace("unfused_det_decode", workspace)
     a = _a_fuse_det_decode(levels, strides, anchors, out, n_anchors, n_ch, stream)
     _keep(stream, workspace)
     return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
 
 
 def _a_unfused_add_rmsnorm(x, r, w, h_out, out, workspace, eps: float = 1e-6, stream=None):
+    _workspace("unfused_add_rmsnorm", workspace)
     a = _a_fuse_add_rmsnorm(x, r, w, h_out, out, eps, stream)
     _keep(stream, workspace)
     return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
@@ -393,6 +506,14 @@ def fuse_rmsnorm_linear(x, w_norm, Wt, bias, out, eps: float = 1e-6, scale: floa
 def np_fold_norm_weight(w_norm, Wt, Wt_folded, stream=None):
     """Wt_folded = round(w_norm * Wt) per element (the norm weight moved into the
     linear weight, once); Wt [N, K]."""
+    fn = "np_fold_norm_weight"
+    dt = _float_dtype(fn, Wt)
+    _need(Wt.dim() == 2, fn, "Wt must be [N, K]")
+    _need(w_norm is not None, fn, "w_norm is required")
+    _dev(fn, "Wt", Wt, dt)
+    _dev(fn, "w_norm", w_norm, dt, Wt.shape[1])
+    _dev(fn, "Wt_folded", Wt_folded, dt, Wt.numel())
+    _on_gpu(fn, w_norm, Wt, Wt_folded)
     _keep(stream, w_norm, Wt, Wt_folded)
     _check(_lib.np_fold_norm_weight(_ptr(w_norm), _ptr(Wt), _ptr(Wt_folded), Wt.shape[0],
                                     Wt.shape[1], dtype_code(Wt), _stream(stream)),

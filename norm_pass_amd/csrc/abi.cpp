@@ -545,9 +545,17 @@ int unfused_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_
   if (rc) return rc;
   if (in_dt != out_dt) return fail(NP_EINVAL, "unfused_chain needs in_dt == out_dt");
   if (n == 0) return ok();
-  for (int j = 0; j < n_inputs; ++j)
-    if (inputs[j] == out && !(j == ops[0].arg))
-      return fail(NP_EINVAL, "out may alias only the first loaded input");
+  for (int j = 0; j < n_inputs; ++j) {
+    if (inputs[j] != out) continue;
+    // the first launch reads this input and overwrites it with its result, so
+    // it may alias out only if no later op reads it again
+    if (j != ops[0].arg) return fail(NP_EINVAL, "out may alias only the first loaded input");
+    for (int i = 1; i < n_ops; ++i)
+      if ((ops[i].kind == NP_LOAD || ops[i].kind == NP_ADD_IN || ops[i].kind == NP_MUL_IN) &&
+          ops[i].arg == j)
+        return fail(NP_EINVAL, "out aliases input %d, which op %d reads after the first launch",
+                    j, i);
+  }
   if ((rc = check_device())) return rc;
   const void* cur = inputs[ops[0].arg];
   hipError_t e = hipSuccess;

@@ -3,6 +3,8 @@
 // the hardware's default mode), and a wave64 sum built on DPP row rotations.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -130,5 +132,18 @@ __device__ __forceinline__ float chain_sigmoid(float v) {
 }
 template <bool FAST>
 __device__ __forceinline__ float chain_tanh(float v) { return FAST ? np_fast_tanh(v) : tanhf(v); }
+
+// Arithmetic of a RoPE rotation: fp32 for 16-bit data; fp64 for fp32 data,
+// where an fp32 cos / sin (each within about one ulp) and two rounded products
+// would put the rotated value u cos - w sin, when it cancels, further than
+// 1e-6 relative from its exact value. In fp64 the result is rounded once to
+// fp32. The angle itself stays the fp32 product fp32(pos) * inv_i.
+template <typename T>
+using rope_math_t = std::conditional_t<sizeof(T) == 4, double, float>;
+
+__device__ inline void rope_sincos(float theta, float* s, float* c) { sincosf(theta, s, c); }
+__device__ inline void rope_sincos(float theta, double* s, double* c) {
+  sincos((double)theta, s, c);
+}
 
 }  // namespace np

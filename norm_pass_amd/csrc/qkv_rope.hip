@@ -25,6 +25,7 @@
 #include "internal.h"
 
 namespace np {
+
 namespace {
 
 constexpr int kBlock = 256;
@@ -39,11 +40,12 @@ constexpr int kTokBlock = NP_ROPE_TOK_BLOCK;
 
 template <typename T, int NC>
 __global__ __launch_bounds__(kTokBlock) void rope_tok(RopeArgs a) {
+  using RT = rope_math_t<T>;
   constexpr int E = Vec<T>::N;  // elements per 16-byte chunk; D == 16 * E here
   constexpr int HALF = 8 * E;
   // cos / sin of the token's angles, plain (K) and multiplied by q_scale (Q)
   static_assert(HALF <= kTokBlock, "one angle per thread at most");
-  __shared__ float tab[4][HALF];
+  __shared__ RT tab[4][HALF];
   const int64_t t = blockIdx.x;
   // the angle inputs, then the row's loads, then the angle table: waits count
   // loads in issue order, so the table is computed while the row is in flight
@@ -59,12 +61,12 @@ __global__ __launch_bounds__(kTokBlock) void rope_tok(RopeArgs a) {
     raw[q] = load_raw(src + (c < total ? c : 0));
   }
   if (ia < HALF) {
-    float sv, cv;
-    sincosf(p * inv, &sv, &cv);  // theta = fp32(pos) * inv_i: one fp32 multiply
+    RT sv, cv;
+    rope_sincos(p * inv, &sv, &cv);  // theta = fp32(pos) * inv_i: one fp32 multiply
     tab[0][ia] = cv;
     tab[1][ia] = sv;
-    tab[2][ia] = cv * a.q_scale;
-    tab[3][ia] = sv * a.q_scale;
+    tab[2][ia] = cv * (RT)a.q_scale;
+    tab[3][ia] = sv * (RT)a.q_scale;
   }
   __syncthreads();
   const int l16 = threadIdx.x & 15;
@@ -89,12 +91,14 @@ __global__ __launch_bounds__(kTokBlock) void rope_tok(RopeArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) pr[e] = dpp_f<0x128>(x[e]);  // row_ror:8 -> partner half
     if (s < 2) {
-      const float* cs = tab[s == 0 ? 2 : 0] + f0;
-      const float* sn = tab[s == 0 ? 3 : 1] + f0;
+      const RT* cs = tab[s == 0 ? 2 : 0] + f0;
+      const RT* sn = tab[s == 0 ? 3 : 1] + f0;
       T e_out[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        e_out[e] = from_f<T>(second ? x[e] * cs[e] + pr[e] * sn[e] : x[e] * cs[e] - pr[e] * sn[e]);
+      for (int e = 0; e < E; ++e) {
+        const RT xe = x[e], pe = pr[e];
+        e_out[e] = from_f<T>((float)(second ? xe * cs[e] + pe * sn[e] : xe * cs[e] - pe * sn[e]));
+      }
       __builtin_memcpy(&res, e_out, 16);
     }
     if (c < total) {
@@ -128,14 +132,15 @@ __global__ __launch_bounds__(kBlock) void rope_vec(RopeArgs a) {
     }
     return;
   }
+  using RT = rope_math_t<T>;
   const float p = a.pos ? (float)a.pos[t] : (float)t;
-  float cs[E], sn[E];
+  RT cs[E], sn[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const float theta = p * a.inv[lo + e];  // one fp32 multiply
-    sincosf(theta, &sn[e], &cs[e]);
+    rope_sincos(theta, &sn[e], &cs[e]);
   }
-  const float sc = s == 0 ? a.q_scale : 1.0f;
+  const RT sc = s == 0 ? (RT)a.q_scale : (RT)1;
   int h = 0;
   for (; h + HU <= a.H; h += HU) {
     float u[HU][E], w[HU][E];
@@ -149,8 +154,9 @@ __global__ __launch_bounds__(kBlock) void rope_vec(RopeArgs a) {
       float o1[E], o2[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        o1[e] = (u[k][e] * cs[e] - w[k][e] * sn[e]) * sc;
-        o2[e] = (w[k][e] * cs[e] + u[k][e] * sn[e]) * sc;
+        const RT ue = u[k][e], we = w[k][e];
+        o1[e] = (float)((ue * cs[e] - we * sn[e]) * sc);
+        o2[e] = (float)((we * cs[e] + ue * sn[e]) * sc);
       }
       store_vec_nt<T>(dst + (h + k) * hstride + lo, o1);
       store_vec_nt<T>(dst + (h + k) * hstride + hi, o2);
@@ -162,8 +168,9 @@ __global__ __launch_bounds__(kBlock) void rope_vec(RopeArgs a) {
     load_vec<T>(src + (int64_t)h * a.D + hi, w);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      o1[e] = (u[e] * cs[e] - w[e] * sn[e]) * sc;
-      o2[e] = (w[e] * cs[e] + u[e] * sn[e]) * sc;
+      const RT ue = u[e], we = w[e];
+      o1[e] = (float)((ue * cs[e] - we * sn[e]) * sc);
+      o2[e] = (float)((we * cs[e] + ue * sn[e]) * sc);
     }
     store_vec_nt<T>(dst + h * hstride + lo, o1);
     store_vec_nt<T>(dst + h * hstride + hi, o2);
@@ -190,15 +197,16 @@ __global__ __launch_bounds__(kBlock) void rope_scalar(RopeArgs a) {
     dst[i + half] = src[i + half];
     return;
   }
+  using RT = rope_math_t<T>;
   const float p = a.pos ? (float)a.pos[t] : (float)t;
   const float theta = p * a.inv[i];
-  float sn, cs;
-  sincosf(theta, &sn, &cs);
-  const float sc = s == 0 ? a.q_scale : 1.0f;
-  const float u = to_f(src[i]);
-  const float w = to_f(src[i + half]);
-  dst[i] = from_f<T>((u * cs - w * sn) * sc);
-  dst[i + half] = from_f<T>((w * cs + u * sn) * sc);
+  RT sn, cs;
+  rope_sincos(theta, &sn, &cs);
+  const RT sc = s == 0 ? (RT)a.q_scale : (RT)1;
+  const RT u = to_f(src[i]);
+  const RT w = to_f(src[i + half]);
+  dst[i] = from_f<T>((float)((u * cs - w * sn) * sc));
+  dst[i + half] = from_f<T>((float)((w * cs + u * sn) * sc));
 }
 
 template <typename T, int NC>

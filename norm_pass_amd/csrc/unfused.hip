@@ -177,11 +177,13 @@ __global__ __launch_bounds__(kBlock) void rope_inplace_kernel(T* x, int64_t T_, 
   if (gid >= T_ * P) return;
   const int64_t t = gid / P;
   const int j = (int)(gid % P);
+  // fp64 rotation for fp32 data (rope_math_t): one rounding of the rotated value
+  using RT = rope_math_t<T>;
   const float p = pos ? (float)pos[t] : (float)t;
   constexpr int EM = Vec<T>::N;
-  float cs[E], sn[E];
+  RT cs[E], sn[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) sincosf(p * inv.inv[j * E + e], &sn[e], &cs[e]);
+  for (int e = 0; e < E; ++e) rope_sincos(p * inv.inv[j * E + e], &sn[e], &cs[e]);
   for (int h = 0; h < H; ++h) {
     T* row = x + ((int64_t)h * T_ + t) * D;
     if constexpr (VEC) {
@@ -191,16 +193,17 @@ __global__ __launch_bounds__(kBlock) void rope_inplace_kernel(T* x, int64_t T_, 
       float o1[EM], o2[EM];
 #pragma unroll
       for (int e = 0; e < EM; ++e) {
-        o1[e] = u[e] * cs[e] - w[e] * sn[e];
-        o2[e] = w[e] * cs[e] + u[e] * sn[e];
+        const RT ue = u[e], we = w[e];
+        o1[e] = (float)(ue * cs[e] - we * sn[e]);
+        o2[e] = (float)(we * cs[e] + ue * sn[e]);
       }
       store_vec_nt<T>(row + j * E, o1);
       store_vec_nt<T>(row + half + j * E, o2);
     } else {
-      const float u = to_f(row[j]);
-      const float w = to_f(row[half + j]);
-      row[j] = from_f<T>(u * cs[0] - w * sn[0]);
-      row[half + j] = from_f<T>(w * cs[0] + u * sn[0]);
+      const RT u = to_f(row[j]);
+      const RT w = to_f(row[half + j]);
+      row[j] = from_f<T>((float)(u * cs[0] - w * sn[0]));
+      row[half + j] = from_f<T>((float)(w * cs[0] + u * sn[0]));
     }
   }
 }

@@ -304,3 +304,71 @@ def test_zero_size_rejects_still_apply(npa):
     assert L.fuse_qkv_rope(*p, 0, 24, 7, NULL, 1e4, 0.125, 2, NULL) == -1
     assert L.fuse_add_layernorm(C.c_void_p(0x1000), NULL, NULL, NULL, NULL, out, 0, 8, 1e-5, 9,
                                 NULL) == -1
+
+
+def test_unfused_chain_rejects_alias_read_again(npa):
+    """out may alias the first loaded input only while no later op reads that
+    input again: the first launch has overwritten it by then."""
+    ops = (npa.np_op * 3)()
+    for i, (k, a, c) in enumerate([(synth.LOAD, 0, 0.0), (synth.MUL_C, 0, 2.0),
+                                   (synth.ADD_IN, 0, 0.0)]):
+        ops[i].kind, ops[i].arg, ops[i].c = k, a, c
+    buf = C.c_void_p(0x10000)
+    ins = (C.c_void_p * 1)(buf)
+    assert npa.lib().unfused_chain(ops, 3, ins, 1, 1, buf, 1, 64, NULL) == -1
+    assert "reads after the first launch" in _err(npa)
+
+
+# ---- the Python binding checks its tensors before any C call -------------
+
+import torch  # noqa: E402
+
+
+def _t(shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("case,msg", [
+    (lambda n: n._a_fuse_chain([(synth.LOAD, 0, 0.0)], [_t(8, torch.float16)], _t(8)),
+     "every tensor must be on a GPU"),
+    (lambda n: n._a_fuse_chain([(synth.LOAD, 0, 0.0), (synth.ADD_IN, 1, 0.0)],
+                               [_t(8), _t(8, torch.float16)], _t(8)), "expected torch.bfloat16"),
+    (lambda n: n._a_fuse_chain([(synth.LOAD, 0, 0.0)], [_t(7)], _t(8)), "has 7 elements"),
+    (lambda n: n._a_fuse_chain([(synth.LOAD, 0, 0.0)], [_t((4, 4)).t()], _t(16)),
+     "must be contiguous"),
+    (lambda n: n._a_fuse_chain([(synth.LOAD, 0, 0.0)], [_t(8)] * 5, _t(8)), "1..4 inputs"),
+    (lambda n: n._a_fuse_add_rmsnorm(_t((2, 3, 8)), _t((2, 3, 8)), _t(7), None, _t((2, 3, 8))),
+     "w has 7 elements, expected 8"),
+    (lambda n: n._a_fuse_add_rmsnorm(_t((2, 3, 8)), _t((2, 3, 8)), _t(8), _t((2, 8)),
+                                     _t((2, 3, 8))), "h_out has 16 elements, expected 48"),
+    (lambda n: n._a_fuse_add_layernorm(_t((4, 8)), None, _t(8), _t(8, torch.float16), None,
+                                       _t((4, 8))), "beta is torch.float16"),
+    (lambda n: n._a_fuse_qkv_rope(_t((4, 3 * 2 * 8)), _t((2, 4, 8)), _t((2, 4, 8)),
+                                  _t((2, 4, 8)), 2, 8, torch.arange(4)), "expected torch.int32"),
+    (lambda n: n._a_fuse_qkv_rope(_t((4, 3 * 2 * 8)), _t((2, 4, 8)), _t((2, 3, 8)),
+                                  _t((2, 4, 8)), 2, 8), "k has 48 elements, expected 64"),
+    (lambda n: n._a_fuse_qkv_rope(_t((4, 40)), _t((2, 4, 8)), _t((2, 4, 8)), _t((2, 4, 8)), 2,
+                                  8), "qkv has 160 elements, expected 192"),
+    (lambda n: n._a_fuse_rmsnorm_linear(_t((4, 64)), None, _t((32, 48)), None, _t((4, 32))),
+     "x must be [M, K] and Wt [N, K]"),
+    (lambda n: n._a_fuse_rmsnorm_linear(_t((4, 64)), None, _t((32, 64)), _t(31), _t((4, 32))),
+     "bias has 31 elements"),
+    (lambda n: n._a_fuse_det_decode([_t((1, 255, 4, 4), torch.float16)], [8.0],
+                                    [[(1, 1)] * 3], _t((1, 48, 84), torch.float32)),
+     "out has 4032 elements, expected 4080"),
+    (lambda n: n._a_fuse_det_decode([_t((1, 254, 4, 4), torch.float16)], [8.0],
+                                    [[(1, 1)] * 3], _t((1, 48, 85), torch.float32)),
+     "[batch, n_anchors * n_ch, H, W]"),
+    (lambda n: n._a_unfused_add_rmsnorm(_t((4, 8)), None, None, None, _t((4, 8)), None),
+     "a workspace tensor is required"),
+    (lambda n: n._a_fuse_transpose021(_t((2, 3, 4, 5)), _t(120)), "need GPU tensors"),
+])
+def test_binding_rejects_bad_tensors(npa, case, msg):
+    with pytest.raises(ValueError, match=re.escape(msg)):
+        case(npa)
+
+
+def test_binding_norm_rows_span_leading_axes(npa):
+    """A [B, T, C] tensor is B * T rows of C (every leading axis is a row)."""
+    assert npa._rows_cols("f", _t((2, 3, 8))) == (6, 8)
+    assert npa._rows_cols("f", _t(8)) == (1, 8)

@@ -64,10 +64,61 @@ def test_valu_count_only_for_current_sources():
         if row is None:
             assert bench.measured_valu_per_element(name) is None
         else:
-            assert row[1] == bench.file_hash(*bench.KERNEL_SOURCES[name])
+            assert row["source hash"] == bench.file_hash(*bench.KERNEL_SOURCES[name])
             assert lo < bench.measured_valu_per_element(name) < hi
 
 
 def test_gpus_above_one_exit_with_message(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_split_covers_every_index_once():
+    for n, p in ((10, 3), (5, 16), (2048, 16), (1, 1), (7, 7)):
+        r = bench._split(n, p)
+        assert r[0][0] == 0 and r[-1][1] == n and len(r) == min(n, p)
+        assert all(a[1] == b[0] for a, b in zip(r, r[1:]))
+        assert all(hi > lo for lo, hi in r)
+
+
+def test_oracle_samples_are_prefixes_of_the_workloads():
+    """The oracle leg draws each sample on its own; it must be the prefix of
+    the tensor the GPU ran (the generator keys chunks by index)."""
+    import numpy as np
+    full = synth.c5_inputs(3 * synth.CHUNK + 5)
+    assert np.array_equal(synth.c5_inputs(synth.CHUNK + 17), full[:synth.CHUNK + 17])
+    x16, r16, w16 = synth.c3_inputs(rows=2048, cols=64)
+    x2, r2, w2 = synth.c3_inputs(rows=100, cols=64)
+    assert np.array_equal(x2, x16[:100]) and np.array_equal(r2, r16[:100])
+    assert np.array_equal(w2, w16)
+
+
+def test_summarize_counters_splits_dispatches(tmp_path):
+    """A synthetic counter run: unrelated dispatches, the three calibration
+    copies, then the manifest's fused and unfused dispatches in order."""
+    import json
+    man = {"calibration_bytes": 1 << 30, "dispatches": [
+        {"workload": "c1", "fused": 2, "unfused": 2 * 3, "unfused_launches": 3,
+         "elements": 1 << 20, "bytes": 12 << 20, "unfused_bytes": 28 << 20}]}
+    mp = tmp_path / "m.json"
+    mp.write_text(json.dumps(man))
+    # KiB per dispatch: the copy reads half its bytes per the counter (factor 2)
+    vals = {"FETCH_SIZE": [7.0, 512 * 1024, 512 * 1024, 512 * 1024, 4096, 4096,
+                           1024, 1024, 2048, 1024, 1024, 2048],
+            "WRITE_SIZE": [7.0, 1 << 20, 1 << 20, 1 << 20, 4096, 4096,
+                           2048, 2048, 4096, 2048, 2048, 4096],
+            "SQ_INSTS_VALU": [1, 1, 1, 1, 16384, 16384, 1, 1, 1, 1, 1, 1]}
+    for c, vs in vals.items():
+        d = tmp_path / "run" / c
+        d.mkdir(parents=True)
+        lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        lines += [f"{i + 1},k{i},{c},{v}" for i, v in enumerate(vs)]
+        (d / "x_counter_collection.csv").write_text("\n".join(lines) + "\n")
+    table = bench.summarize_counters(str(mp), str(tmp_path / "run"))
+    rows = {r.split("|")[1].strip(): [c.strip() for c in r.strip().strip("|").split("|")]
+            for r in table.splitlines() if r.startswith("| c1")}
+    assert rows["c1"][2] == str(4096 * 1024 * 2) and rows["c1"][3] == str(4096 * 1024)
+    # unfused: per call (2 calls of 3 launches): fetch 2 * (1024 + 1024 + 2048) KiB x 2 / 2
+    assert rows["c1_unfused"][2] == str(4096 * 1024 * 2)
+    assert rows["c1_unfused"][3] == str(8192 * 1024)
+    assert float(rows["c1"][7]) == 16384 * 64 / (1 << 20)

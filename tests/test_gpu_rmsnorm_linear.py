@@ -1,15 +1,26 @@
 """GPU parity of fuse_rmsnorm_linear / unfused_rmsnorm_linear against the
 oracle (TeleTron write-up, section 4.2: RMSNorm + linear + scale in one
-kernel, the RMS factor applied to the linear layer's accumulation).
+kernel, the RMS factor applied to the linear layer's accumulation, the
+weighted input x * w held in fp32).
 
-Tolerance, from the arithmetic: the kernel forms the dt operand x*w exactly as
-the oracle does (an exact product rounded once), accumulates the K products in
-fp32 on the matrix cores in its own order, and applies rstd, bias and scale
-in fp32. Its fp32 value can differ from the exact one by at most
-2^-24 (K + 16) times the magnitude |scale| rstd sum|a W| of the terms, and the
-final rounding adds at most one ulp of the output type; every element must
-lie within that, and at least 99.5 % of the elements must equal the oracle's
-rounded value bit for bit.
+Tolerance, from the arithmetic. The oracle's operand is x * w unrounded. The
+matrix cores take dt operands, so the kernel rounds one operand to dt where a
+norm weight is involved: x * w when the weight is passed, w * Wt when it was
+folded into the linear weight (np_fold_norm_weight); without a norm weight
+both operands are the inputs themselves and nothing is rounded. The kernel
+then accumulates the K products in fp32 in its own order and applies rstd,
+bias and scale in fp32. Per element, with t_k = scale * rstd * a_k * Wt_nk:
+  - fp32 evaluation: at most 2^-24 (K + 16) * cond, cond = sum_k |t_k|;
+  - operand rounding: sum_k d_k t_k with independent |d_k| <= u (u = 2^-8 for
+    bf16, 2^-11 for fp16, the unit roundoff of dt). Hoeffding's inequality
+    bounds it by 7 u l2, l2 = sqrt(sum_k t_k^2), except with probability
+    2 exp(-24.5) < 1e-10 per element (the worst case u * cond is true but
+    about twenty times looser at K = 4096 and would let a dropped bias pass);
+  - the final rounding: one ulp of dt.
+Every element must lie within the sum. Elements beyond 2 ulp of the oracle's
+rounded value are counted and printed for each path; on the path that rounds
+no operand at least 99.5 % of the elements must equal the oracle's rounded
+value bit for bit.
 """
 import numpy as np
 import pytest
@@ -17,7 +28,7 @@ import torch
 
 import synth
 from gpu_util import ORACLE_DT, empty, need_gpu, to_dev, to_host
-from tolerance import bf16_bits_to_f32
+from tolerance import bf16_bits_to_f32, ordinal16
 
 pytestmark = pytest.mark.gpu
 
@@ -50,14 +61,34 @@ def _inputs(M, K, N, seed, dt):
     return x, w, Wt, b
 
 
-def _check(got, exact, cond, K, dt, min_equal=0.995, want_bits=None):
+UNIT_ROUNDOFF = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def _l2(x, w, Wt, scale, dt):
+    """|scale| rstd_m sqrt(sum_k (x_mk w_k Wt_nk)^2): the size of the terms for
+    the operand-rounding part of the tolerance."""
+    xv = _vals(x, dt)
+    wv = np.ones(xv.shape[1]) if w is None else _vals(w, dt)
+    Wv = _vals(Wt.reshape(-1), dt).reshape(Wt.shape)
+    rstd = 1.0 / np.sqrt((xv * xv).mean(axis=1, keepdims=True) + float(np.float32(1e-6)))
+    return abs(scale) * rstd * np.sqrt(((xv * wv) ** 2) @ (Wv ** 2).T)
+
+
+def _check(got, exact, cond, K, dt, want_bits=None, l2=None, what="", min_equal=0.995):
+    """l2 given: one operand was rounded to dt (the norm-weight paths)."""
     g = _vals(got, dt)
     err = np.abs(g - exact)
     lim = _ulp(exact, dt) + 2.0 ** -24 * (K + 16) * cond
+    if l2 is not None:
+        lim = lim + 7.0 * UNIT_ROUNDOFF[dt] * l2
     bad = err > lim
     assert not bad.any(), (int(bad.sum()), float((err - lim).max()))
     if want_bits is not None:
-        assert (got == want_bits).mean() >= min_equal, float((got == want_bits).mean())
+        d = np.abs(ordinal16(got) - ordinal16(want_bits))
+        print(f"[{what}] {dt}: {int((d > 2).sum())} of {d.size} elements beyond 2 ulp "
+              f"({(d > 2).mean():.4%}), {(d == 0).mean():.4%} bit-equal", flush=True)
+        if l2 is None:
+            assert (d == 0).mean() >= min_equal, float((d == 0).mean())
 
 
 CASES = [  # M, N, K (K a multiple of 64: the four-wave kernels; otherwise the eight-wave ones)
@@ -80,7 +111,8 @@ def test_fused_matches_oracle(npa, orc, M, N, K, dt, with_w, with_b, scale):
     npa.fuse_rmsnorm_linear(to_dev(x, dt), None if w is None else to_dev(w, dt), to_dev(Wt, dt),
                             None if b is None else to_dev(b, dt), out, 1e-6, scale)
     torch.cuda.synchronize()
-    _check(to_host(out), exact, cond, K, dt, want_bits=want)
+    _check(to_host(out), exact, cond, K, dt, want_bits=want,
+           l2=_l2(x, w, Wt, scale, dt) if with_w else None, what=f"fused {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 260, 520)])
@@ -117,7 +149,8 @@ def test_full_size_sampled_rows(npa, orc):
     want, exact, cond = orc.rmsnorm_linear(x[rows], w, Wt, b, 1e-6, synth.RMS_LINEAR_SCALE,
                                            ORACLE_DT["bf16"], want_exact=True)
     got = to_host(out[torch.from_numpy(rows).cuda()])
-    _check(got, exact, cond, K, "bf16", want_bits=want)
+    _check(got, exact, cond, K, "bf16", want_bits=want,
+           l2=_l2(x[rows], w, Wt, synth.RMS_LINEAR_SCALE, "bf16"), what="weight passed, full size")
 
 
 def _oracle_fold(orc, w, Wt, dt):
@@ -156,13 +189,30 @@ def test_direct_lds_path_matches_oracle(npa, orc, M, N, K, dt, with_b):
     npa.fuse_rmsnorm_linear(to_dev(x, dt), None, to_dev(Wt, dt),
                             None if b is None else to_dev(b, dt), out, 1e-6, 0.75)
     torch.cuda.synchronize()
-    _check(to_host(out), exact, cond, K, dt, want_bits=want)
+    _check(to_host(out), exact, cond, K, dt, want_bits=want, what=f"direct-to-LDS {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 512), (129, 130, 96)])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_folded_matches_oracle(npa, orc, M, N, K, dt):
+    """The norm weight folded into Wt (np_fold_norm_weight), then the
+    direct-to-LDS kernel, against the oracle given x, w and the unfolded Wt."""
+    x, w, Wt, b = _inputs(M, K, N, 6300 + M + N + K, dt)
+    want, exact, cond = orc.rmsnorm_linear(x, w, Wt, b, 1e-6, 0.5, ORACLE_DT[dt],
+                                           want_exact=True)
+    Wf = empty((N, K), dt)
+    npa.np_fold_norm_weight(to_dev(w, dt), to_dev(Wt, dt), Wf)
+    out = empty((M, N), dt)
+    npa.fuse_rmsnorm_linear(to_dev(x, dt), None, Wf, to_dev(b, dt), out, 1e-6, 0.5)
+    torch.cuda.synchronize()
+    _check(to_host(out), exact, cond, K, dt, want_bits=want, l2=_l2(x, w, Wt, 0.5, dt),
+           what=f"folded {M}x{N}x{K}")
 
 
 def test_folded_full_size_sampled_rows(npa, orc):
     """The bench's folded launch: the norm weight folded into Wt once, then the
     direct-to-LDS kernel on the 16384 x 4096 x 4096 workload; sampled rows
-    against the oracle with the oracle's own folded weight."""
+    against the oracle given x, w and the unfolded Wt."""
     M, K, N = synth.RMS_LINEAR_SHAPE
     x, w, Wt, b = synth.rmsnorm_linear_inputs()
     Wf = empty((N, K), "bf16")
@@ -171,14 +221,14 @@ def test_folded_full_size_sampled_rows(npa, orc):
     npa.fuse_rmsnorm_linear(to_dev(x, "bf16"), None, Wf, to_dev(b, "bf16"), out, 1e-6,
                             synth.RMS_LINEAR_SCALE)
     torch.cuda.synchronize()
-    Wf_o = _oracle_fold(orc, w, Wt, "bf16")
-    assert np.array_equal(to_host(Wf), Wf_o)
+    assert np.array_equal(to_host(Wf), _oracle_fold(orc, w, Wt, "bf16"))
     rng = np.random.default_rng(23)
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
-    want, exact, cond = orc.rmsnorm_linear(x[rows], None, Wf_o, b, 1e-6, synth.RMS_LINEAR_SCALE,
+    want, exact, cond = orc.rmsnorm_linear(x[rows], w, Wt, b, 1e-6, synth.RMS_LINEAR_SCALE,
                                            ORACLE_DT["bf16"], want_exact=True)
     got = to_host(out[torch.from_numpy(rows).cuda()])
-    _check(got, exact, cond, K, "bf16", want_bits=want)
+    _check(got, exact, cond, K, "bf16", want_bits=want,
+           l2=_l2(x[rows], w, Wt, synth.RMS_LINEAR_SCALE, "bf16"), what="folded, full size")
 
 
 def test_empty_and_rejects(npa):

@@ -14,7 +14,7 @@ import torch
 
 import synth
 from gpu_util import ORACLE_DT, empty, misaligned, need_gpu, to_dev, to_host
-from tolerance import check_half, half_values
+from tolerance import check_f32_counted, check_half, half_values
 
 pytestmark = pytest.mark.gpu
 QS = float(np.float32(1.0 / math.sqrt(128.0)))
@@ -46,9 +46,8 @@ def _check(npa, orc, qkv, H, D, dt, qs=QS, pos=None, fn="fuse", align=True):
                                               eager=(fn != "fuse"), want_bound=True)
     assert np.array_equal(gv.view(np.uint8), rv.view(np.uint8))
     if dt == "f32":
-        for g, e, b in ((gq, eq, bq), (gk, ek, bk)):
-            assert (np.abs(g.astype(np.float64) - e) <= 1e-6 * np.abs(e) + b).all()
-        return None
+        return tuple(check_f32_counted(g, r, e, b, what=f"{name} {qkv.shape} {fn}")
+                     for name, g, r, e, b in (("Q", gq, rq, eq, bq), ("K", gk, rk, ek, bk)))
     s1 = check_half(gq, rq, dt, half_values(gq, dt), eq, bq, what=f"Q {qkv.shape} {fn}")
     s2 = check_half(gk, rk, dt, half_values(gk, dt), ek, bk, what=f"K {qkv.shape} {fn}")
     return s1, s2
