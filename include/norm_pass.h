@@ -273,6 +273,24 @@ int unfused_det_decode(const void* const* level_logits, int n_levels, const int3
                        int n_anchors, int n_ch, int batch, np_dtype in_dt, float* out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * unfused_det_decode_noalloc: unfused_det_decode (same kernels, same results)
+ * for callers that cannot allocate device memory around a call -- code under
+ * HIP graph capture, serving loops that must not call the allocator,
+ * harnesses that forbid allocation. Instead of a caller workspace the call
+ * stages through a 16 MiB array that the library owns, one per GPU, held
+ * until the process ends; it calls no hipMalloc / hipFree. The staged bytes
+ * (2 * batch * sum_l n_anchors * H[l] * W[l] * n_ch * sizeof(in_dt); 8,568,000
+ * for one image of the 3-level 80/40/20 YOLO head) must fit in 16 MiB,
+ * else NP_EINVAL. Calls that overlap on one GPU (concurrent streams or host
+ * threads) share that array and race; calls on one stream are ordered.
+ * Errors otherwise as unfused_det_decode.
+ */
+int unfused_det_decode_noalloc(const void* const* level_logits, int n_levels, const int32_t* H,
+                               const int32_t* W, const float* strides, const float* anchors_wh,
+                               int n_anchors, int n_ch, int batch, np_dtype in_dt, float* out,
+                               hipStream_t stream);
+
 /* 6 launches: add; square; row mean; (+eps, 1/sqrt); times rstd; times w.
  * workspace: at least (rows * cols + 2 * rows) * sizeof(dt) bytes, plus
  * rows * cols * sizeof(dt) when h_out == NULL. w == NULL skips the last launch. */

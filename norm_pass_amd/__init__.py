@@ -60,6 +60,7 @@ def _load():
         "unfused_add_layernorm": [P, P, P, P, P, P, I64, I64, F, I, P, S, P],
         "unfused_chain": [OPS, I, P, I, I, P, I, I64, P],
         "unfused_det_decode": [P, I, P, P, P, P, I, I, I, I, P, P, S, P],
+        "unfused_det_decode_noalloc": [P, I, P, P, P, P, I, I, I, I, P, P],
         "unfused_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I, P, S, P],
         "unfused_qkv_rope": [P, P, P, P, I64, I, I, P, F, F, I, P],
         "np_empty_launches": [I, P],
@@ -415,6 +416,9 @@ def _a_unfused_det_decode(levels, strides, anchors, out, workspace, n_anchors: i
     return a[:-1] + (_ptr(workspace), workspace.numel() * workspace.element_size(), a[-1])
 
 
+_a_unfused_det_decode_noalloc = _a_fuse_det_decode
+
+
 def _a_unfused_add_rmsnorm(x, r, w, h_out, out, workspace, eps: float = 1e-6, stream=None):
     _workspace("unfused_add_rmsnorm", workspace)
     a = _a_fuse_add_rmsnorm(x, r, w, h_out, out, eps, stream)
@@ -593,6 +597,15 @@ def unfused_det_decode(levels, strides, anchors, out, workspace, n_anchors: int 
     _check(_lib.unfused_det_decode(*_a_unfused_det_decode(levels, strides, anchors, out,
                                                           workspace, n_anchors, n_ch, stream)),
            "unfused_det_decode")
+    return out
+
+
+def unfused_det_decode_noalloc(levels, strides, anchors, out, n_anchors: int = 3, n_ch: int = 85,
+                               stream=None):
+    """unfused_det_decode staged through the library's own 16 MiB device array
+    (no workspace argument, no allocation)."""
+    _check(_lib.unfused_det_decode_noalloc(*_a_unfused_det_decode_noalloc(
+        levels, strides, anchors, out, n_anchors, n_ch, stream)), "unfused_det_decode_noalloc")
     return out
 
 

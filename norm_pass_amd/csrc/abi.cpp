@@ -410,6 +410,20 @@ int shuffle_shape(int64_t N, int64_t C, int64_t H, int64_t W, int64_t groups, in
 
 }  // namespace
 
+namespace np {
+
+int validate_det_call(const void* const* lv, int n_levels, const int32_t* H, const int32_t* W,
+                      const float* strides, const float* anchors, int n_anchors, int n_ch,
+                      int batch, int in_dt, const float* out) {
+  return validate_det(lv, n_levels, H, W, strides, anchors, n_anchors, n_ch, batch, in_dt, out);
+}
+
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+int check_device_call() { return check_device(); }
+
+}  // namespace np
+
 extern "C" {
 
 int np_init(int device) {

@@ -139,6 +139,16 @@ hipError_t launch_tr_items(const void* in, void* out, const ItemArgs& a, int ite
                            bool nt, hipStream_t s);
 
 hipError_t launch_cast_to_f32(const void* in, float* out, int64_t n, int dt, hipStream_t s);
+
+// the argument checks of fuse_det_decode / unfused_det_decode (NP_OK, or
+// NP_EINVAL with the thread's error message set)
+int validate_det_call(const void* const* lv, int n_levels, const int32_t* H, const int32_t* W,
+                      const float* strides, const float* anchors, int n_anchors, int n_ch,
+                      int batch, int in_dt, const float* out);
+// set the thread's error message (np_last_error) and return code
+int set_error(int code, const char* msg);
+// the per-device gfx950 check every call makes before its first HIP call
+int check_device_call();
 hipError_t launch_empty(hipStream_t s);
 
 }  // namespace np
