@@ -241,6 +241,25 @@ def summarize_counters(manifest_path: str, run_dir: str) -> str:
     return "\n".join(lines)
 
 
+def summarize_kernel_trace(path: str, kernel: str) -> str:
+    """Count, mean, median, p10 and p90 of the dispatch durations (us) of the
+    kernels whose name starts with `kernel`, from a rocprofv3 kernel trace."""
+    import csv
+    import statistics as st
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+         if r["Kernel_Name"].startswith(kernel)]
+    if not d:
+        return f"no dispatch of {kernel}"
+    q = sorted(d)
+    pct = lambda p: q[min(len(q) - 1, int(p * len(q)))]
+    out = [f"| kernel | dispatches | mean us | median us | p10 us | p90 us |",
+           "|---|---|---|---|---|---|",
+           f"| {kernel} | {len(d)} | {st.mean(d):.2f} | {st.median(d):.2f} | {pct(0.1):.2f} | "
+           f"{pct(0.9):.2f} |"]
+    return "\n".join(out)
+
+
 def summarize_graph_trace(path: str, launches: int) -> str:
     """Kernel durations, gaps between the kernels of one call and gaps between
     calls, from a kernel trace of --graph-trace (its last 300 calls' worth of
@@ -308,10 +327,14 @@ def graph_time(torch, npa, spec, copies: int, trials: int):
         call = npa.bind(name, *args)
         for _ in range(copies):
             call()
-    many, _, _ = time_calls(torch, gm.replay, 1, trials)
+    for _ in range(3):
+        gm.replay()
+    many, _, _ = time_calls(torch, gm.replay, 5, trials)
     g1 = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g1):
         npa.bind(name, *args)()
+    for _ in range(3):
+        g1.replay()
     one, _, _ = time_calls(torch, g1.replay, max(3, copies), trials)
     torch.cuda.synchronize()
     return many / copies, one
@@ -940,12 +963,18 @@ def main(argv=None):
                          "graph holding 50 calls")
     ap.add_argument("--summarize-graph-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "LAUNCHES"),
                     help="print kernel durations and gaps of a --graph-trace kernel trace")
+    ap.add_argument("--summarize-kernel-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "KERNEL"),
+                    help="print the dispatch durations of the kernels whose name starts with "
+                         "KERNEL in a rocprofv3 kernel trace, and per-kernel totals")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("MANIFEST", "RUN_DIR"),
                     help="print the counter table from rocprofv3 --pmc runs: RUN_DIR holds "
                          "one sub-directory per counter (FETCH_SIZE, WRITE_SIZE, SQ_INSTS_VALU)")
     args = ap.parse_args(argv)
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters))
+        return 0
+    if args.summarize_kernel_trace:
+        print(summarize_kernel_trace(*args.summarize_kernel_trace))
         return 0
     if args.summarize_graph_trace:
         print(summarize_graph_trace(args.summarize_graph_trace[0],
@@ -1016,11 +1045,9 @@ def main(argv=None):
         return 0
 
     if args.graph_trace:
+        # graphs first (their capture runs one call each), then the traced
+        # sequence: 100 eager calls, 100 one-call replays, 2 x 50-call replays
         name, a_ = W[args.graph_trace]["unfused_spec"]
-        eager = npa.bind(name, *a_)
-        for _ in range(100):
-            eager()
-        torch.cuda.synchronize()
         graphs = []
         for copies in (1, 50):
             s_ = torch.cuda.Stream()
@@ -1034,6 +1061,10 @@ def main(argv=None):
                 for _ in range(copies):
                     c_()
             graphs.append(g_)
+        torch.cuda.synchronize()
+        eager = npa.bind(name, *a_)
+        for _ in range(100):
+            eager()
         torch.cuda.synchronize()
         for _ in range(100):
             graphs[0].replay()
@@ -1129,10 +1160,6 @@ def main(argv=None):
         f_med, f_p10, f_p90 = time_calls(torch, w["fused"], reps, args.trials)
         reps_u = pick_reps(torch, w["unfused"])
         u_med, _, _ = time_calls(torch, w["unfused"], reps_u, max(5, args.trials // 2))
-        # the same unfused launches captured in a HIP graph and replayed:
-        # launch cost removed, every intermediate HBM round trip kept
-        g_med, g_one = graph_time(torch, npa, w["unfused_spec"], reps_u,
-                                  max(5, args.trials // 2))
         gbps = w["bytes"] / f_med / 1e9
         cold = None
         if "cold" in w:
@@ -1153,8 +1180,7 @@ def main(argv=None):
             "unfused": {"launches": w["launches"], "us_med": round(u_med * 1e6, 3),
                         "GBps": round(w["unfused_bytes"] / u_med / 1e9, 1),
                         "bytes": w["unfused_bytes"],
-                        "graph_us_med": round(g_med * 1e6, 3),
-                        "graph_one_call_per_replay_us_med": round(g_one * 1e6, 3)},
+                        "reps": reps_u},
             "speedup": round(u_med / f_med, 2),
         }
         if cold:
@@ -1192,9 +1218,20 @@ def main(argv=None):
             if "torch_us_med" in per[k]:
                 per[k]["torch_TFLOPs"] = round(w["flops"] / (per[k]["torch_us_med"] * 1e-6) / 1e12, 1)
         log(f"[bench] {k}: fused {f_med * 1e6:.2f} us ({gbps:.0f} GB/s), "
-            f"unfused {u_med * 1e6:.2f} us x{w['launches']} launches "
-            f"(graph {g_med * 1e6:.2f} us)"
+            f"unfused {u_med * 1e6:.2f} us x{w['launches']} launches"
             + (f", cold {cold['us_med']:.2f} us ({cold['GBps']:.0f} GB/s)" if cold else ""))
+
+    # the same unfused launches captured in a HIP graph and replayed (launch
+    # cost removed, every intermediate HBM round trip kept), in a pass of
+    # their own after the eager timings
+    for k in order + extra:
+        w = W[k]
+        g_med, g_one = graph_time(torch, npa, w["unfused_spec"], per[k]["unfused"].pop("reps"),
+                                  max(5, args.trials // 2))
+        per[k]["unfused"]["graph_us_med"] = round(g_med * 1e6, 3)
+        per[k]["unfused"]["graph_one_call_per_replay_us_med"] = round(g_one * 1e6, 3)
+        log(f"[bench] {k}: unfused launches replayed as a graph {g_med * 1e6:.2f} us per call "
+            f"({g_one * 1e6:.2f} us with one call per replay)")
 
     # achievable streaming ceiling: a plain 16-byte-per-lane copy of 1 GiB
     n_copy = 1 << 28

@@ -51,7 +51,10 @@ extern "C" {
 
 #define NP_VERSION 1
 
-/* status codes */
+/* Status codes. The runtime page's host function (section 4.3) returns 0 on
+ * success and -1 when the launch reports an error (it checks the last runtime
+ * error after the launch and never synchronises the device); these codes keep
+ * 0 and -1 and split the other failures by cause. */
 #define NP_OK 0
 #define NP_EINVAL (-1)   /* invalid argument (nothing was launched) */
 #define NP_ELAUNCH (-3)  /* a HIP call or kernel launch failed */
@@ -88,15 +91,23 @@ typedef struct {
 
 /* ---------------------------------------------------------------- helpers */
 
-/* Check that `device` is a gfx950 GPU and make the library ready on it.
- * Optional: the first call on a device does it lazily. Returns NP_EDEVICE if
- * the device is missing or not gfx950. */
+/* Make `device` current through its primary context and check that it is a
+ * gfx950 GPU (DeepJIT write-up, section 3.2: before loading runtime-compiled
+ * modules, retain the device's primary context and make it current, so the
+ * library shares the framework's context instead of creating its own; in HIP
+ * hipSetDevice does both). Optional: the first call on a device does the check
+ * lazily. Returns NP_EDEVICE if the device is missing or not gfx950. */
 int np_init(int device);
 
-/* Message for the last failing call on this thread ("" if none). The pointer
+/* Message for the last failing call on this thread ("" if none): the text the
+ * runtime page's host function prints with the runtime's error string
+ * (section 4.3), kept per thread for the caller to read instead. The pointer
  * stays valid until the next call on this thread. */
 const char* np_last_error(void);
 
+/* NP_VERSION of the built library, for a caller to check the ABI it was
+ * compiled against at run time (the runtime page, section 4.4: the host
+ * runtime's version decides what an operator library must provide). */
 int np_version(void);
 
 /* Release runtime-compiled modules. Every stream that ran a specialised chain
@@ -195,7 +206,9 @@ int64_t np_set_chain_table_min(int64_t n);
  *   out[2] = exp(t2) * anchor_w           out[3] = exp(t3) * anchor_h
  *   out[k] = sigmoid(t_k) for k >= 4.
  * Limits: 1 <= n_levels <= 8, 1 <= n_anchors <= 16, 5 <= n_ch <= 1024,
- * H[l] * W[l] <= 2^22 cells per level.
+ * H[l] * W[l] <= 2^22 cells per level, and fewer than 2^23 tiles of 24 cells
+ * (n_ch <= 256; 8 cells beyond) over all images, anchors and levels: one
+ * 256-thread workgroup per tile in a single launch.
  * Errors: NP_EINVAL on NULL pointers or out-of-range sizes.
  */
 int fuse_det_decode(const void* const* level_logits, int n_levels, const int32_t* H,
@@ -251,12 +264,20 @@ int fuse_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n_h
                   int head_dim, const int32_t* positions, float base, float q_scale,
                   np_dtype dt, hipStream_t stream);
 
+/* Launch size. A dispatch grid counts at most 2^32 work-items, so the fused
+ * calls split a long input into several launches on the same stream: the
+ * chain every 2^30 elements, the norms every 2^22 rows, QKV + RoPE every
+ * 2^21 tokens (fewer for very wide rows). The results do not depend on it. */
+
 /* ------------------------------------------ unfused (N-launch) baselines */
 /* The same chains as one kernel per operator, each kernel reading its operands
  * from HBM and storing its result in the storage type before the next launch
  * (NaiveRT write-up: K calls of cost L + T_k each; DeepJIT write-up, section
  * 1.1: every small kernel reads and writes the whole tensor). Results follow
- * the unfused definitions: rounding after every operator. */
+ * the unfused definitions: rounding after every operator. Each runs one
+ * thread per element in one launch per operator, so a call takes fewer than
+ * 2^31 elements (and the norms fewer than 2^23 rows); larger calls return
+ * NP_EINVAL. */
 
 /* One launch per op after the initial NP_LOAD (a lone load is one copy
  * launch), in place in `out`. Requires in_dt == out_dt (the storage type). */

@@ -41,6 +41,16 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 bool valid_dt(int dt) { return dt == NP_F32 || dt == NP_F16 || dt == NP_BF16; }
+
+// A dispatch grid counts at most 2^32 work-items. The fused calls split long
+// inputs into launches of at most these many elements or rows (each a
+// multiple of 16 elements, so a 16-byte aligned buffer stays aligned at every
+// launch's start); the unfused baselines, one thread per element, take at most
+// kUnfusedMax elements per call.
+constexpr int64_t kChainChunk = (int64_t)1 << 30;  // elements per chain launch
+constexpr int64_t kRowChunk = (int64_t)1 << 22;    // rows per norm launch (<= 512 threads each)
+constexpr int64_t kUnfusedMax = (int64_t)1 << 31;
+constexpr int64_t kUnfusedRowMax = (int64_t)1 << 23;  // rows of 256-thread row reductions
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Per-device gfx950 check, done once per device and cached.
@@ -189,7 +199,10 @@ int fill_det_args(np::DetArgs& a, const void* const* lv, int n_levels, const int
     row += n_anchors * hw;
     a.tiles[l] = (int32_t)((hw + tp - 1) / tp);
     tiles_total += (int64_t)batch * n_anchors * a.tiles[l];
-    if (tiles_total >= ((int64_t)1 << 31)) return fail(NP_EINVAL, "too many tiles");
+    // one 256-thread workgroup per tile: fewer than 2^31 work-items per launch
+    if (tiles_total >= ((int64_t)1 << 23))
+      return fail(NP_EINVAL, "output too large for one launch (%lld tiles of %d cells, limit 2^23)",
+                  (long long)tiles_total, tp);
     a.tile_start[l + 1] = (int32_t)tiles_total;
   }
   a.total_rows = row;
@@ -451,14 +464,21 @@ int fuse_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_inp
   if ((rc = check_device())) return rc;
   bool vec = aligned16(out);
   for (int j = 0; j < n_inputs; ++j) vec = vec && aligned16(inputs[j]);
-  np::ChainArgs a = chain_args(ops, n_ops, inputs, n_inputs, out, n);
-  hipError_t e;
-  if (vec && np::rtc_launch(a, n_inputs, in_dt, out_dt, stream, &e)) {
-    if (e != hipSuccess) return hip_fail(e, "fuse_chain (specialised)");
-    return ok();
+  const np::ChainArgs all = chain_args(ops, n_ops, inputs, n_inputs, out, n);
+  for (int64_t base = 0; base < n; base += kChainChunk) {
+    np::ChainArgs a = all;
+    a.n = std::min(kChainChunk, n - base);
+    for (int j = 0; j < n_inputs; ++j)
+      a.in[j] = static_cast<const char*>(inputs[j]) + base * np::dt_size(in_dt);
+    a.out = static_cast<char*>(out) + base * np::dt_size(out_dt);
+    hipError_t e;
+    if (vec && np::rtc_launch(a, n_inputs, in_dt, out_dt, stream, &e)) {
+      if (e != hipSuccess) return hip_fail(e, "fuse_chain (specialised)");
+      continue;
+    }
+    e = np::launch_chain(a, in_dt, out_dt, n_inputs, vec, stream);
+    if (e != hipSuccess) return hip_fail(e, "fuse_chain");
   }
-  e = np::launch_chain(a, in_dt, out_dt, n_inputs, vec, stream);
-  if (e != hipSuccess) return hip_fail(e, "fuse_chain");
   return ok();
 }
 
@@ -508,8 +528,16 @@ int fuse_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out, v
   if ((rc = check_device())) return rc;
   const bool vec = aligned16(x) && aligned16(out) && (!r || aligned16(r)) &&
                    (!w || aligned16(w)) && (!h_out || aligned16(h_out));
-  hipError_t e = np::launch_add_rmsnorm(x, r, w, h_out, out, rows, cols, eps, dt, vec, stream);
-  if (e != hipSuccess) return hip_fail(e, "fuse_add_rmsnorm");
+  const int64_t es = np::dt_size(dt);
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowChunk) {
+    const int64_t off = r0 * cols * es;
+    auto at = [&](const void* p) { return p ? static_cast<const char*>(p) + off : nullptr; };
+    hipError_t e = np::launch_add_rmsnorm(at(x), at(r), w, const_cast<char*>(at(h_out)),
+                                          const_cast<char*>(at(out)),
+                                          std::min(kRowChunk, rows - r0), cols, eps, dt, vec,
+                                          stream);
+    if (e != hipSuccess) return hip_fail(e, "fuse_add_rmsnorm");
+  }
   return ok();
 }
 
@@ -523,9 +551,17 @@ int fuse_add_layernorm(const void* x, const void* r, const void* gamma, const vo
   const bool vec = aligned16(x) && aligned16(out) && (!r || aligned16(r)) &&
                    (!gamma || aligned16(gamma)) && (!beta || aligned16(beta)) &&
                    (!h_out || aligned16(h_out));
-  hipError_t e =
-      np::launch_add_layernorm(x, r, gamma, beta, h_out, out, rows, cols, eps, dt, vec, stream);
-  if (e != hipSuccess) return hip_fail(e, "fuse_add_layernorm");
+  const int64_t es = np::dt_size(dt);
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowChunk) {
+    const int64_t off = r0 * cols * es;
+    auto at = [&](const void* p) { return p ? static_cast<const char*>(p) + off : nullptr; };
+    hipError_t e = np::launch_add_layernorm(at(x), at(r), gamma, beta,
+                                            const_cast<char*>(at(h_out)),
+                                            const_cast<char*>(at(out)),
+                                            std::min(kRowChunk, rows - r0), cols, eps, dt, vec,
+                                            stream);
+    if (e != hipSuccess) return hip_fail(e, "fuse_add_layernorm");
+  }
   return ok();
 }
 
@@ -543,6 +579,8 @@ int fuse_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int n_h
   a.v = v;
   a.pos = positions;
   a.T = T;
+  a.t0 = 0;
+  a.t_end = T;
   a.H = n_heads;
   a.D = head_dim;
   a.q_scale = q_scale;
@@ -558,6 +596,9 @@ int unfused_chain(const np_op* ops, int n_ops, const void* const* inputs, int n_
   int rc = validate_chain(ops, n_ops, inputs, n_inputs, in_dt, out, out_dt, n);
   if (rc) return rc;
   if (in_dt != out_dt) return fail(NP_EINVAL, "unfused_chain needs in_dt == out_dt");
+  if (n >= kUnfusedMax)
+    return fail(NP_EINVAL, "n = %lld: the unfused baseline takes fewer than 2^31 elements",
+                (long long)n);
   if (n == 0) return ok();
   for (int j = 0; j < n_inputs; ++j) {
     if (inputs[j] != out) continue;
@@ -599,6 +640,8 @@ int unfused_det_decode(const void* const* level_logits, int n_levels, const int3
   int64_t rows = 0;
   for (int l = 0; l < n_levels; ++l) rows += (int64_t)n_anchors * H[l] * W[l];
   const int64_t es = np::dt_size(in_dt);
+  if ((int64_t)batch * rows * n_ch >= kUnfusedMax)
+    return fail(NP_EINVAL, "the unfused baseline takes fewer than 2^31 output elements");
   const int64_t need = 2 * (int64_t)batch * rows * n_ch * es;
   if (!workspace || (int64_t)workspace_bytes < need)
     return fail(NP_EINVAL, "workspace needs %lld bytes", (long long)need);
@@ -638,6 +681,8 @@ int unfused_add_rmsnorm(const void* x, const void* r, const void* w, void* h_out
   if (rc) return rc;
   const int64_t es = np::dt_size(dt);
   const int64_t need = (rows * cols + 2 * rows + (h_out ? 0 : rows * cols)) * es;
+  if (rows * cols >= kUnfusedMax || rows >= kUnfusedRowMax)
+    return fail(NP_EINVAL, "the unfused baseline takes fewer than 2^31 elements and 2^23 rows");
   if (rows == 0) return ok();
   if (!workspace || (int64_t)workspace_bytes < need)
     return fail(NP_EINVAL, "workspace needs %lld bytes", (long long)need);
@@ -667,6 +712,8 @@ int unfused_add_layernorm(const void* x, const void* r, const void* gamma, const
   if (rc) return rc;
   const int64_t es = np::dt_size(dt);
   const int64_t need = (rows * cols + 3 * rows + (h_out ? 0 : rows * cols)) * es;
+  if (rows * cols >= kUnfusedMax || rows >= kUnfusedRowMax)
+    return fail(NP_EINVAL, "the unfused baseline takes fewer than 2^31 elements and 2^23 rows");
   if (rows == 0) return ok();
   if (!workspace || (int64_t)workspace_bytes < need)
     return fail(NP_EINVAL, "workspace needs %lld bytes", (long long)need);
@@ -699,6 +746,8 @@ int unfused_qkv_rope(const void* qkv, void* q, void* k, void* v, int64_t T, int 
                      np_dtype dt, hipStream_t stream) {
   int rc = validate_rope(qkv, q, k, v, T, n_heads, head_dim, base, q_scale, dt);
   if (rc) return rc;
+  if (T * 3 * n_heads * head_dim >= kUnfusedMax)
+    return fail(NP_EINVAL, "the unfused baseline takes fewer than 2^31 elements");
   if (T == 0) return ok();
   if ((rc = check_device())) return rc;
   float inv[256];
@@ -768,6 +817,8 @@ int unfused_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, co
                            hipStream_t stream) {
   int rc = validate_rms_linear(x, w_norm, Wt, bias, out, M, N, K, eps, scale, dt);
   if (rc) return rc;
+  if (M * std::max(K, N) >= kUnfusedMax || M >= kUnfusedRowMax)
+    return fail(NP_EINVAL, "the unfused baseline takes fewer than 2^31 elements and 2^23 rows");
   if (M == 0) return ok();
   const uint64_t need = (uint64_t)M * K * 2;
   if (!workspace || workspace_bytes < need || !aligned16(workspace))

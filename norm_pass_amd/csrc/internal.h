@@ -67,7 +67,8 @@ struct RopeArgs {
   void* k;
   void* v;
   const int32_t* pos;
-  int64_t T;
+  int64_t T;           // tokens of the whole call (the head stride of q, k, v)
+  int64_t t0, t_end;   // the tokens [t0, t_end) this launch covers
   int32_t H, D;
   float q_scale;
   float inv[256];

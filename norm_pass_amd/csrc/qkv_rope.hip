@@ -21,6 +21,8 @@
 // all 48 rotated head vectors. Blocks are (token tile) x (q, k, v); V blocks
 // are plain 16-byte copies into the head-major layout. Reads and writes are
 // full 128-byte lines: 8 lanes cover one 256-byte head vector.
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(kTokBlock) void rope_tok(RopeArgs a) {
   // cos / sin of the token's angles, plain (K) and multiplied by q_scale (Q)
   static_assert(HALF <= kTokBlock, "one angle per thread at most");
   __shared__ RT tab[4][HALF];
-  const int64_t t = blockIdx.x;
+  const int64_t t = a.t0 + blockIdx.x;
   // the angle inputs, then the row's loads, then the angle table: waits count
   // loads in issue order, so the table is computed while the row is in flight
   const int ia = threadIdx.x;  // this thread's angle, if any
@@ -115,9 +117,9 @@ __global__ __launch_bounds__(kBlock) void rope_vec(RopeArgs a) {
   const int P = half / E;            // chunks per half head vector (divides kBlock)
   const int TB = kBlock / P;         // tokens per block
   const int j = threadIdx.x % P;
-  const int64_t t = (int64_t)blockIdx.x * TB + threadIdx.x / P;
+  const int64_t t = a.t0 + (int64_t)blockIdx.x * TB + threadIdx.x / P;
   const int s = blockIdx.y;          // 0 = q, 1 = k, 2 = v
-  if (t >= a.T) return;
+  if (t >= a.t_end) return;
   const T* src = static_cast<const T*>(a.qkv) + (t * 3 + s) * (int64_t)a.H * a.D;
   T* dst = static_cast<T*>(s == 0 ? a.q : s == 1 ? a.k : a.v) + t * a.D;
   const int64_t hstride = a.T * a.D;  // distance between heads in the output
@@ -182,14 +184,14 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void rope_scalar(RopeArgs a) {
   const int half = a.D / 2;
   const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  const int64_t total = a.T * 3 * a.H * half;
+  const int64_t total = (a.t_end - a.t0) * 3 * a.H * half;
   if (gid >= total) return;
   const int i = (int)(gid % half);
   int64_t rest = gid / half;
   const int h = (int)(rest % a.H);
   rest /= a.H;
   const int s = (int)(rest % 3);
-  const int64_t t = rest / 3;
+  const int64_t t = a.t0 + rest / 3;
   const T* src = static_cast<const T*>(a.qkv) + ((t * 3 + s) * a.H + h) * (int64_t)a.D;
   T* dst = static_cast<T*>(s == 0 ? a.q : s == 1 ? a.k : a.v) + ((int64_t)h * a.T + t) * a.D;
   if (s == 2) {
@@ -211,36 +213,55 @@ __global__ __launch_bounds__(kBlock) void rope_scalar(RopeArgs a) {
 
 template <typename T, int NC>
 void launch_tok(const RopeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rope_tok<T, NC>), dim3((unsigned)a.T), dim3(kTokBlock), 0, s, a);
+  hipLaunchKernelGGL((rope_tok<T, NC>), dim3((unsigned)(a.t_end - a.t0)), dim3(kTokBlock), 0, s,
+                     a);
 }
 
+// A dispatch grid counts at most 2^32 work-items, so long calls are split into
+// launches over token ranges [t0, t_end) (the kernels index q, k, v with the
+// whole call's T). Token launches: 2^21 tokens x 768 threads < 2^31 items.
+constexpr int64_t kTokChunk = (int64_t)1 << 21;
+constexpr int64_t kMaxItems = (int64_t)1 << 31;
+
 template <typename T>
-hipError_t launch_t(const RopeArgs& a, bool vec, hipStream_t s) {
+hipError_t launch_t(const RopeArgs& a0, bool vec, hipStream_t s) {
   constexpr int E = Vec<T>::N;
-  const int half = a.D / 2;
+  const int half = a0.D / 2;
   const int P = half / E;
-  const int nc = (3 * a.H * 16 + kTokBlock - 1) / kTokBlock;
-  if (vec && a.D == 16 * E && nc <= 8) {
-    switch (nc) {
-      case 1: launch_tok<T, 1>(a, s); break;
-      case 2: launch_tok<T, 2>(a, s); break;
-      case 3: launch_tok<T, 3>(a, s); break;
-      case 4: launch_tok<T, 4>(a, s); break;
-      case 5: launch_tok<T, 5>(a, s); break;
-      case 6: launch_tok<T, 6>(a, s); break;
-      case 7: launch_tok<T, 7>(a, s); break;
-      default: launch_tok<T, 8>(a, s); break;
+  const int nc = (3 * a0.H * 16 + kTokBlock - 1) / kTokBlock;
+  const int path = (vec && a0.D == 16 * E && nc <= 8) ? 0
+                   : (vec && half % E == 0 && P > 0 && kBlock % P == 0) ? 1 : 2;
+  // scalar path: one thread per (token, q/k/v, head, pair)
+  const int64_t chunk = path < 2 ? kTokChunk
+                                 : std::max<int64_t>(1, kMaxItems / (3 * (int64_t)a0.H * half));
+  for (int64_t t0 = 0; t0 < a0.T; t0 += chunk) {
+    RopeArgs a = a0;
+    a.t0 = t0;
+    a.t_end = std::min(a0.T, t0 + chunk);
+    if (path == 0) {
+      switch (nc) {
+        case 1: launch_tok<T, 1>(a, s); break;
+        case 2: launch_tok<T, 2>(a, s); break;
+        case 3: launch_tok<T, 3>(a, s); break;
+        case 4: launch_tok<T, 4>(a, s); break;
+        case 5: launch_tok<T, 5>(a, s); break;
+        case 6: launch_tok<T, 6>(a, s); break;
+        case 7: launch_tok<T, 7>(a, s); break;
+        default: launch_tok<T, 8>(a, s); break;
+      }
+    } else if (path == 1) {
+      const int TB = kBlock / P;
+      const unsigned gx = (unsigned)((a.t_end - a.t0 + TB - 1) / TB);
+      hipLaunchKernelGGL((rope_vec<T, 4>), dim3(gx, 3), dim3(kBlock), 0, s, a);
+    } else {
+      const int64_t total = (a.t_end - a.t0) * 3 * a.H * (int64_t)half;
+      hipLaunchKernelGGL((rope_scalar<T>), dim3((unsigned)((total + kBlock - 1) / kBlock)),
+                         dim3(kBlock), 0, s, a);
     }
-  } else if (vec && half % E == 0 && P > 0 && kBlock % P == 0) {
-    const int TB = kBlock / P;
-    const unsigned gx = (unsigned)((a.T + TB - 1) / TB);
-    hipLaunchKernelGGL((rope_vec<T, 4>), dim3(gx, 3), dim3(kBlock), 0, s, a);
-  } else {
-    const int64_t total = a.T * 3 * a.H * (int64_t)half;
-    hipLaunchKernelGGL((rope_scalar<T>), dim3((unsigned)((total + kBlock - 1) / kBlock)),
-                       dim3(kBlock), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace

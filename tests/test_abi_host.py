@@ -372,3 +372,34 @@ def test_binding_norm_rows_span_leading_axes(npa):
     """A [B, T, C] tensor is B * T rows of C (every leading axis is a row)."""
     assert npa._rows_cols("f", _t((2, 3, 8))) == (6, 8)
     assert npa._rows_cols("f", _t(8)) == (1, 8)
+
+
+def test_unfused_baselines_reject_oversized_calls(npa):
+    """One thread per element: the unfused baselines take fewer than 2^31
+    elements (and row reductions fewer than 2^23 rows) per call; nothing is
+    launched then."""
+    ops = (npa.np_op * 2)()
+    ops[0].kind, ops[1].kind = synth.LOAD, synth.RELU
+    buf = (C.c_void_p * 1)(C.c_void_p(0x10000))
+    assert npa.lib().unfused_chain(ops, 2, buf, 1, 1, C.c_void_p(0x20000), 1, 1 << 31, NULL) == -1
+    assert "2^31" in _err(npa)
+    p = [C.c_void_p(0x1000 * (i + 1)) for i in range(6)]
+    assert npa.lib().unfused_add_rmsnorm(p[0], NULL, NULL, p[1], p[2], 1 << 23, 1, 1e-6, 2,
+                                         p[3], 1 << 40, NULL) == -1
+    assert "2^23 rows" in _err(npa)
+    assert npa.lib().unfused_qkv_rope(p[0], p[1], p[2], p[3], 1 << 22, 24, 128, NULL, 1e4, 0.5,
+                                      2, NULL) == -1
+    assert "2^31" in _err(npa)
+
+
+def test_det_decode_rejects_more_tiles_than_one_launch(npa):
+    """One 256-thread workgroup per 24-cell tile: at most 2^23 tiles."""
+    lv = (C.c_void_p * 1)(C.c_void_p(0x10000))
+    H = (C.c_int32 * 1)(2048)
+    W = (C.c_int32 * 1)(2048)
+    st = (C.c_float * 1)(8.0)
+    an = (C.c_float * 2)(10.0, 13.0)
+    # 2048 x 2048 cells = 174,763 tiles per (image, anchor); 48 images: 8.4e6 tiles
+    assert npa.lib().fuse_det_decode(lv, 1, H, W, st, an, 1, 85, 48, 1, C.c_void_p(0x20000),
+                                     NULL) == -1
+    assert "tiles" in _err(npa)

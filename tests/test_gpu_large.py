@@ -9,8 +9,15 @@ room to spare (4-5 GB per tensor).
 - QKV split + RoPE + scale with 2^18 + 5 tokens (2.4 * 10^9 input elements),
   sampled tokens against the oracle at their positions.
 
+A dispatch grid counts at most 2^32 work-items, so the library splits long
+calls into several launches: the chain every 2^30 elements (the chain test
+above crosses two such boundaries), the norms every 2^22 rows and QKV + RoPE
+every 2^21 tokens. The boundary tests below run just past one such launch
+and check the rows or tokens on both sides of it.
+
 Inputs are drawn on the device (gpu_util.gpu_normal). Samples always include
-both ends and the elements, rows or tokens around index 2^31.
+both ends and the elements, rows or tokens around index 2^31 or the launch
+boundary.
 """
 import math
 
@@ -114,3 +121,52 @@ def test_qkv_rope_past_2_31_elements(npa, orc):
     assert np.array_equal(gv.view(np.uint16), np.asarray(rv).view(np.uint16))
     check_half(gq, rq, "bf16", half_values(gq, "bf16"), eq, bq, what="Q, sampled tokens")
     check_half(gk, rk, "bf16", half_values(gk, "bf16"), ek, bk, what="K, sampled tokens")
+
+
+ROW_CHUNK, TOK_CHUNK = 1 << 22, 1 << 21  # rows / tokens per launch in the library
+
+
+@pytest.mark.parametrize("norm", ["rms", "layer"])
+def test_norms_across_launch_boundary(npa, orc, norm):
+    rows, cols = ROW_CHUNK + 5, 8
+    x = gpu_normal((rows, cols), "bf16", seed=2041)
+    r = gpu_normal((rows, cols), "bf16", seed=2042)
+    w = gpu_normal((cols,), "bf16", seed=2043, mean=1.0, std=0.1)
+    b = gpu_normal((cols,), "bf16", seed=2044, std=0.1)
+    h, out = empty((rows, cols), "bf16"), empty((rows, cols), "bf16")
+    if norm == "rms":
+        npa.fuse_add_rmsnorm(x, r, w, h, out, 1e-6)
+    else:
+        npa.fuse_add_layernorm(x, r, w, b, h, out, 1e-5)
+    torch.cuda.synchronize()
+    ri = torch.from_numpy(sample(rows, 4096, ROW_CHUNK, 4)).cuda()
+    xs, rs = to_host(x[ri]), to_host(r[ri])
+    ws, bs = to_host(w), to_host(b)
+    if norm == "rms":
+        rh, ro = orc.add_rmsnorm(xs, rs, ws, 1e-6, BF16)
+    else:
+        rh, ro = orc.add_layernorm(xs, rs, ws, bs, 1e-5, BF16)
+    assert np.array_equal(to_host(h[ri]).view(np.uint16), np.asarray(rh).view(np.uint16))
+    check_half(to_host(out[ri]), ro, "bf16", max_ulp=2,
+               what=f"{norm} [{rows}, {cols}] across the row launch boundary")
+
+
+@pytest.mark.parametrize("D", [128, 64])  # token workgroups; (token, chunk) threads
+def test_qkv_rope_across_launch_boundary(npa, orc, D):
+    T, H = TOK_CHUNK + 3, 1
+    qs = float(np.float32(1 / math.sqrt(D)))
+    qkv = gpu_normal((T, 3 * H * D), "bf16", seed=2045 + D)
+    pos_np = ((np.arange(T, dtype=np.int64) * 7) % 16384).astype(np.int32)
+    pos = torch.from_numpy(pos_np).cuda()
+    q, k, v = (empty((H, T, D), "bf16") for _ in range(3))
+    npa.fuse_qkv_rope(qkv, q, k, v, H, D, pos, 10000.0, qs)
+    torch.cuda.synchronize()
+    ti = sample(T, 2048, TOK_CHUNK, 5)
+    tt = torch.from_numpy(ti).cuda()
+    rq, rk, rv, eq, ek, bq, bk = orc.qkv_rope(to_host(qkv[tt]), H, D, 10000.0, qs, BF16,
+                                              positions=pos_np[ti],
+                                              want_bound=True)
+    gq, gk, gv = (to_host(t[:, tt, :]) for t in (q, k, v))
+    assert np.array_equal(gv.view(np.uint16), np.asarray(rv).view(np.uint16))
+    check_half(gq, rq, "bf16", half_values(gq, "bf16"), eq, bq, what="Q across the boundary")
+    check_half(gk, rk, "bf16", half_values(gk, "bf16"), ek, bk, what="K across the boundary")
