@@ -327,17 +327,27 @@ def graph_time(torch, npa, spec, copies: int, trials: int):
         call = npa.bind(name, *args)
         for _ in range(copies):
             call()
-    for _ in range(3):
-        gm.replay()
+    warm(torch, gm.replay)
     many, _, _ = time_calls(torch, gm.replay, 5, trials)
     g1 = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g1):
         npa.bind(name, *args)()
-    for _ in range(3):
-        g1.replay()
+    warm(torch, g1.replay)
     one, _, _ = time_calls(torch, g1.replay, max(3, copies), trials)
     torch.cuda.synchronize()
     return many / copies, one
+
+
+def warm(torch, fn, seconds: float = 0.02):
+    """Run fn back to back for `seconds` before it is timed: right after a
+    heavy phase (the steps, the GEMM) the first replays of a graph of small
+    kernels ran at half speed, a transient that a short run of the same work
+    settles."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
 
 
 def single_launch(torch, fn, trials: int = 41):
