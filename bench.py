@@ -645,7 +645,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         torch=lambda: torch.nn.functional.linear(yr, Wr, br).mul_(sc),
         plan=None, bytes=2 * (Mr * Kr + Nr * Kr + Mr * Nr + Kr + Nr),
         unfused_bytes=2 * (3 * Mr * Kr + Nr * Kr + 3 * Mr * Nr + Kr + Nr),
-        flops=2 * Mr * Nr * Kr, launches=3, kernel="rms_linear_dma4", elements=Mr * Nr)
+        flops=2 * Mr * Nr * Kr, launches=3, kernel="rms_linear_rs4", elements=Mr * Nr)
     W["_compile_ms"] = compile_ms
     return W
 

@@ -17,8 +17,8 @@
 // B[8 (l / 32) .. + 8][l % 32] (16 contiguous bytes of a K-contiguous row
 // each); accumulator register j of lane l is C[8 (j / 4) + 4 (l / 32) + j % 4]
 // [l % 32]. Three kernels, by how the operands reach LDS:
-//  - rms_linear_dma4: no norm weight (or one folded into Wt) and K % 64 == 0:
-//    four waves of 128 x 128 outputs, both operands by direct-to-LDS DMA;
+//  - rms_linear_rs4: no norm weight (or one folded into Wt) and K % 64 == 0:
+//    four waves of 128 x 128 outputs, both operands staged through registers;
 //  - rms_linear_reg4: the same four-wave layout with A = round(x w) formed in
 //    registers (B by DMA), or both operands through registers when K is not a
 //    multiple of 64 (masked partial last step);
@@ -272,41 +272,58 @@ __global__ __launch_bounds__(NTHR) void rms_linear_dma(const T* __restrict__ x,
   }
 }
 
-// ---- four-wave direct-to-LDS pipeline (K a multiple of 64) -----------------
+// ---- four-wave register-staged pipeline (K a multiple of 64) ---------------
 //
-// The same direct-to-LDS scheme with one wave per SIMD, each owning 128 x 128
-// outputs (4 x 4 MFMA blocks, 256 fp32 accumulators per lane, held in the
-// accumulation registers): a fragment read from LDS now feeds four MFMAs
-// instead of two or four, which halves the LDS read traffic per MFMA (the
-// eight-wave kernel's reads and DMA writes together kept LDS about as busy as
-// the matrix cores). With a single wave per SIMD no other wave hides LDS
-// latency, so the fragments of the next 16-wide k slice are read while this
-// slice's MFMAs run (two register sets, reads spread between the MFMAs). Each
-// K step is 64 wide, so every row's 128 bytes -- one cache line -- arrive in
-// one step; two 64 KiB stages form the ring. LDS rows are 128 bytes and chunk
-// c of row r sits at position c ^ ((r >> 1) & 7): gfx950 serves a 16-byte LDS
-// read 16 lanes per cycle from 64 four-byte banks, so the 16 rows of a phase
-// must fall in 16 different 16-byte bank groups (2 rows share a 256-byte bank
-// line, hence r & 1 and r >> 1). The earlier c ^ (r & 7) suits 8-lane
-// phases; rocprofv3 showed it stalled every fragment read for a 2-way bank
-// conflict (SQ_LDS_BANK_CONFLICT = 4 cycles per read). The row sums of x^2 come from the A
-// fragments the MFMAs read: each of the two waves sharing a 128-row half takes
-// two of its four 32-row blocks, so every wave runs the same code (a branch
-// around the sums would split the MFMA / LDS-read interleave of the waves that
-// take it, and with one wave per SIMD nothing else fills the gap).
+// One wave per SIMD, each owning 128 x 128 outputs (4 x 4 MFMA blocks, 256
+// fp32 accumulators per lane, held in the accumulation registers), so that a
+// fragment read from LDS feeds four MFMAs. With a single wave per SIMD no other
+// wave hides latency, so the fragments of the next 16-wide k slice are read
+// while this slice's MFMAs run (two register sets). Each K step is 64 wide, so
+// every row's 128 bytes -- one cache line -- arrive in one step; two 64 KiB
+// stages form the LDS ring. LDS rows are 128 bytes and chunk c of row r sits at
+// position c ^ ((r >> 1) & 7): gfx950 serves a 16-byte LDS read 16 lanes per
+// cycle from 64 four-byte banks, so the 16 rows of a phase must fall in 16
+// different 16-byte bank groups (2 rows share a 256-byte bank line, hence r & 1
+// and r >> 1; rocprofv3 showed c ^ (r & 7) stalling every fragment read for a
+// 2-way conflict).
+//
+// Operands reach LDS through registers: each thread holds 16 staged 16-byte
+// chunks (8 of A, 8 of B: rows 32 q + tid / 8, k chunk tid % 8, so a wave's load
+// covers 8 whole cache lines). A K step is four phases of 16 MFMAs; every
+// phase issues, one per MFMA, the 8 fragment reads of the next slice and 4
+// (LDS write, global reload) pairs: chunk q of step s + 1 is written into the
+// free stage and the register immediately reloaded with step s + 2. Each chunk
+// is written at the same point of every step, so every load has a full step
+// to arrive and the wait before each write is the same count (15 newer loads)
+// everywhere. The alternative -- loads straight into LDS -- can only start once
+// the stage is free and must land before the next barrier, and issuing the
+// step's 16 DMAs together stalled the wave behind them: measured on MI355X
+// (same tile, same outputs bit for bit) 472 us for the DMA form, 438 us with
+// its DMAs spread over the step, 433-445 us for this form.
+//
+// One barrier per step: before it each wave's LDS writes of step s + 1 (and its
+// reads of step s) are complete, so afterwards step s + 1 may be read and step
+// s's stage overwritten. Global loads are buffer loads with the k offset in the
+// scalar offset, so the 16 per-thread offsets stay loop invariant; rows past M
+// or N are read from the last valid row (their outputs are discarded), and the
+// buffer's size bounds every access to the tile's rows. The row sums of x^2 come
+// from the A fragments the MFMAs read: each of the two waves sharing a 128-row
+// half takes two of its four 32-row blocks, so every wave runs the same code.
 constexpr int Q_BK = 64, Q_NTHR = 256;
 constexpr int Q_ABYTES = BM * Q_BK * 2, Q_STAGE = 2 * Q_ABYTES;  // A then B, 32 KiB each
 constexpr int Q_SMEM = 2 * Q_STAGE > BM * CPITCH * 2 ? 2 * Q_STAGE : BM * CPITCH * 2;
 constexpr int Q_NJ = Q_ABYTES / 1024 / (Q_NTHR / 64);  // DMA instructions per wave and operand
 static_assert(BM == BN && Q_NJ == 8, "DMA map");
 
+constexpr int kReadOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};  // fragment f: 0..3 A, 4..7 B
+
 template <typename T, bool NORM, bool HAS_B>
-__global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ x,
-                                                          const T* __restrict__ Wt,
-                                                          const T* __restrict__ bias,
-                                                          T* __restrict__ out, int M, int N, int K,
-                                                          float eps, float scale, int tiles_m,
-                                                          int tiles_n, int vec_out) {
+__global__ __launch_bounds__(Q_NTHR) void rms_linear_rs4(const T* __restrict__ x,
+                                                         const T* __restrict__ Wt,
+                                                         const T* __restrict__ bias,
+                                                         T* __restrict__ out, int M, int N, int K,
+                                                         float eps, float scale, int tiles_m,
+                                                         int tiles_n, int vec_out) {
   typedef typename Mfma<T>::v8 v8;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Q_SMEM];
   __shared__ float rstd_s[BM];
@@ -318,27 +335,28 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ 
   const int g = t / per_group, within = t - g * per_group;
   const int gsz = min(GROUP_M, tiles_m - g * GROUP_M);
   const int m0 = (g * GROUP_M + within % gsz) * BM, n0 = (within / gsz) * BN;
-  // DMA map: instruction j of this wave fills LDS chunks (wave Q_NJ + j) 64 + lane:
-  // row p / 8, stored chunk p % 8, which holds k chunk (p % 8) ^ (row % 8)
-  const uint8_t* const xa0 = reinterpret_cast<const uint8_t*>(x + (int64_t)m0 * K);
-  const uint8_t* const wb0 = reinterpret_cast<const uint8_t*>(Wt + (int64_t)n0 * K);
-  uint32_t oa[Q_NJ], ob[Q_NJ];
+  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+  // staged chunk q: rows 32 (q % 8) + tid / 8 of A (q < 8) or B, k chunk tid % 8
+  const int srow = tid >> 3, skc = tid & 7;
+  uint32_t goff[16], soff[16];
 #pragma unroll
-  for (int j = 0; j < Q_NJ; ++j) {
-    const int p = (wave * Q_NJ + j) * 64 + lane;
-    const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-    oa[j] = (uint32_t)(((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2);
-    ob[j] = (uint32_t)(((min(n0 + r, N - 1) - n0) * K + 8 * c) * 2);
+  for (int q = 0; q < 16; ++q) {
+    const int r = 32 * (q & 7) + srow;
+    goff[q] = (uint32_t)((min(r, (q < 8 ? rows_a : rows_b) - 1) * K + 8 * skc) * 2);
+    soff[q] = (uint32_t)((q < 8 ? 0 : Q_ABYTES) + r * 128 + ((skc ^ ((r >> 1) & 7)) << 4));
   }
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (int64_t)m0 * K), (short)0, rows_a * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Wt + (int64_t)n0 * K), (short)0, rows_b * K * 2, 0x00020000);
   const int ksteps = K / Q_BK;
-  auto issue = [&](int step) {
-    const int k0b = min(step, ksteps - 1) * Q_BK * 2;  // steps past the end refill a free stage
-    uint8_t* st = smem + (step & 1) * Q_STAGE;
-#pragma unroll
-    for (int j = 0; j < Q_NJ; ++j) {
-      lds_dma16(xa0 + k0b, oa[j], st + (wave * Q_NJ + j) * 1024);
-      lds_dma16(wb0 + k0b, ob[j], st + Q_ABYTES + (wave * Q_NJ + j) * 1024);
-    }
+  u32x4 R[16];
+  auto gload = [&](int q, int step) {  // steps past the end reload the last one
+    const int k0b = min(step, ksteps - 1) * Q_BK * 2;
+    R[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q < 8 ? ra : rb, goff[q], k0b, 0));
+  };
+  auto swrite = [&](int q, int step) {
+    *reinterpret_cast<u32x4*>(smem + (step & 1) * Q_STAGE + soff[q]) = R[q];
   };
   f32x16 acc[4][4];
 #pragma unroll
@@ -349,30 +367,24 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ 
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   // register slot i holds row block i ^ (2 wn) of the wave's 128 rows, so that
   // slots 0 and 1 are the two blocks whose sums of squares this wave forms
-  // (the two waves of a row half split its four blocks; no branch)
   float ss[2] = {0.0f, 0.0f};
   const int l32 = lane & 31, hi = lane >> 5;
-  auto rb = [&](int i) { return i ^ (2 * wn); };
+  auto rb_ = [&](int i) { return i ^ (2 * wn); };
   v8 fa[2][4], fb[2][4];
-  // fragments of 16-wide k slice ks (0..3) of a stage into register set buf
-  auto rd = [&](int buf, int stage, int ks) {
+  // fragment f (0..3 A, 4..7 B) of 16-wide k slice ks of a stage into set buf
+  auto rd1 = [&](int buf, int stage, int ks, int f) {
     const uint8_t* As = smem + stage * Q_STAGE;
-    const uint8_t* Bs = As + Q_ABYTES;
     const int c = 2 * ks + hi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + 32 * rb(i) + l32;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(As + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-      __builtin_memcpy(&fa[buf][i], &v, 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + 32 * j + l32;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-      __builtin_memcpy(&fb[buf][j], &v, 16);
-    }
+    const int r = f < 4 ? wm * 128 + 32 * rb_(f) + l32 : wn * 128 + 32 * (f - 4) + l32;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(As + (f < 4 ? 0 : Q_ABYTES) + r * 128 +
+                                                    ((c ^ ((r >> 1) & 7)) << 4));
+    if (f < 4) __builtin_memcpy(&fa[buf][f], &v, 16);
+    else __builtin_memcpy(&fb[buf][f - 4], &v, 16);
   };
-  auto mm = [&](int buf) {
+  // one phase: 16 MFMAs on set buf; the 8 reads of slice nks of stage nst into
+  // set buf ^ 1; chunks q0 .. q0 + 3 of step wstep written to LDS, each reloaded
+  // with step wstep + 1. Source order is the issue order of the memory operations.
+  auto phase = [&](int buf, int nst, int nks, int q0, int wstep) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -381,41 +393,64 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 2; ++i) ss[i] = Mfma<T>::sumsq(fa[buf][i], ss[i]);
     }
-    // one MFMA, then one LDS read (the next slice's fragments), eight times
+    // reads in the order the next phase's MFMAs consume them: A0, B0..B3, A1..A3
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int u = 0; u < 4; ++u) {
+      rd1(buf ^ 1, nst, nks, kReadOrder[2 * u]);
+      rd1(buf ^ 1, nst, nks, kReadOrder[2 * u + 1]);
+      swrite(q0 + u, wstep);
+      gload(q0 + u, wstep + 1);
+    }
+    // MFMA, read, MFMA, read, MFMA, LDS write, MFMA, global load -- four times
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
-  issue(0);
-  issue(1);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Q_NJ) : "memory");  // this wave's step 0
-  asm volatile("s_barrier" ::: "memory");                         // everyone's
-  rd(0, 0, 0);
+  // prologue: step 0 -> stage 0; chunks 0..3 of step 1 -> stage 1 (the rest of
+  // step 1 stays in registers); registers 0..3 reloaded with step 2
+#pragma unroll
+  for (int q = 0; q < 16; ++q) gload(q, 0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) swrite(q, 0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) gload(q, 1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    swrite(q, 1);
+    gload(q, 2);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int f = 0; f < 8; ++f) rd1(0, 0, 0, f);
+  // lgkmcnt(0), written with the builtin so that the compiler's own wait
+  // placement knows no LDS operation is in flight when the loop starts
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   for (int s = 0; s < ksteps; ++s) {
     const int st = s & 1;
-    rd(1, st, 1);
-    mm(0);
-    rd(0, st, 2);
-    mm(1);
-    rd(1, st, 3);
-    mm(0);
-    // step s + 1 has landed everywhere, and every wave has read all of step s
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    phase(0, st, 1, 4, s + 1);
+    phase(1, st, 2, 8, s + 1);
+    phase(0, st, 3, 12, s + 1);
+    // this wave's writes of step s + 1 and reads of step s are complete; after
+    // the barrier step s + 1 is readable and step s's stage free for step s + 2
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     asm volatile("s_barrier" ::: "memory");
-    issue(s + 2);  // into the stage of step s
-    rd(0, st ^ 1, 0);
-    mm(1);
+    phase(1, st ^ 1, 0, 0, s + 2);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still write LDS
-  __syncthreads();
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");  // no load in flight
   if (NORM) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const float v = ss[i] + __shfl_xor(ss[i], 32);  // the two k halves of the row
-      if (hi == 0) rstd_s[wm * 128 + 32 * rb(i) + l32] = 1.0f / sqrtf(v / (float)K + eps);
+      if (hi == 0) rstd_s[wm * 128 + 32 * rb_(i) + l32] = 1.0f / sqrtf(v / (float)K + eps);
     }
     __syncthreads();
   }
@@ -431,7 +466,7 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ 
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wm * 128 + rb(i) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const int row = wm * 128 + rb_(i) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
       const float rs = NORM ? rstd_s[row] : 1.0f;
       T* const crow = cs + row * CPITCH + wn * 128 + l32;
 #pragma unroll
@@ -457,7 +492,7 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_dma4(const T* __restrict__ 
 
 // ---- four-wave kernel with register-staged operands --------------------------
 //
-// The four-wave layout of rms_linear_dma4 where an operand must pass through
+// The four-wave layout of rms_linear_rs4 where an operand must pass through
 // registers: A when a norm weight is passed (a = round(x w) is formed first),
 // and B as well when K is not a multiple of 64 (B_REGS: the last K step is
 // partial, and a DMA cannot zero the chunks past K -- registers are loaded
@@ -716,10 +751,10 @@ hipError_t launch_t(const void* x, const void* w, const void* Wt, const void* b,
   T* op = static_cast<T*>(out);
   if (!w && K % Q_BK == 0 && K < (1 << 22)) {
     if (b)
-      hipLaunchKernelGGL((rms_linear_dma4<T, NORM, true>), grid, dim3(Q_NTHR), 0, s, xp, Wp, bp,
+      hipLaunchKernelGGL((rms_linear_rs4<T, NORM, true>), grid, dim3(Q_NTHR), 0, s, xp, Wp, bp,
                          op, M, N, K, eps, scale, tm, tn, vec_out);
     else
-      hipLaunchKernelGGL((rms_linear_dma4<T, NORM, false>), grid, dim3(Q_NTHR), 0, s, xp, Wp, bp,
+      hipLaunchKernelGGL((rms_linear_rs4<T, NORM, false>), grid, dim3(Q_NTHR), 0, s, xp, Wp, bp,
                          op, M, N, K, eps, scale, tm, tn, vec_out);
     return hipGetLastError();
   }
