@@ -434,7 +434,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         desc="fp32 relu(a+b)*0.5, 1,048,576 elements",
         cold=_rotation(torch, c1_set, 12 * n1), single=True,
         sample_out=sampler(f1, lambda: _bits(y1)),
-        fused=f1,
+        fused=f1, fused_spec=("fuse_chain", (synth.C1_CHAIN, [ta, tb], y1)),
         unfused=npa.bind("unfused_chain", synth.C1_CHAIN, [ta, tb], y1),
         unfused_spec=("unfused_chain", (synth.C1_CHAIN, [ta, tb], y1)),
         bytes=12 * n1, unfused_bytes=28 * n1, launches=3, kernel="np_chain_spec_k4_n1048576",
@@ -457,7 +457,7 @@ def build_workloads(torch, npa, synth, quick: bool):
         desc="YOLO decode fp16 [1,255,80|40|20] -> fp32 [1,25200,85]",
         cold=_rotation(torch, c2_set, fb), single=True,
         sample_out=sampler(f2, lambda: _bits(out2)),
-        fused=f2,
+        fused=f2, fused_spec=("fuse_det_decode", (lv, st, an, out2)),
         unfused=npa.bind("unfused_det_decode", lv, st, an, out2, ws2),
         unfused_spec=("unfused_det_decode", (lv, st, an, out2, ws2)),
         bytes=fb, unfused_bytes=ub, launches=23, kernel="det_decode_kernel",
@@ -554,6 +554,8 @@ def build_workloads(torch, npa, synth, quick: bool):
             path="table" if n >= table_min else "per element")
         if n >= table_min:
             W[name]["fused_per_element"] = per_element
+        if name == "c5_small":
+            W[name]["fused_spec"] = ("fuse_chain", (ops, [xin], yo))
         if name == "c5_small":
             def c5_set(xin=xin, yo=yo):
                 x_ = torch.empty_like(xin)
@@ -1242,6 +1244,15 @@ def main(argv=None):
         per[k]["unfused"]["graph_one_call_per_replay_us_med"] = round(g_one * 1e6, 3)
         log(f"[bench] {k}: unfused launches replayed as a graph {g_med * 1e6:.2f} us per call "
             f"({g_one * 1e6:.2f} us with one call per replay)")
+        if "fused_spec" in w:
+            # a small fused call back to back from Python is bound by the host's
+            # launch rate; 64 of them captured in one graph give the device's
+            # per-call time (launch gaps inside a graph included)
+            f_g, f_one = graph_time(torch, npa, w["fused_spec"], 64, max(5, args.trials // 2))
+            per[k]["fused_graph_us_med"] = round(f_g * 1e6, 3)
+            per[k]["fused_graph_GBps"] = round(w["bytes"] / f_g / 1e9, 1)
+            log(f"[bench] {k}: fused call replayed as a graph of 64 {f_g * 1e6:.2f} us per call "
+                f"({f_one * 1e6:.2f} us with one call per replay)")
 
     # achievable streaming ceiling: a plain 16-byte-per-lane copy of 1 GiB
     n_copy = 1 << 28

@@ -11,7 +11,7 @@ import torch
 
 import synth
 from gpu_util import need_gpu, to_dev, to_host
-from tolerance import check_half, half_values
+from tolerance import check_f32, check_half, half_values
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +123,55 @@ def test_bind_keeps_its_tensors_alive(npa):
     del call
     gc.collect()
     assert wx() is None and wy() is None
+
+
+# The fused calls captured the same way (the bench times the small ones as
+# graphs of 64 back-to-back calls, so that the host's launch rate does not set
+# the figure); each replay is checked against the oracle's fused definition.
+@pytest.mark.parametrize("copies", [1, 64])
+def test_graph_fused_chain(npa, orc, copies):
+    xs = synth.c5_inputs(1 << 16)
+    x = to_dev(xs, "f16")
+    out = torch.empty_like(x)
+    ops = synth.c5_chain()
+    ref, exact, bound = orc.chain(ops, [xs], 1, want_bound=True)
+
+    def check(t):
+        got = to_host(t)
+        check_half(got, ref.view(np.uint16), "f16", half_values(got, "f16"), exact, bound,
+                   what="graph fused chain")
+
+    junk = torch.empty_like(x)
+    _replays(lambda: npa.fuse_chain(ops, [x], out), out,
+             lambda: npa.unfused_chain(ops, [x], junk), check, copies)
+
+
+@pytest.mark.parametrize("copies", [1, 64])
+def test_graph_fused_c1_chain(npa, orc, copies):
+    a, b = synth.c1_inputs(1 << 16)
+    ta, tb = to_dev(a, "f32"), to_dev(b, "f32")
+    out = torch.empty_like(ta)
+    ref = orc.chain(synth.C1_CHAIN, [a, b], 0)  # fp32 output
+
+    def check(t):
+        assert np.array_equal(to_host(t).view(np.uint32), np.asarray(ref).view(np.uint32))
+
+    _replays(lambda: npa.fuse_chain(synth.C1_CHAIN, [ta, tb], out), out, lambda: None, check,
+             copies)
+
+
+@pytest.mark.parametrize("copies", [1, 64])
+def test_graph_fused_det_decode(npa, orc, copies):
+    lvn = synth.c2_inputs()
+    lv = [to_dev(a, "f16") for a in lvn]
+    hw = [(h, w) for h, w, _ in synth.YOLO_LEVELS]
+    st = [s for _, _, s in synth.YOLO_LEVELS]
+    an = np.array(synth.YOLO_ANCHORS, np.float32).reshape(3, 3, 2)
+    out = torch.empty((1, 25200, 85), device="cuda")
+    want = orc.det_decode(lvn, hw, st, an, 3, 85, in_dt=1)
+
+    def check(t):
+        check_f32(t.cpu().numpy(), want, what="graph fused det decode")
+
+    _replays(lambda: npa.fuse_det_decode(lv, st, an.tolist(), out), out, lambda: None, check,
+             copies)
