@@ -177,35 +177,37 @@ int fill_det_args(np::DetArgs& a, const void* const* lv, int n_levels, const int
                   const int32_t* W, const float* strides, const float* anchors, int n_anchors,
                   int n_ch, int batch, float* out) {
   a = np::DetArgs{};
-  a.n_levels = n_levels;
-  a.n_anchors = n_anchors;
-  a.n_ch = n_ch;
-  a.batch = batch;
-  a.out = out;
+  np::DetHeader& h = a.h;
+  h.n_levels = n_levels;
+  h.n_anchors = n_anchors;
+  h.n_ch = n_ch;
+  h.batch = batch;
+  h.out = out;
   const int tp = np::det_tile_cells(n_ch);
-  a.tile_cells = tp;
+  h.tile_cells = tp;
   int64_t row = 0;
   int64_t tiles_total = 0;
-  a.tile_start[0] = 0;
+  h.tile_start[0] = 0;
   for (int l = 0; l < n_levels; ++l) {
-    a.H[l] = H[l];
-    a.W[l] = W[l];
-    a.in[l] = lv[l];
-    a.stride[l] = strides[l];
-    for (int j = 0; j < n_anchors * 2; ++j)
-      a.anchor[l * n_anchors * 2 + j] = anchors[l * n_anchors * 2 + j];
-    a.row_off[l] = row;
+    np::DetLevel& L = a.lv[l];
+    L.in = lv[l];
+    L.hw = H[l] * W[l];
+    L.w = W[l];
+    L.stride = strides[l];
+    L.inv_w = 1.0f / (float)W[l];
+    for (int j = 0; j < n_anchors * 2; ++j) L.anchor[j] = anchors[l * n_anchors * 2 + j];
+    L.row_off = row;
     const int64_t hw = (int64_t)H[l] * W[l];
     row += n_anchors * hw;
-    a.tiles[l] = (int32_t)((hw + tp - 1) / tp);
-    tiles_total += (int64_t)batch * n_anchors * a.tiles[l];
+    h.tiles[l] = (int32_t)((hw + tp - 1) / tp);
+    tiles_total += (int64_t)batch * n_anchors * h.tiles[l];
     // one 256-thread workgroup per tile: fewer than 2^31 work-items per launch
     if (tiles_total >= ((int64_t)1 << 23))
       return fail(NP_EINVAL, "output too large for one launch (%lld tiles of %d cells, limit 2^23)",
                   (long long)tiles_total, tp);
-    a.tile_start[l + 1] = (int32_t)tiles_total;
+    h.tile_start[l + 1] = (int32_t)tiles_total;
   }
-  a.total_rows = row;
+  h.total_rows = row;
   return NP_OK;
 }
 

@@ -12,6 +12,8 @@
 //            conflict);
 //   phase 2: the tile's output rows are one contiguous span of the
 //            concatenated output; copy it linearly with dwordx4 stores.
+#include <stddef.h>
+
 #include "device.h"
 #include "internal.h"
 
@@ -74,28 +76,57 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
   extern __shared__ float tile[];
+  // the header, copied at once as ints so that its reads go out together
+  // (copied as a struct, the compiler spread them over several waits)
+  int32_t hw_[sizeof(DetHeader) / 4];
+  __builtin_memcpy(hw_, &a.h, sizeof(hw_));
+  DetHeader h;
+  __builtin_memcpy(&h, hw_, sizeof(h));
   const int bid = NP_DET_XCD_REMAP ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
-  int l = 0;
-  while (l + 1 < a.n_levels && bid >= a.tile_start[l + 1]) ++l;
-  const int idx = bid - a.tile_start[l];
-  const int tiles = a.tiles[l];
-  const int A = a.n_anchors;
-  const int C = a.n_ch;
+  asm volatile("" ::"s"(h.out), "s"(h.total_rows), "s"(bid));  // all in the first round
+  // the level, by comparisons against the whole prefix rather than a search
+  // whose every step waits for its own read
+  const int nl = h.n_levels;
+  int l = 0, ts = 0, tiles = h.tiles[0];
+#pragma unroll
+  for (int i = 1; i < kDetMaxLevels; ++i) {
+    const int tsi = h.tile_start[i];
+    const int ti = h.tiles[i];
+    const bool past = i < nl && bid >= tsi;
+    l += past ? 1 : 0;
+    ts = past ? tsi : ts;
+    tiles = past ? ti : tiles;
+  }
+  const int idx = bid - ts;
+  const int A = h.n_anchors;
+  const int C = h.n_ch;
   const int b = idx / (A * tiles);
   const int rem = idx - b * A * tiles;
   const int an = rem / tiles;
   const int tl = rem - an * tiles;
-  const int HW = a.H[l] * a.W[l];
-  const int TP = a.tile_cells;
+  // the level's record and the tile's anchor: one more batch of reads
+  struct {
+    const void* in;
+    int64_t row_off;
+    int32_t hw, w;
+    float stride, inv_w;
+  } L;
+  static_assert(sizeof(L) == offsetof(DetLevel, anchor), "level record layout");
+  __builtin_memcpy(&L, &a.lv[l], sizeof(L));
+  float anc[2];
+  __builtin_memcpy(anc, &a.lv[l].anchor[2 * an], sizeof(anc));
+  asm volatile("" ::"s"(anc[0]), "s"(anc[1]));  // read with the record, not later
+  const int HW = L.hw;
+  const int TP = h.tile_cells;
   const int cell0 = tl * TP;
   const int ncell = min(TP, HW - cell0);
-  const T* plane0 = static_cast<const T*>(a.in[l]) + ((int64_t)(b * A + an) * C) * HW + cell0;
+  const T* plane0 = static_cast<const T*>(L.in) + ((int64_t)(b * A + an) * C) * HW + cell0;
   TileConst tc;
-  tc.stride = a.stride[l];
-  tc.aw = a.anchor[(l * A + an) * 2 + 0];
-  tc.ah = a.anchor[(l * A + an) * 2 + 1];
-  tc.w = a.W[l];
-  tc.inv_w = 1.0f / (float)tc.w;
+  tc.stride = L.stride;
+  tc.aw = anc[0];
+  tc.ah = anc[1];
+  tc.w = L.w;
+  tc.inv_w = L.inv_w;
 
   // phase 1: channel planes -> decoded values in row layout
   if (VEC) {
@@ -123,8 +154,8 @@ __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
   __syncthreads();
 
   // phase 2: contiguous output span of ncell rows
-  const int64_t row0 = a.row_off[l] + (int64_t)an * HW + cell0;
-  float* dst = a.out + ((int64_t)b * a.total_rows + row0) * C;
+  const int64_t row0 = L.row_off + (int64_t)an * HW + cell0;
+  float* dst = h.out + ((int64_t)b * h.total_rows + row0) * C;
   const int len = ncell * C;
   const int head = (int)(((16 - ((uintptr_t)dst & 15)) & 15) >> 2);  // floats to 16-B alignment
   if (((uintptr_t)dst & 3) == 0 && len > head + 4) {
@@ -147,8 +178,8 @@ __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
 
 template <typename T>
 hipError_t launch_t(const DetArgs& a, bool vec_in, hipStream_t s) {
-  const int blocks = a.tile_start[a.n_levels];
-  const size_t lds = (size_t)a.tile_cells * a.n_ch * sizeof(float);
+  const int blocks = a.h.tile_start[a.h.n_levels];
+  const size_t lds = (size_t)a.h.tile_cells * a.h.n_ch * sizeof(float);
   if (vec_in)
     hipLaunchKernelGGL((det_decode_kernel<T, true>), dim3(blocks), dim3(kBlock), lds, s, a);
   else

@@ -26,18 +26,30 @@ hipError_t launch_chain(const ChainArgs& a, int in_dt, int out_dt, int n_inputs,
                         hipStream_t s);
 
 // detection-head decode
-struct DetArgs {
+// Arguments of the decode kernel. A workgroup reads the header first (fixed
+// offsets: two 64-byte lines), finds its level there, then reads that level's
+// record (fields and anchors, a few lines, all in one batch): two rounds of
+// argument reads before its first plane load.
+constexpr int kDetMaxLevels = 8, kDetMaxAnchors = 16;
+struct DetLevel {
+  const void* in;       // the level's logits [batch, n_anchors * n_ch, H, W]
+  int64_t row_off;      // first output row of the level (within one batch image)
+  int32_t hw, w;        // H * W and W
+  float stride, inv_w;  // grid stride; 1 / W (float)
+  float anchor[2 * kDetMaxAnchors];  // (width, height) per anchor
+};
+struct DetHeader {
   int32_t n_levels, n_anchors, n_ch, batch;
-  int32_t H[8], W[8];
-  int64_t row_off[8];     // first output row of level l (within one batch image)
-  int32_t tiles[8];       // tiles per (batch, anchor) of level l
-  int32_t tile_start[9];  // prefix over levels of batch * n_anchors * tiles[l]
-  int64_t total_rows;     // rows per batch image
-  float stride[8];
-  float anchor[8 * 16 * 2];
-  const void* in[8];
+  int32_t tile_cells;                     // cells per tile
+  int32_t tile_start[kDetMaxLevels + 1];  // prefix over levels of batch * n_anchors * tiles[l]
+  int32_t tiles[kDetMaxLevels];           // tiles per (batch, anchor) of level l
+  int32_t pad_;
+  int64_t total_rows;                     // rows per batch image
   float* out;
-  int32_t tile_cells;     // cells per tile
+};
+struct DetArgs {
+  DetHeader h;
+  DetLevel lv[kDetMaxLevels];
 };
 hipError_t launch_det_decode(const DetArgs& a, int in_dt, bool vec_in, hipStream_t s);
 int det_tile_cells(int n_ch);  // cells per workgroup tile of the decode kernel
