@@ -173,14 +173,17 @@ def test_fold_norm_weight_bit_exact(npa, orc, dt):
 # the direct-to-LDS kernels: no norm weight and K a multiple of 32 (the
 # four-wave kernel when K is a multiple of 64, the eight-wave one otherwise);
 # ragged M and N, and N not a multiple of 8 (element-wise output stores)
-DMA_CASES = [(300, 260, 512), (33, 1000, 96), (517, 40, 64), (256, 512, 4096), (1, 8, 32),
-             (1, 8, 64), (513, 257, 192), (300, 250, 128), (70, 30, 96)]
+# no norm weight: K % 64 == 0 -> the register-staged four-wave kernel (1, 2, 3,
+# 8 and 64 K steps: its prologue stages steps 0..2, clamped past the end);
+# K % 32 == 0 otherwise -> the eight-wave direct-to-LDS kernel
+NO_W_CASES = [(300, 260, 512), (33, 1000, 96), (517, 40, 64), (256, 512, 4096), (1, 8, 32),
+              (1, 8, 64), (513, 257, 192), (300, 250, 128), (70, 30, 96)]
 
 
-@pytest.mark.parametrize("M,N,K", DMA_CASES)
+@pytest.mark.parametrize("M,N,K", NO_W_CASES)
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("with_b", [True, False])
-def test_direct_lds_path_matches_oracle(npa, orc, M, N, K, dt, with_b):
+def test_no_norm_weight_paths_match_oracle(npa, orc, M, N, K, dt, with_b):
     x, w, Wt, b = _inputs(M, K, N, 6200 + M + N + K, dt)
     b = b if with_b else None
     want, exact, cond = orc.rmsnorm_linear(x, None, Wt, b, 1e-6, 0.75, ORACLE_DT[dt],
@@ -189,7 +192,7 @@ def test_direct_lds_path_matches_oracle(npa, orc, M, N, K, dt, with_b):
     npa.fuse_rmsnorm_linear(to_dev(x, dt), None, to_dev(Wt, dt),
                             None if b is None else to_dev(b, dt), out, 1e-6, 0.75)
     torch.cuda.synchronize()
-    _check(to_host(out), exact, cond, K, dt, want_bits=want, what=f"direct-to-LDS {M}x{N}x{K}")
+    _check(to_host(out), exact, cond, K, dt, want_bits=want, what=f"no norm weight {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 260, 512), (129, 130, 96)])
