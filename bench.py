@@ -969,6 +969,10 @@ def main(argv=None):
                     help="only a few launches of each kernel (for rocprofv3 runs)")
     ap.add_argument("--only", default="", help="profile mode: comma-separated workloads")
     ap.add_argument("--manifest", default="", help="profile mode: write the dispatch manifest here")
+    ap.add_argument("--fused-graph-trace", default="", metavar="WORKLOAD",
+                    help="for a kernel trace: the workload's fused call captured 64 times in one "
+                         "graph and replayed 8 times after the clocks settle (device-side "
+                         "back-to-back dispatches of a small kernel)")
     ap.add_argument("--graph-trace", default="", metavar="WORKLOAD",
                     help="for a kernel trace: the workload's unfused call 100 times eagerly, "
                          "then 100 replays of a graph holding one call, then 2 replays of a "
@@ -1054,6 +1058,28 @@ def main(argv=None):
             with open(args.manifest, "w") as f:
                 json.dump({"calibration_bytes": 4 * n, "dispatches": manifest}, f, indent=1)
         log("[bench] profile pass done")
+        return 0
+
+    if args.fused_graph_trace:
+        name, a_ = W[args.fused_graph_trace]["fused_spec"]
+        s_ = torch.cuda.Stream()
+        s_.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_):
+            npa.bind(name, *a_)()
+        torch.cuda.current_stream().wait_stream(s_)
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_):
+            c_ = npa.bind(name, *a_)
+            for _ in range(64):
+                c_()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < SETTLE_S:  # clocks up
+            W["c5_large"]["fused"]()
+            torch.cuda.synchronize()
+        for _ in range(8):
+            g_.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] fused graph trace of {args.fused_graph_trace} done")
         return 0
 
     if args.graph_trace:
