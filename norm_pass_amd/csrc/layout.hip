@@ -58,10 +58,12 @@ struct TileGeom {
   static constexpr int VPR = ROWB / 16;              // 16-byte vectors per row
   static constexpr int RPP = NT / VPR;               // rows per pass of NT threads
   static constexpr int IPV = 16 / U;                 // units per vector
-  // LDS row pitch: one pad word (keeps a column's units in different banks);
-  // 8- and 16-byte units pad by their own size so LDS accesses stay aligned.
-  static constexpr int PITCH = ROWB + (U <= 4 ? 4 : U);
-  static constexpr int LDS = T * PITCH;              // 66,048 bytes at most (U = 4)
+  // LDS row pitch: one pad word for 1- and 2-byte units (keeps a column's
+  // units in different banks); 8- and 16-byte units pad by their own size so
+  // LDS accesses stay aligned; 4-byte units: 640 bytes, with the placement
+  // in swz4.
+  static constexpr int PITCH = U == 4 ? 640 : ROWB + (U < 4 ? 4 : U);
+  static constexpr int LDS = T * PITCH;              // 81,920 bytes at most (U = 4)
 };
 
 // Store 16 bytes into LDS at an address aligned to the unit size only.
@@ -79,6 +81,18 @@ __device__ __forceinline__ void lds_put16(uint8_t* p, u32x4 v) {
     q[2] = v.z;
     q[3] = v.w;
   }
+}
+
+// 4-byte units: unit (i, c) of the 128 x 128 tile at word
+// ((c / 4 + i / 4) mod 32) + 32 (c mod 4) of row i, rows 640 bytes apart (160
+// words, so row i starts on bank 32 (i mod 2)). A wave stores rows i, i + 1
+// (i even), lane (row, v) the units 4 v .. 4 v + 3 at four fixed offsets: for
+// each store the banks are ((v + const) mod 32) + 32 (row mod 2), all 64. It
+// reads units (4 v + k, j) and (4 v + k, j + 1) (j even): ((v + const) mod 32)
+// + 32 ((k + j) mod 2), all 64 again. With the 516-byte pitch the reads were
+// two-way conflicted (a wave's 32 reads of one output row fell on 16 banks).
+__device__ __forceinline__ uint32_t swz4(int i, int c) {
+  return (uint32_t)(i * 640 + 4 * ((((c >> 2) + (i >> 2)) & 31) + 32 * (c & 3)));
 }
 
 template <int U, bool VEC>
@@ -115,6 +129,22 @@ __global__ __launch_bounds__(TileGeom<U>::NT) void tr_tile(const uint8_t* __rest
     // Row pitches and tile edges are whole 16-byte vectors on both sides.
     constexpr int P = G::T / G::RPP;  // passes
     const int lr = tid / G::VPR, lv = tid % G::VPR;
+    // units 4 lv .. 4 lv + 3 of tile row i (4-byte units only)
+    auto put4 = [&](int i, int lv_, u32x4 x) {
+      uint32_t* q = reinterpret_cast<uint32_t*>(lds + swz4(i, 4 * lv_));
+      q[0] = x.x;
+      q[32] = x.y;
+      q[64] = x.z;
+      q[96] = x.w;
+    };
+    // unit (i, c) of the tile
+    auto get = [&](int i, int c) -> W {
+      if constexpr (U == 4) {
+        return *reinterpret_cast<const W*>(lds + swz4(i, c));
+      } else {
+        return *reinterpret_cast<const W*>(lds + i * G::PITCH + c * U);
+      }
+    };
     if (nr == G::T && ns == G::T) {
       // Interior tile: every load is issued before the first LDS store, so
       // each wave keeps P loads in flight.
@@ -122,15 +152,19 @@ __global__ __launch_bounds__(TileGeom<U>::NT) void tr_tile(const uint8_t* __rest
 #pragma unroll
       for (int p = 0; p < P; ++p) v[p] = load_raw(src + (p * G::RPP + lr) * in_pitch + lv * 16);
 #pragma unroll
-      for (int p = 0; p < P; ++p) lds_put16<U>(lds + (p * G::RPP + lr) * G::PITCH + lv * 16, v[p]);
+      for (int p = 0; p < P; ++p) {
+        if constexpr (U == 4) {
+          put4(p * G::RPP + lr, lv, v[p]);
+        } else {
+          lds_put16<U>(lds + (p * G::RPP + lr) * G::PITCH + lv * 16, v[p]);
+        }
+      }
       __syncthreads();
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         W e[G::IPV];
 #pragma unroll
-        for (int k = 0; k < G::IPV; ++k)
-          e[k] = *reinterpret_cast<const W*>(lds + (lv * G::IPV + k) * G::PITCH +
-                                             (p * G::RPP + lr) * U);
+        for (int k = 0; k < G::IPV; ++k) e[k] = get(lv * G::IPV + k, p * G::RPP + lr);
         __builtin_memcpy(&v[p], e, 16);
       }
 #pragma unroll
@@ -140,8 +174,13 @@ __global__ __launch_bounds__(TileGeom<U>::NT) void tr_tile(const uint8_t* __rest
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int i = p * G::RPP + lr;
-      if (i < nr && lv * G::IPV < ns)
-        lds_put16<U>(lds + i * G::PITCH + lv * 16, load_raw(src + i * in_pitch + lv * 16));
+      if (i < nr && lv * G::IPV < ns) {
+        if constexpr (U == 4) {
+          put4(i, lv, load_raw(src + i * in_pitch + lv * 16));
+        } else {
+          lds_put16<U>(lds + i * G::PITCH + lv * 16, load_raw(src + i * in_pitch + lv * 16));
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -150,8 +189,7 @@ __global__ __launch_bounds__(TileGeom<U>::NT) void tr_tile(const uint8_t* __rest
       if (j < ns && lv * G::IPV < nr) {
         W e[G::IPV];
 #pragma unroll
-        for (int k = 0; k < G::IPV; ++k)
-          e[k] = *reinterpret_cast<const W*>(lds + (lv * G::IPV + k) * G::PITCH + j * U);
+        for (int k = 0; k < G::IPV; ++k) e[k] = get(lv * G::IPV + k, j);
         u32x4 v;
         __builtin_memcpy(&v, e, 16);
         store_raw_nt(dst + j * out_pitch + lv * 16, v);
