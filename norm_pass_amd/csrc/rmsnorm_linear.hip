@@ -310,7 +310,7 @@ __global__ __launch_bounds__(NTHR) void rms_linear_dma(const T* __restrict__ x,
 // from the A fragments the MFMAs read: each of the two waves sharing a 128-row
 // half takes two of its four 32-row blocks, so every wave runs the same code.
 constexpr int Q_BK = 64, Q_NTHR = 256;
-constexpr int Q_ABYTES = BM * Q_BK * 2, Q_STAGE = 2 * Q_ABYTES;  // A then B, 32 KiB each
+constexpr int Q_ABYTES = BM * Q_BK * 2, Q_STAGE = 2 * Q_ABYTES;  // A and B, 32 KiB each
 constexpr int Q_SMEM = 2 * Q_STAGE > BM * CPITCH * 2 ? 2 * Q_STAGE : BM * CPITCH * 2;
 constexpr int Q_NJ = Q_ABYTES / 1024 / (Q_NTHR / 64);  // DMA instructions per wave and operand
 static_assert(BM == BN && Q_NJ == 8, "DMA map");
@@ -338,25 +338,34 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_rs4(const T* __restrict__ x
   const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
   // staged chunk q: rows 32 (q % 8) + tid / 8 of A (q < 8) or B, k chunk tid % 8
   const int srow = tid >> 3, skc = tid & 7;
-  uint32_t goff[16], soff[16];
+  uint32_t goff[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int r = 32 * (q & 7) + srow;
     goff[q] = (uint32_t)((min(r, (q < 8 ? rows_a : rows_b) - 1) * K + 8 * skc) * 2);
-    soff[q] = (uint32_t)((q < 8 ? 0 : Q_ABYTES) + r * 128 + ((skc ^ ((r >> 1) & 7)) << 4));
   }
+  // LDS: A of stages 0 and 1, then B of stages 0 and 1, so that with the stage
+  // known at compile time every LDS address is a loop-invariant register plus
+  // an immediate offset (no address arithmetic in the K loop). Row r = 32 j +
+  // srow has the swizzle of srow, so chunk q sits 4096 (q % 8) bytes above the
+  // thread's first chunk of its operand.
+  const uint32_t wa0 = (uint32_t)(srow * 128 + ((skc ^ ((srow >> 1) & 7)) << 4));
+  uint32_t wb0 = 2 * Q_ABYTES + wa0;
+  // opaque to the compiler, which would otherwise fold the 64 KiB into the
+  // offsets of the stage-1 B writes, past the 16-bit immediate field
+  asm volatile("" : "+v"(wb0));
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(x + (int64_t)m0 * K), (short)0, rows_a * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Wt + (int64_t)n0 * K), (short)0, rows_b * K * 2, 0x00020000);
   const int ksteps = K / Q_BK;
   u32x4 R[16];
-  auto gload = [&](int q, int step) {  // steps past the end reload the last one
+  auto gload = [&](int q, int step) __attribute__((always_inline)) {  // steps past the end reload the last one
     const int k0b = min(step, ksteps - 1) * Q_BK * 2;
     R[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q < 8 ? ra : rb, goff[q], k0b, 0));
   };
-  auto swrite = [&](int q, int step) {
-    *reinterpret_cast<u32x4*>(smem + (step & 1) * Q_STAGE + soff[q]) = R[q];
+  auto swrite = [&](int q, int wst) __attribute__((always_inline)) {  // wst: the stage, a compile-time constant
+    *reinterpret_cast<u32x4*>(smem + (q < 8 ? wa0 : wb0) + 4096 * (q & 7) + wst * Q_ABYTES) = R[q];
   };
   f32x16 acc[4][4];
 #pragma unroll
@@ -371,20 +380,31 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_rs4(const T* __restrict__ x
   const int l32 = lane & 31, hi = lane >> 5;
   auto rb_ = [&](int i) { return i ^ (2 * wn); };
   v8 fa[2][4], fb[2][4];
-  // fragment f (0..3 A, 4..7 B) of 16-wide k slice ks of a stage into set buf
-  auto rd1 = [&](int buf, int stage, int ks, int f) {
-    const uint8_t* As = smem + stage * Q_STAGE;
-    const int c = 2 * ks + hi;
-    const int r = f < 4 ? wm * 128 + 32 * rb_(f) + l32 : wn * 128 + 32 * (f - 4) + l32;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(As + (f < 4 ? 0 : Q_ABYTES) + r * 128 +
-                                                    ((c ^ ((r >> 1) & 7)) << 4));
+  // fragment bases per k slice ks: the lane's row l32 (its swizzle is that of
+  // every row 32 j + l32) and chunk 2 ks + hi; A slots 0, 1 (blocks 2 wn, 2 wn
+  // + 1) from ra_lo, slots 2, 3 from ra_hi, B block j at rbb + 4096 j
+  uint32_t ra_lo[4], ra_hi[4], rbb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t lp = (uint32_t)(l32 * 128 + (((2 * ks + hi) ^ ((l32 >> 1) & 7)) << 4));
+    ra_lo[ks] = wm * 16384 + 8192 * wn + lp;
+    ra_hi[ks] = wm * 16384 + 8192 * (1 - wn) + lp;
+    rbb[ks] = 2 * Q_ABYTES + wn * 16384 + lp;
+  }
+  // fragment f (0..3 A, 4..7 B) of 16-wide k slice ks of a stage (compile-time
+  // constant) into set buf
+  auto rd1 = [&](int buf, int stage, int ks, int f) __attribute__((always_inline)) {
+    const uint32_t off = f < 4 ? (f < 2 ? ra_lo[ks] : ra_hi[ks]) + 4096 * (f & 1)
+                               : rbb[ks] + 4096 * (f - 4);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + off + stage * Q_ABYTES);
     if (f < 4) __builtin_memcpy(&fa[buf][f], &v, 16);
     else __builtin_memcpy(&fb[buf][f - 4], &v, 16);
   };
   // one phase: 16 MFMAs on set buf; the 8 reads of slice nks of stage nst into
-  // set buf ^ 1; chunks q0 .. q0 + 3 of step wstep written to LDS, each reloaded
-  // with step wstep + 1. Source order is the issue order of the memory operations.
-  auto phase = [&](int buf, int nst, int nks, int q0, int wstep) {
+  // set buf ^ 1; chunks q0 .. q0 + 3 of step wstep written to LDS (its stage
+  // wst), each reloaded with step wstep + 1. Source order is the issue order of
+  // the memory operations.
+  auto phase = [&](int buf, int nst, int nks, int q0, int wstep, int wst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -398,7 +418,7 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_rs4(const T* __restrict__ x
     for (int u = 0; u < 4; ++u) {
       rd1(buf ^ 1, nst, nks, kReadOrder[2 * u]);
       rd1(buf ^ 1, nst, nks, kReadOrder[2 * u + 1]);
-      swrite(q0 + u, wstep);
+      swrite(q0 + u, wst);
       gload(q0 + u, wstep + 1);
     }
     // MFMA, read, MFMA, read, MFMA, LDS write, MFMA, global load -- four times
@@ -434,17 +454,23 @@ __global__ __launch_bounds__(Q_NTHR) void rms_linear_rs4(const T* __restrict__ x
   // lgkmcnt(0), written with the builtin so that the compiler's own wait
   // placement knows no LDS operation is in flight when the loop starts
   __builtin_amdgcn_s_waitcnt(0xC07F);
-  for (int s = 0; s < ksteps; ++s) {
-    const int st = s & 1;
-    phase(0, st, 1, 4, s + 1);
-    phase(1, st, 2, 8, s + 1);
-    phase(0, st, 3, 12, s + 1);
+  // K step s, its stage st = s % 2 spelled out as a constant
+  auto kstep = [&](int s, int st) __attribute__((always_inline)) {
+    phase(0, st, 1, 4, s + 1, st ^ 1);
+    phase(1, st, 2, 8, s + 1, st ^ 1);
+    phase(0, st, 3, 12, s + 1, st ^ 1);
     // this wave's writes of step s + 1 and reads of step s are complete; after
     // the barrier step s + 1 is readable and step s's stage free for step s + 2
     __builtin_amdgcn_s_waitcnt(0xC07F);
     asm volatile("s_barrier" ::: "memory");
-    phase(1, st ^ 1, 0, 0, s + 2);
+    phase(1, st ^ 1, 0, 0, s + 2, st);
+  };
+  int s = 0;
+  for (; s + 1 < ksteps; s += 2) {
+    kstep(s, 0);
+    kstep(s + 1, 1);
   }
+  if (s < ksteps) kstep(s, 0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");  // no load in flight
   if (NORM) {
 #pragma unroll
