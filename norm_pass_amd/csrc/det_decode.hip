@@ -55,6 +55,45 @@ __device__ __forceinline__ float decode_one(const TileConst& tc, int k, int cell
   return is_exp ? e * anc : (sig + grid) * mul;
 }
 
+// The same values for the N consecutive cells of one channel k that a thread
+// decodes from one vector, with every channel choice made once per thread: the
+// lanes of a wave then run one instruction stream whatever their channels
+// (with per-element selects the compiler branched, and the wave holding the
+// box channels ran every branch). The cells c0 .. c0 + N - 1 lie in at most two
+// grid rows when W >= N: cell c0 + i is at x0 + i - W [i >= W - x0], row y0 +
+// [i >= W - x0], and the grid term is gA + gB i + gD [i >= W - x0] with
+// (gA, gB, gD) = (x0, 1, -W) for k = 0, (y0, 0, 1) for k = 1 and 0 otherwise,
+// all small integers, exact in fp32: the results are those of decode_one.
+struct ChanConst {
+  float gA, gB, gD, mul, anc, sgn;
+  int wrap_at;
+  bool is_exp;
+};
+
+__device__ __forceinline__ ChanConst chan_const(const TileConst& tc, int k, int c0) {
+  ChanConst cc;
+  const int y0 = (int)(((float)c0 + 0.5f) * tc.inv_w);
+  const int x0 = c0 - y0 * tc.w;
+  cc.is_exp = k == 2 || k == 3;
+  cc.sgn = cc.is_exp ? 1.0f : -1.0f;
+  cc.gA = k == 0 ? (float)x0 : k == 1 ? (float)y0 : 0.0f;
+  cc.gB = k == 0 ? 1.0f : 0.0f;
+  cc.gD = k == 0 ? -(float)tc.w : k == 1 ? 1.0f : 0.0f;
+  cc.mul = k < 2 ? tc.stride : 1.0f;
+  cc.anc = k == 3 ? tc.ah : tc.aw;
+  cc.wrap_at = tc.w - x0;
+  return cc;
+}
+
+__device__ __forceinline__ float decode_cell(const ChanConst& cc, int i, float t) {
+  const float e = np_fast_exp(t * cc.sgn);
+  const float grid = __builtin_fmaf(cc.gB, (float)i, cc.gA) + (i >= cc.wrap_at ? cc.gD : 0.0f);
+  const float sig = __builtin_amdgcn_rcpf(__builtin_fmaf(e, 0x1p-32f, 0x1p-32f)) * 0x1p-32f;
+  const float box = (sig + grid) * cc.mul;
+  const float ex = e * cc.anc;
+  return cc.is_exp ? ex : box;
+}
+
 #ifndef NP_DET_XCD_REMAP
 #define NP_DET_XCD_REMAP 1
 #endif
@@ -132,15 +171,22 @@ __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
   if (VEC) {
     constexpr int N = Vec<T>::N;
     const int groups = ncell / N;  // ncell is a multiple of N on this path
+    const bool two_rows = tc.w >= N;  // a vector's cells span at most two grid rows
     for (int e = threadIdx.x; e < C * groups; e += kBlock) {
       const int k = e / groups;
       const int cg = e - k * groups;
       float t[N];
       load_vec<T>(plane0 + (int64_t)k * HW + cg * N, t);
+      if (two_rows) {
+        const ChanConst cc = chan_const(tc, k, cell0 + cg * N);
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int c = cg * N + i;
-        tile[c * C + k] = decode_one(tc, k, cell0 + c, t[i]);
+        for (int i = 0; i < N; ++i) tile[(cg * N + i) * C + k] = decode_cell(cc, i, t[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const int c = cg * N + i;
+          tile[c * C + k] = decode_one(tc, k, cell0 + c, t[i]);
+        }
       }
     }
   } else {
