@@ -74,6 +74,9 @@ def test_full_config_unfused(npa, orc):
     (((16, 16, 8.0),), 1, 85, "f16", False),               # misaligned level pointers
     (((1, 1, 8.0), (2, 1, 16.0)), 1, 5, "f16", True),
     (((64, 80, 8.0),), 1, 600, "f16", True),               # wide rows: smaller tiles
+    # W not a multiple of the vector: a vector's cells cross into the next grid row
+    (((8, 12, 8.0), (4, 10, 16.0)), 2, 85, "f16", True),
+    (((6, 6, 8.0), (8, 2, 16.0)), 1, 9, "f32", True),       # fp32 vectors; W = 2 < 4 per cell
 ])
 def test_shapes(npa, orc, levels, batch, n_ch, dt, align):
     lv = synth.c2_inputs(levels=levels, n_ch=n_ch, batch=batch, dtype=dt, seed=7)
@@ -92,9 +95,12 @@ def test_shapes(npa, orc, levels, batch, n_ch, dt, align):
         assert rel.max() <= 2 * (2.0 ** -10 if dt == "f16" else 2.0 ** -7)
 
 
-def test_marker_layout_bit_exact(npa, orc):
+@pytest.mark.parametrize("hw", [
+    [(3, 2), (1, 3)],    # per-cell path (H*W not a multiple of 8)
+    [(2, 12), (1, 8)],   # 16-byte vectors; with W = 12 some vectors cross a grid row
+])
+def test_marker_layout_bit_exact(npa, orc, hw):
     """One logit = 1, all others 0: exactly the predicted output element changes."""
-    hw = [(3, 2), (1, 3)]
     n_anchors, n_ch = 3, 6
     levels = tuple((h, w, s) for (h, w), s in zip(hw, (8.0, 16.0)))
     zero = [np.zeros((1, n_anchors * n_ch, h, w), np.float16) for h, w in hw]
