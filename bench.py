@@ -962,7 +962,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--trials", type=int, default=11)
+    ap.add_argument("--trials", type=int, default=21)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="reduced sizes (smoke runs only)")
     ap.add_argument("--profile", action="store_true",
