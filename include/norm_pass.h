@@ -350,9 +350,11 @@ int np_empty_launches(int count, hipStream_t stream);
  *   out_mn = scale * (rstd_m * sum_k round_dt(x_mk w_k) Wt_nk + bias_n)
  *   (the product x w is rounded to dt once, as the matrix cores take dt
  *   operands; the sums are fp32).
- * Kernels: with w_norm == NULL and K a multiple of 32 both operands stream
- * straight into LDS (a four-stage ring); otherwise x passes through registers
- * where it is multiplied by w_norm (see np_fold_norm_weight).
+ * Kernels: with w_norm == NULL and K a multiple of 64, both operands are
+ * staged through registers into a two-stage LDS ring (the fastest form); with
+ * w_norm == NULL and K a multiple of 32 otherwise, both stream straight into
+ * LDS through a four-stage ring; in every other case x passes through
+ * registers where it is multiplied by w_norm (see np_fold_norm_weight).
  * Limits: K a multiple of 8; M, N, K < 2^31; x, Wt, w_norm 16-byte aligned.
  * M = 0 is a no-op that touches no buffer.
  * Errors: NP_EINVAL for another dtype, bad sizes or alignment, NULL x / Wt /
@@ -380,8 +382,8 @@ int unfused_rmsnorm_linear(const void* x, const void* w_norm, const void* Wt, co
  * once: fuse_rmsnorm_linear(x, NULL, Wt_folded, ...) then computes
  *   scale * (rstd_m * sum_k x_mk round_dt(w_k Wt_nk) + bias_n),
  * the same value in exact arithmetic as with w_norm, rounded in the weight
- * instead of in the activation, and takes the faster kernel whose operands
- * stream straight into LDS. Wt_folded may be Wt itself (in place) but must not
+ * instead of in the activation, and takes the faster kernel that stages both
+ * operands unchanged. Wt_folded may be Wt itself (in place) but must not
  * partially overlap it or overlap w_norm. All buffers 16-byte aligned, dt
  * NP_BF16 or NP_F16, K a multiple of 8. Errors: NP_EINVAL.
  */
