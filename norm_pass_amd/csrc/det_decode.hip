@@ -94,6 +94,11 @@ __device__ __forceinline__ float decode_cell(const ChanConst& cc, int i, float t
   return cc.is_exp ? ex : box;
 }
 
+// Cells per tile (the choice is explained at det_tile_cells below).
+#ifndef NP_DET_TILE_CELLS
+#define NP_DET_TILE_CELLS 24
+#endif
+
 #ifndef NP_DET_XCD_REMAP
 #define NP_DET_XCD_REMAP 1
 #endif
@@ -112,7 +117,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return x * per + min(x, rem) + j;
 }
 
-template <typename T, bool VEC>
+// GF: vectors per channel row of a whole tile (tile cells / N), when known at
+// compile time (0: read from the arguments), so that the thread -> (channel,
+// vector) split is a division by a constant.
+template <typename T, bool VEC, int GF>
 __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
   extern __shared__ float tile[];
   // the header, copied at once as ints so that its reads go out together
@@ -170,11 +178,14 @@ __global__ __launch_bounds__(kBlock) void det_decode_kernel(DetArgs a) {
   // phase 1: channel planes -> decoded values in row layout
   if (VEC) {
     constexpr int N = Vec<T>::N;
-    const int groups = ncell / N;  // ncell is a multiple of N on this path
+    // ncell is a multiple of N on this path; a partial tile's missing vectors
+    // are skipped, so the split follows the whole tile's vector count
+    const int groups = GF ? GF : TP / N;
     const bool two_rows = tc.w >= N;  // a vector's cells span at most two grid rows
     for (int e = threadIdx.x; e < C * groups; e += kBlock) {
       const int k = e / groups;
       const int cg = e - k * groups;
+      if (cg * N >= ncell) continue;
       float t[N];
       load_vec<T>(plane0 + (int64_t)k * HW + cg * N, t);
       if (two_rows) {
@@ -226,10 +237,13 @@ template <typename T>
 hipError_t launch_t(const DetArgs& a, bool vec_in, hipStream_t s) {
   const int blocks = a.h.tile_start[a.h.n_levels];
   const size_t lds = (size_t)a.h.tile_cells * a.h.n_ch * sizeof(float);
-  if (vec_in)
-    hipLaunchKernelGGL((det_decode_kernel<T, true>), dim3(blocks), dim3(kBlock), lds, s, a);
+  constexpr int kGF = NP_DET_TILE_CELLS / Vec<T>::N;
+  if (vec_in && a.h.tile_cells == NP_DET_TILE_CELLS)
+    hipLaunchKernelGGL((det_decode_kernel<T, true, kGF>), dim3(blocks), dim3(kBlock), lds, s, a);
+  else if (vec_in)
+    hipLaunchKernelGGL((det_decode_kernel<T, true, 0>), dim3(blocks), dim3(kBlock), lds, s, a);
   else
-    hipLaunchKernelGGL((det_decode_kernel<T, false>), dim3(blocks), dim3(kBlock), lds, s, a);
+    hipLaunchKernelGGL((det_decode_kernel<T, false, 0>), dim3(blocks), dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
 
@@ -242,9 +256,6 @@ hipError_t launch_t(const DetArgs& a, bool vec_in, hipStream_t s) {
 // 192-512 threads. The tile stays a multiple of 8 cells so that every tile is
 // whole 16-byte vectors. Wide rows (n_ch > 256) use 8 cells to keep the tile
 // within 32 KiB.
-#ifndef NP_DET_TILE_CELLS
-#define NP_DET_TILE_CELLS 24
-#endif
 int det_tile_cells(int n_ch) { return n_ch <= 256 ? NP_DET_TILE_CELLS : 8; }
 
 hipError_t launch_det_decode(const DetArgs& a, int in_dt, bool vec_in, hipStream_t s) {
