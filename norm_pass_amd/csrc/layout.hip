@@ -86,8 +86,9 @@ __device__ __forceinline__ void lds_put16(uint8_t* p, u32x4 v) {
 // 4-byte units: unit (i, c) of the 128 x 128 tile at word
 // ((c / 4 + i / 4) mod 32) + 32 (c mod 4) of row i, rows 640 bytes apart (160
 // words, so row i starts on bank 32 (i mod 2)). A wave stores rows i, i + 1
-// (i even), lane (row, v) the units 4 v .. 4 v + 3 at four fixed offsets: for
-// each store the banks are ((v + const) mod 32) + 32 (row mod 2), all 64. It
+// (i even), lane (row, v) the units 4 v + m (m = 0..3) at four fixed offsets:
+// for each store the banks are ((v + const) mod 32) + 32 ((row + m) mod 2),
+// all 64. It
 // reads units (4 v + k, j) and (4 v + k, j + 1) (j even): ((v + const) mod 32)
 // + 32 ((k + j) mod 2), all 64 again. With the 516-byte pitch the reads were
 // two-way conflicted (a wave's 32 reads of one output row fell on 16 banks).
